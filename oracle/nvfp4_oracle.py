@@ -1,0 +1,274 @@
+"""Plain CPU oracle for NVFP4 quantized matmul.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this
+module: only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, tables or
+constants with the HIP library; it is written from the pages' description
+of the format and is deliberately slow and literal.
+
+Sources (pages as published on the web):
+
+* P1 = mlxcel issue "perf(nvfp4): direct-transcode ModelOpt triplets to
+  MLX native" -- sections "Technical notes" (packing, E2M1 table, E4M3 block
+  scales of 16, little-endian words) and "Implementation plan" (four source
+  bytes become one word; weight_scale kept as E4M3 bytes; weight_scale_2
+  kept as a global-scale sidecar).
+* P3 = mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM" --
+  "Summary" (global_scale[expert] / (448 * 6) applied once per output;
+  GatherQMM over experts), "Numerical results" (the reference is
+  ``x @ dequantize(w).T`` on the CPU, error = max abs error relative to
+  max|reference|), "Changes during review" (quantized-axis rule, partial
+  blocks, out-of-range experts give exact zeros, scale-plane shape) and
+  "Implementation Review Summary / Verification" (fp_dequantize multiplies
+  by global_scale / (448 * 6)).
+
+Readings where the pages are silent (each listed in the design notes):
+
+* element j of a packed word sits at bits [4j, 4j+4) (low nibble first);
+* the E2M1 sign is nibble bit 3;
+* "FP8 E4M3" is the OCP E4M3FN encoding (bias 7, subnormals, no infinity,
+  NaN only at S.1111.111) -- 448, its largest finite value, is the constant
+  the pages divide by;
+* the sidecar written by transcode is gs = fl32(weight_scale_2 * 2688), so
+  that gs / 2688 restores weight_scale_2 (to one f32 rounding);
+* g = fl32(gs / 2688) is formed once in float32 and each dequantized value is
+  fl32(e2m1 * e4m3 * g) -- float32 is the precision the pages fix for the
+  global scale and for the dequantized reference;
+* the contraction is carried out in float64 (stricter than the pages' f32
+  reference) so the oracle's own rounding does not eat the error budget;
+* gather rows whose expert or lhs index is out of range are +0.0.
+
+Every function below works on numpy arrays; bf16 tensors are represented as
+their uint16 bit patterns.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+# P1 "Technical notes": E2M1 magnitudes in LUT order, with a sign bit.
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+# P3 "Summary" / "Verification": the global scale is divided by 448 * 6
+# (448 = largest E4M3 value, 6 = largest E2M1 value).
+GLOBAL_DIVISOR = 448.0 * 6.0
+
+# P1 "Technical notes": one E4M3 scale per 16 elements, eight nibbles per word.
+GROUP_SIZE = 16
+NIBBLES_PER_WORD = 8
+
+
+# ----------------------------------------------------------------------------
+# Element decoders
+# ----------------------------------------------------------------------------
+
+def e2m1_value(nibble: int) -> float:
+    """Value of one FP4 E2M1 nibble (P1 "Technical notes": LUT order 0, 0.5,
+    1, 1.5, 2, 3, 4, 6 plus a sign bit; sign read as bit 3)."""
+    magnitude = E2M1_MAGNITUDES[nibble & 7]
+    return -magnitude if nibble & 8 else magnitude
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one FP8 E4M3 byte (P1 "Technical notes": the block scales are
+    "uint8 FP8 E4M3"), decoded as OCP E4M3FN: sign bit 7, exponent bits 6..3
+    with bias 7, mantissa bits 2..0, subnormals at exponent 0, NaN at
+    exponent 15 with mantissa 7, no infinities."""
+    sign = -1.0 if code & 0x80 else 1.0
+    exponent = (code >> 3) & 0xF
+    mantissa = code & 0x7
+    if exponent == 0xF and mantissa == 0x7:
+        return float("nan")
+    if exponent == 0:
+        return sign * mantissa * 2.0 ** -9          # (m / 8) * 2^(1 - 7)
+    return sign * (1.0 + mantissa / 8.0) * 2.0 ** (exponent - 7)
+
+
+def decode_e2m1(nibbles: np.ndarray) -> np.ndarray:
+    """Vectorised :func:`e2m1_value` over an integer array (float64 out)."""
+    table = np.array([e2m1_value(n) for n in range(16)], dtype=np.float64)
+    return table[np.asarray(nibbles, dtype=np.int64)]
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Vectorised :func:`e4m3_value` over a uint8 array (float64 out)."""
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.int64)]
+
+
+def unpack_nibbles(words: np.ndarray) -> np.ndarray:
+    """Split uint32 words into their eight nibbles along a new last axis,
+    element j taken from bits [4j, 4j+4); the result's last axis is 8x the
+    input's (P1 "Technical notes": eight nibbles per uint32 word)."""
+    words = np.asarray(words, dtype=np.uint32)
+    shifts = np.arange(NIBBLES_PER_WORD, dtype=np.uint32) * np.uint32(4)
+    nibbles = (words[..., None] >> shifts) & np.uint32(0xF)
+    return nibbles.reshape(words.shape[:-1] + (words.shape[-1] * NIBBLES_PER_WORD,)).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# bf16 helpers (bit patterns in uint16)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(values: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even) and return
+    the uint16 bit patterns.  NaN maps to a quiet NaN of the same sign."""
+    f = np.ascontiguousarray(values, dtype=np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    rounded = ((bits + np.uint64(0x7FFF) + ((bits >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16))
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(f)
+    out[nan] = ((bits[nan] >> np.uint64(16)).astype(np.uint16) | np.uint16(0x0040))
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 exactly."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Global scale
+# ----------------------------------------------------------------------------
+
+def global_factor(gs) -> np.float32:
+    """Per-output factor g = global_scale / (448 * 6), formed once in float32
+    (P3 "Summary": applied once per output; "Verification": fp_dequantize
+    multiplies by global_scale / (448 * 6))."""
+    return np.float32(np.float32(gs) / np.float32(GLOBAL_DIVISOR))
+
+
+# ----------------------------------------------------------------------------
+# Dequantize
+# ----------------------------------------------------------------------------
+
+def check_planes(w: np.ndarray, scales: np.ndarray) -> None:
+    """The scale plane must be shaped w.shape[:-1] + [w.shape[-1] / 2] with one
+    byte per scale (P3 "Changes during review", scale-plane check)."""
+    if w.dtype != np.uint32 or scales.dtype != np.uint8:
+        raise ValueError("w must be uint32 and scales uint8")
+    if w.shape[-1] % 2 != 0 or scales.shape != w.shape[:-1] + (w.shape[-1] // 2,):
+        raise ValueError(f"scale plane {scales.shape} does not match weight plane {w.shape}")
+
+
+def dequantize(w: np.ndarray, scales: np.ndarray, gs=None) -> np.ndarray:
+    """Expand a packed plane along its last (quantized) axis to float32.
+
+    value = e2m1(nibble) * e4m3(scale of its 16-block), which is exact in
+    float32; with a global scale, value = fl32(value * g), g = fl32(gs/2688)
+    (P1 "Technical notes"; P3 "Summary": the dequantize kernel expands a plane
+    exactly; P3 "Verification": the global-scale multiply).
+    """
+    check_planes(w, scales)
+    elements = decode_e2m1(unpack_nibbles(w))                      # [..., 8W]
+    block = decode_e4m3(scales)                                    # [..., 8W/16]
+    block = np.repeat(block, GROUP_SIZE, axis=-1)                  # one per element
+    exact = (elements * block).astype(np.float32)                  # exact product
+    if gs is None:
+        return exact
+    return (exact * global_factor(gs)).astype(np.float32)
+
+
+def dequantize_bf16_bits(w: np.ndarray, scales: np.ndarray, gs=None) -> np.ndarray:
+    """Dequantize, then round the float32 values to bf16 (uint16 bits)."""
+    return f32_to_bf16_bits(dequantize(w, scales, gs))
+
+
+# ----------------------------------------------------------------------------
+# Quantized matmul
+# ----------------------------------------------------------------------------
+
+def qmm(x: np.ndarray, w: np.ndarray, scales: np.ndarray, gs=None,
+        transpose: bool = True) -> np.ndarray:
+    """Reference quantized matmul (P3 "Numerical results": x @ dequantize(w).T
+    on the CPU).
+
+    transpose=True: w is [N, K/8] quantized along K, out = x @ W.T.
+    transpose=False: w is [K, N/8] quantized along N, out = x @ W.
+    x is float32 values (bf16 inputs widened exactly).  The result is float64:
+    each product of two float32 values is exact in float64 and the sum is
+    formed in float64.
+    """
+    W = dequantize(w, scales, gs).astype(np.float64)
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    if transpose:
+        if W.shape[-1] != x64.shape[-1]:
+            raise ValueError("K mismatch")
+        return x64 @ W.T
+    if W.shape[0] != x64.shape[-1]:
+        raise ValueError("K mismatch")
+    return x64 @ W
+
+
+def gather_qmm(x: np.ndarray, lhs: Optional[np.ndarray], rhs: np.ndarray,
+               w: np.ndarray, scales: np.ndarray, gs: Optional[np.ndarray]) -> np.ndarray:
+    """Reference GatherQMM over experts (P3 "Summary": GatherQMM with a
+    per-expert global scale; "Changes during review": out-of-range expert
+    indices produce exact zeros).
+
+    x [X, M, K]; lhs [R] (None = identity, r -> r); rhs [R];
+    w [E, N, K/8]; scales [E, N, K/16]; gs [E] or None.
+    out[r] = x[lhs[r]] @ dequantize(w[rhs[r]]).T, or +0.0 when rhs[r] is not
+    in [0, E) or lhs[r] is not in [0, X).  Returns float64 [R, M, N].
+    """
+    X, M, _ = x.shape
+    E, N = w.shape[0], w.shape[1]
+    R = rhs.shape[0]
+    out = np.zeros((R, M, N), dtype=np.float64)
+    for r in range(R):
+        e = int(rhs[r])
+        src = int(lhs[r]) if lhs is not None else r
+        if not (0 <= e < E) or not (0 <= src < X):
+            continue
+        out[r] = qmm(x[src], w[e], scales[e], None if gs is None else gs[e], transpose=True)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Transcode (ModelOpt triplet -> native planes + sidecar)
+# ----------------------------------------------------------------------------
+
+def transcode(weight_u8: np.ndarray, weight_scale: np.ndarray,
+              weight_scale_2: Optional[np.ndarray]):
+    """ModelOpt NVFP4 triplet to native planes, without dense values
+    (P1 "Goal", "Technical notes" and "Implementation plan" step 3):
+
+    * every four source bytes b0..b3 become one little-endian word
+      b0 | b1 << 8 | b2 << 16 | b3 << 24;
+    * the E4M3 block-scale bytes are kept as they are;
+    * weight_scale_2 becomes the global-scale sidecar gs = fl32(ws2 * 2688),
+      the value whose gs / (448 * 6) is the second-level scale.
+
+    weight_u8 [..., rows, cols/2]; weight_scale [..., rows, cols/16];
+    weight_scale_2 [batch] float32 or None.
+    """
+    src = np.asarray(weight_u8, dtype=np.uint8)
+    if src.shape[-1] % 4 != 0:
+        raise ValueError("source row length must be a multiple of four bytes")
+    b = src.reshape(src.shape[:-1] + (src.shape[-1] // 4, 4)).astype(np.uint32)
+    words = b[..., 0] | (b[..., 1] << np.uint32(8)) | (b[..., 2] << np.uint32(16)) | (b[..., 3] << np.uint32(24))
+    words = words.astype(np.uint32)
+    scales = np.array(weight_scale, dtype=np.uint8, copy=True)
+    check_planes(words, scales)
+    gs = None
+    if weight_scale_2 is not None:
+        gs = (np.asarray(weight_scale_2, dtype=np.float32) * np.float32(GLOBAL_DIVISOR)).astype(np.float32)
+    return words, scales, gs
+
+
+# ----------------------------------------------------------------------------
+# Error metric
+# ----------------------------------------------------------------------------
+
+def relative_error(out: np.ndarray, ref: np.ndarray) -> float:
+    """max |out - ref| / max |ref| (P3 "Numerical results")."""
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    denom = np.max(np.abs(ref)) if ref.size else 0.0
+    err = np.max(np.abs(out - ref)) if ref.size else 0.0
+    if denom == 0.0:
+        return float(err)
+    return float(err / denom)

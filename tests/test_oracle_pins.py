@@ -1,0 +1,471 @@
+"""Pins for the CPU oracle, independent of the oracle itself.
+
+Each test checks the oracle against something other than its own code:
+the E2M1 table the pages print, a library FP8 decoder, exact rational
+arithmetic (fractions.Fraction) with an independently written float32
+rounding, byte identities, and exact zeros.  The mutation tests at the end
+plant plausible mistakes in the oracle (on the CPU) and check that these
+pins catch every one of them.
+"""
+
+import functools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import nvfp4_oracle as orc
+import nvfp4_synth as synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# Independent helpers
+# ----------------------------------------------------------------------------
+
+def load_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def golden_e2m1():
+    return {int(k): float(v) for k, v in load_table("e2m1_lut.txt")}
+
+
+def golden_constants():
+    return {k: float(v) for k, v in load_table("global_scale.txt")}
+
+
+@functools.lru_cache(maxsize=None)
+def torch_e4m3(code: int) -> float:
+    """Library decode of one FP8 E4M3FN byte."""
+    t = torch.tensor([code], dtype=torch.uint8).view(torch.float8_e4m3fn)
+    return float(t.to(torch.float64)[0])
+
+
+def round_to_f32(q: Fraction) -> Fraction:
+    """Round an exact rational to the nearest float32 (ties to even),
+    written from the IEEE 754 definition rather than by calling a float
+    conversion."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum_exp = max(e, -126) - 23          # 24 significant bits, subnormals below 2^-126
+    quantum = Fraction(2) ** quantum_exp
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * quantum
+    assert v <= Fraction(2) ** 128, "overflow"
+    return sign * v
+
+
+def f32_bits(values) -> np.ndarray:
+    return np.ascontiguousarray(values, dtype=np.float32).view(np.uint32)
+
+
+def words_from_nibbles(nibbles):
+    """Pack a flat list of nibbles, element j of each word at bits 4j."""
+    out = []
+    for i in range(0, len(nibbles), 8):
+        w = 0
+        for j, n in enumerate(nibbles[i:i + 8]):
+            w |= (n & 0xF) << (4 * j)
+        out.append(w)
+    return np.array(out, dtype=np.uint32)
+
+
+def brute_dequant(w, scales, gs=None):
+    """Element-by-element exact dequantize with Fraction; returns Fractions
+    (or None for NaN) in a nested list [rows][elements]."""
+    e2m1 = golden_e2m1()
+    divisor = Fraction(int(golden_constants()["divisor"]))
+    g = None if gs is None else round_to_f32(Fraction(float(np.float32(gs))) / divisor)
+    rows = []
+    for r in range(w.shape[0]):
+        row = []
+        for k in range(w.shape[1] * 8):
+            word = int(w[r, k // 8])
+            nib = (word >> (4 * (k % 8))) & 0xF
+            s = torch_e4m3(int(scales[r, k // 16]))
+            if math.isnan(s):
+                row.append(None)
+                continue
+            v = Fraction(e2m1[nib]) * Fraction(s)
+            if g is not None:
+                v = round_to_f32(v * g)
+            row.append(v)
+        rows.append(row)
+    return rows
+
+
+def brute_zero_sign(w, scales, r, k):
+    """Sign of a zero element: the product of the nibble's and the scale's
+    signs (IEEE multiply of signed values)."""
+    nib = (int(w[r, k // 8]) >> (4 * (k % 8))) & 0xF
+    neg = (math.copysign(1.0, golden_e2m1()[nib]) < 0) != (math.copysign(1.0, torch_e4m3(int(scales[r, k // 16]))) < 0)
+    return -0.0 if neg else 0.0
+
+
+# ----------------------------------------------------------------------------
+# Element decoders
+# ----------------------------------------------------------------------------
+
+def test_e2m1_matches_page_table():
+    table = golden_e2m1()
+    for nib in range(16):
+        got = orc.e2m1_value(nib)
+        assert got == table[nib] and math.copysign(1, got) == math.copysign(1, table[nib]), nib
+
+
+def test_e4m3_matches_library_decoder_all_codes():
+    for code in range(256):
+        want = torch_e4m3(code)
+        got = orc.e4m3_value(code)
+        if math.isnan(want):
+            assert math.isnan(got), code
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), hex(code)
+
+
+def test_e4m3_spot_values_and_max():
+    for code_hex, value in load_table("e4m3_spot.txt"):
+        got = orc.e4m3_value(int(code_hex, 16))
+        want = float(value)
+        if math.isnan(want):
+            assert math.isnan(got)
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), code_hex
+    finite = [orc.e4m3_value(c) for c in range(256) if not math.isnan(orc.e4m3_value(c))]
+    assert max(finite) == golden_constants()["e4m3_max"]
+    assert max(abs(orc.e2m1_value(n)) for n in range(16)) == golden_constants()["e2m1_max"]
+
+
+def test_nibble_order_low_first():
+    w = np.array([[0x76543210, 0xFEDCBA98]], dtype=np.uint32)
+    assert orc.unpack_nibbles(w).tolist() == [list(range(16))]
+
+
+# ----------------------------------------------------------------------------
+# Dequantize
+# ----------------------------------------------------------------------------
+
+def every_pair_plane():
+    """256 rows (one per scale code), 16 elements per row = nibbles 0..15."""
+    w = np.tile(words_from_nibbles(list(range(16))), (256, 1))
+    scales = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    return w, scales
+
+
+@pytest.mark.parametrize("gs", [None, 1.0, 777.25, 2688.0 * 3.5, 0.5, 1999.0])
+def test_dequantize_every_nibble_and_code_bruteforce(gs):
+    w, scales = every_pair_plane()
+    got = orc.dequantize(w, scales, None if gs is None else np.float32(gs))
+    assert got.dtype == np.float32
+    want = brute_dequant(w, scales, gs)
+    for r in range(256):
+        for k in range(16):
+            if want[r][k] is None:
+                assert np.isnan(got[r, k])
+                continue
+            wv = np.float32(float(want[r][k]))
+            if want[r][k] == 0:
+                wv = np.float32(brute_zero_sign(w, scales, r, k))
+            assert float(wv) == want[r][k]
+            assert f32_bits(got[r, k]) == f32_bits(wv), (r, k, got[r, k], float(want[r][k]))
+
+
+def test_dequantize_random_plane_bruteforce():
+    g = synth.rng(11)
+    w = synth.packed_words(g, (5, 6))          # 48 elements per row, 3 blocks
+    sc = synth.scale_codes(g, (5, 3), synth.FINITE_POSITIVE_CODES)
+    gs = synth.global_scales(g, 1)[0]
+    for gsv in (None, gs):
+        got = orc.dequantize(w, sc, gsv)
+        want = brute_dequant(w, sc, gsv)
+        for r in range(5):
+            for k in range(48):
+                assert Fraction(float(got[r, k])) == want[r][k]
+
+
+def test_global_scale_of_2688_is_identity():
+    w, scales = every_pair_plane()
+    a = orc.dequantize(w, scales, None)
+    b = orc.dequantize(w, scales, np.float32(2688.0))
+    assert np.array_equal(f32_bits(a), f32_bits(b))
+
+
+def test_dequantize_bf16_matches_library_rounding():
+    g = synth.rng(12)
+    w = synth.packed_words(g, (64, 16))
+    sc = synth.scale_codes(g, (64, 8))
+    gs = synth.global_scales(g, 1)[0]
+    f = orc.dequantize(w, sc, gs)
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.dequantize_bf16_bits(w, sc, gs)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rounding_matches_library():
+    g = synth.rng(13)
+    vals = np.concatenate([
+        g.standard_normal(4096).astype(np.float32) * np.float32(1e3),
+        np.array([0.0, -0.0, np.inf, -np.inf, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8,
+                  3.4e38, 1e-40, -1e-40], dtype=np.float32),
+    ])
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.f32_to_bf16_bits(vals)
+    assert np.array_equal(got, want)
+    nan = orc.f32_to_bf16_bits(np.array([np.nan], dtype=np.float32))
+    assert np.isnan(orc.bf16_bits_to_f32(nan)[0])
+    back = orc.bf16_bits_to_f32(got)
+    assert np.array_equal(back, torch.from_numpy(vals).to(torch.bfloat16).float().numpy())
+
+
+def test_scale_plane_shape_is_checked():
+    w = np.zeros((4, 4), dtype=np.uint32)
+    with pytest.raises(ValueError):
+        orc.dequantize(w, np.zeros((4, 3), dtype=np.uint8))
+    with pytest.raises(ValueError):
+        orc.dequantize(w, np.zeros((4, 2, 1), dtype=np.uint8))
+
+
+# ----------------------------------------------------------------------------
+# Quantized matmul
+# ----------------------------------------------------------------------------
+
+class Exact:
+    """An exact dot product and the sum of its terms' magnitudes."""
+    def __init__(self, terms):
+        self.value = sum(terms, Fraction(0))
+        self.mag = sum((abs(t) for t in terms), Fraction(0))
+
+    def close(self, got, rel=Fraction(1, 2 ** 50)):
+        """float64 summation error is bounded by K * eps * sum|terms|."""
+        return abs(Fraction(float(got)) - self.value) <= self.mag * rel
+
+
+def brute_qmm(x, w, scales, gs, transpose):
+    W = brute_dequant(w, scales, gs)            # rows of the plane
+    M = x.shape[0]
+    if transpose:
+        N, K = len(W), len(W[0])
+        return [[Exact([Fraction(float(x[m, k])) * W[n][k] for k in range(K)]) for n in range(N)] for m in range(M)]
+    K, N = len(W), len(W[0])
+    return [[Exact([Fraction(float(x[m, k])) * W[k][n] for k in range(K)]) for n in range(N)] for m in range(M)]
+
+
+@pytest.mark.parametrize("with_gs", [False, True])
+def test_qmm_transposed_bruteforce(with_gs):
+    c = synth.dense_case(21, M=2, K=32, N=3, transpose=True, with_gs=with_gs,
+                         code_range=synth.FINITE_POSITIVE_CODES)
+    gs = None if c.gs is None else c.gs[0]
+    got = orc.qmm(c.x, c.w, c.scales, gs, transpose=True)
+    want = brute_qmm(c.x, c.w, c.scales, gs, True)
+    assert got.shape == (2, 3)
+    for m in range(2):
+        for n in range(3):
+            assert want[m][n].close(got[m, n]), (m, n)
+
+
+@pytest.mark.parametrize("with_gs", [False, True])
+def test_qmm_nontransposed_k17_bruteforce(with_gs):
+    c = synth.dense_case(22, M=3, K=17, N=32, transpose=False, with_gs=with_gs)
+    assert c.w.shape == (17, 4) and c.scales.shape == (17, 2)
+    gs = None if c.gs is None else c.gs[0]
+    got = orc.qmm(c.x, c.w, c.scales, gs, transpose=False)
+    want = brute_qmm(c.x, c.w, c.scales, gs, False)
+    assert got.shape == (3, 32)
+    for m in range(3):
+        for n in range(32):
+            assert want[m][n].close(got[m, n]), (m, n)
+
+
+def test_qmm_one_hot_picks_a_dequantized_element():
+    c = synth.dense_case(23, M=1, K=64, N=5, with_gs=True)
+    W = brute_dequant(c.w, c.scales, c.gs[0])
+    for k in (0, 7, 8, 15, 16, 63):
+        x = np.zeros((1, 64), dtype=np.float32)
+        x[0, k] = 1.0
+        got = orc.qmm(x, c.w, c.scales, c.gs[0])
+        for n in range(5):
+            assert Fraction(float(got[0, n])) == W[n][k]
+
+
+# ----------------------------------------------------------------------------
+# Gather
+# ----------------------------------------------------------------------------
+
+def test_gather_rows_and_out_of_range_zeros():
+    c = synth.gather_case(31, tokens=3, E=4, N=5, K=32, top_k=2, sort=False,
+                          with_gs=True, M=2, out_of_range=(4, 5, 2 ** 31 - 1, -1))
+    lhs = c.lhs.copy()
+    lhs[1] = 3                      # lhs outside [0, X) as well
+    got = orc.gather_qmm(c.x, lhs, c.rhs, c.w, c.scales, c.gs)
+    assert got.shape == (6, 2, 5)
+    for r in range(6):
+        e, src = int(c.rhs[r]), int(lhs[r])
+        if not (0 <= e < 4) or not (0 <= src < 3):
+            assert np.all(got[r] == 0.0) and not np.any(np.signbit(got[r])), r
+            continue
+        want = brute_qmm(c.x[src], c.w[e], c.scales[e], c.gs[e], True)
+        for m in range(2):
+            for n in range(5):
+                assert want[m][n].close(got[r, m, n]), (r, m, n)
+    zero_rows = [r for r in range(6) if not (0 <= int(c.rhs[r]) < 4) or not (0 <= int(lhs[r]) < 3)]
+    assert len(zero_rows) >= 4
+
+
+# ----------------------------------------------------------------------------
+# Transcode
+# ----------------------------------------------------------------------------
+
+def test_transcode_is_a_byte_move():
+    g = synth.rng(41)
+    wu8, ws, ws2 = synth.modelopt_triplet(g, 2, 8, 64)
+    words, scales, gs = orc.transcode(wu8, ws, ws2)
+    assert words.shape == (2, 8, 8) and words.dtype == np.uint32
+    # On a little-endian host the word plane viewed as bytes is the source.
+    assert np.array_equal(words.astype("<u4").view(np.uint8).reshape(wu8.shape), wu8)
+    assert np.array_equal(scales, ws)
+    assert gs.dtype == np.float32 and gs.shape == (2,)
+
+
+def test_transcode_reconstructs_source_weights():
+    """Dequantizing the transcoded planes gives e2m1 * weight_scale *
+    weight_scale_2 of the source within a few float32 roundings."""
+    g = synth.rng(42)
+    wu8, ws, ws2 = synth.modelopt_triplet(g, 3, 4, 32)
+    words, scales, gs = orc.transcode(wu8, ws, ws2)
+    e2m1 = golden_e2m1()
+    for b in range(3):
+        deq = orc.dequantize(words[b], scales[b], gs[b])
+        for r in range(4):
+            for k in range(32):
+                byte = int(wu8[b, r, k // 2])
+                nib = byte & 0xF if k % 2 == 0 else byte >> 4
+                want = Fraction(e2m1[nib]) * Fraction(torch_e4m3(int(ws[b, r, k // 16]))) * Fraction(float(ws2[b]))
+                got = Fraction(float(deq[r, k]))
+                assert abs(got - want) <= abs(want) * Fraction(3, 2 ** 24), (b, r, k)
+
+
+def test_transcode_without_second_scale():
+    g = synth.rng(43)
+    wu8, ws, _ = synth.modelopt_triplet(g, 1, 2, 16, with_ws2=False)
+    words, scales, gs = orc.transcode(wu8, ws, None)
+    assert gs is None and words.shape == (1, 2, 2)
+
+
+def test_relative_error_metric():
+    ref = np.array([1.0, -4.0, 2.0])
+    out = np.array([1.0, -4.5, 2.0])
+    assert orc.relative_error(out, ref) == 0.125
+
+
+# ----------------------------------------------------------------------------
+# Mutation checks: plausible mistakes planted in the oracle must be caught.
+# ----------------------------------------------------------------------------
+
+PIN_TESTS = [
+    test_e2m1_matches_page_table,
+    test_e4m3_matches_library_decoder_all_codes,
+    test_nibble_order_low_first,
+    lambda: test_dequantize_every_nibble_and_code_bruteforce(777.25),
+    test_dequantize_random_plane_bruteforce,
+    lambda: test_qmm_transposed_bruteforce(True),
+    lambda: test_qmm_nontransposed_k17_bruteforce(True),
+    test_gather_rows_and_out_of_range_zeros,
+    test_transcode_reconstructs_source_weights,
+]
+
+
+def caught(monkeypatch_fn):
+    """True when at least one pin fails with the mutation in place."""
+    for t in PIN_TESTS:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+def _mut_e4m3_bias(code):
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    return s * (m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 8))
+
+
+def _mut_e4m3_nan(code):
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    return s * (m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def _mut_nibble_order(words):
+    words = np.asarray(words, dtype=np.uint32)
+    shifts = (7 - np.arange(8, dtype=np.uint32)) * np.uint32(4)
+    nib = (words[..., None] >> shifts) & np.uint32(0xF)
+    return nib.reshape(words.shape[:-1] + (words.shape[-1] * 8,)).astype(np.uint8)
+
+
+def _mut_sign(n):
+    mag = orc.E2M1_MAGNITUDES[n & 7]
+    return mag
+
+
+def _mut_qmm_transpose(x, w, scales, gs=None, transpose=True):
+    W = orc.dequantize(w, scales, gs).astype(np.float64)
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    if transpose:
+        return x64 @ W.T
+    return (x64 @ W[::-1]) if W.shape[0] > 1 else x64 @ W
+
+
+def _mut_gather_no_zero(x, lhs, rhs, w, scales, gs):
+    R = rhs.shape[0]
+    out = np.zeros((R, x.shape[1], w.shape[1]))
+    for r in range(R):
+        e = int(rhs[r]) % w.shape[0]
+        src = (int(lhs[r]) if lhs is not None else r) % x.shape[0]
+        out[r] = orc.qmm(x[src], w[e], scales[e], None if gs is None else gs[e])
+    return out
+
+
+MUTATIONS = {
+    "e4m3 exponent bias 8": ("e4m3_value", _mut_e4m3_bias),
+    "e4m3 no NaN code": ("e4m3_value", _mut_e4m3_nan),
+    "nibble order high first": ("unpack_nibbles", _mut_nibble_order),
+    "e2m1 sign dropped": ("e2m1_value", _mut_sign),
+    "global divisor 448": ("GLOBAL_DIVISOR", 448.0),
+    "global divisor 6": ("GLOBAL_DIVISOR", 6.0),
+    "E2M1 table swapped": ("E2M1_MAGNITUDES", (0.0, 0.5, 1.0, 1.5, 2.0, 4.0, 3.0, 6.0)),
+    "non-transposed operand reversed": ("qmm", _mut_qmm_transpose),
+    "gather out-of-range wraps": ("gather_qmm", _mut_gather_no_zero),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, value = MUTATIONS[name]
+    monkeypatch.setattr(orc, attr, value)
+    assert caught(monkeypatch), f"no pin caught: {name}"
