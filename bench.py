@@ -1,0 +1,393 @@
+#!/usr/bin/env python3
+"""Benchmark of NVFP4 quantized matmul on one MI355X.
+
+Headline (``value``): the decode workload -- qmm with M=1, K=5376, N=21504,
+bf16 activations and output, scalar global scale -- as achieved HBM GB/s
+of algorithmic bytes.  One step is one nvfp4_qmm call (weight stream, scale
+stream, decode, MAC, reduction, epilogue).  The K timed steps are launched
+as one captured HIP graph and rotate over 8 independent copies of the
+weight planes (520 MB > the 256 MB MALL) so weights come from HBM.
+
+Also reported, each against its roofline: the prefill GEMM (M=2048,
+TFLOP/s), the multi-row qmv (M=16) and the MoE gather (sorted prefill and
+unsorted decode, GB/s).  Kernel durations come from HIP events around a replayed
+graph of back-to-back launches on the launch stream.  The CPU oracle is timed on the host
+on the full decode workload (cpu_baseline).
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import nvfp4_quantized_matmul_amd as nv  # noqa: E402
+import nvfp4_synth as synth  # noqa: E402
+
+METRIC = "NVFP4 qmv HBM GB/s (M=1) and dequant+GEMM TFLOP/s (M=2048), % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+DEV = "cuda:0"
+BF16 = 1
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def words_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(DEV)
+
+
+def u8_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
+
+
+def P(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def stream_ptr():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def graph_launch_us(work, n: int, reps: int = 3):
+    """Average duration of one launch: `n` launches captured in one HIP
+    graph, replayed between two events on the launch stream; the median of
+    `reps` replays is returned with the spread."""
+    work.launch(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            work.launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        per.append(1e3 * e0.elapsed_time(e1) / n)
+    per.sort()
+    return {"mean_us": per[len(per) // 2], "min_us": per[0], "max_us": per[-1],
+            "launches_per_replay": n, "replays": reps}
+
+
+def check(status, what):
+    if status != 0:
+        raise RuntimeError(f"{what}: {nv.status_string(status)}")
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+class Decode:
+    """qmm M=1, K=5376, N=21504, bf16, scalar gs; `copies` weight planes."""
+    M, K, N = 1, 5376, 21504
+
+    def __init__(self, copies: int):
+        wl = synth.WORKLOADS["decode_qmv_m1_k5376_n21504_bf16"]
+        case = synth.dense_case(wl["seed"], self.M, self.K, self.N, with_gs=True)
+        w0, s0 = words_dev(case.w), u8_dev(case.scales)
+        self.w = [w0] + [w0.clone() for _ in range(copies - 1)]
+        self.s = [s0] + [s0.clone() for _ in range(copies - 1)]
+        self.gs = torch.from_numpy(case.gs).to(DEV)
+        self.x = torch.from_numpy(case.x).to(torch.bfloat16).to(DEV)
+        self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=DEV)
+        self.lib = nv.load_library()
+        self.copies = copies
+        self.bytes = (case.w.nbytes + case.scales.nbytes + 4 + self.x.numel() * 2 + self.out.numel() * 2)
+
+    def launch(self, i):
+        c = i % self.copies
+        check(self.lib.nvfp4_qmm(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]),
+                                 P(self.gs), 1, 0, P(self.out), stream_ptr()), "decode qmm")
+
+
+class Prefill:
+    """qmm M=2048, K=5376, N=21504, bf16, gs after the matmul."""
+    M, K, N = 2048, 5376, 21504
+
+    def __init__(self, decode: Decode):
+        wl = synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]
+        g = synth.rng(wl["seed"])
+        self.x = torch.from_numpy(synth.activations(g, (self.M, self.K))).to(torch.bfloat16).to(DEV)
+        self.w, self.s, self.gs = decode.w, decode.s, decode.gs   # same plane distribution
+        self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=DEV)
+        self.lib = decode.lib
+        self.flops = 2.0 * self.M * self.N * self.K
+
+    def launch(self, i):
+        c = i % len(self.w)
+        check(self.lib.nvfp4_qmm(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]),
+                                 P(self.gs), 1, 0, P(self.out), stream_ptr()), "prefill qmm")
+
+
+class MultiRow:
+    """qmm M=16, K=4096, N=14336, bf16, gs; 16 weight copies (530 MB)."""
+    K, N = 4096, 14336
+
+    def __init__(self, M: int, copies: int):
+        wl = synth.WORKLOADS["multirow_qmv_k4096_n14336"]
+        case = synth.dense_case(wl["seed"], M, self.K, self.N, with_gs=True)
+        w0, s0 = words_dev(case.w), u8_dev(case.scales)
+        self.M = M
+        self.w = [w0] + [w0.clone() for _ in range(copies - 1)]
+        self.s = [s0] + [s0.clone() for _ in range(copies - 1)]
+        self.gs = torch.from_numpy(case.gs).to(DEV)
+        self.x = torch.from_numpy(case.x).to(torch.bfloat16).to(DEV)
+        self.out = torch.empty((M, self.N), dtype=torch.bfloat16, device=DEV)
+        self.lib = nv.load_library()
+        self.bytes = case.w.nbytes + case.scales.nbytes + 4 + self.x.numel() * 2 + self.out.numel() * 2
+        self.flops = 2.0 * M * self.K * self.N
+
+    def launch(self, i):
+        c = i % len(self.w)
+        check(self.lib.nvfp4_qmm(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]),
+                                 P(self.gs), 1, 0, P(self.out), stream_ptr()), "multirow qmm")
+
+
+class Gather:
+    """MoE GatherQMM: E=128, N=1536, K=2048, top-8; bf16; per-expert gs."""
+    E, N, K, TOPK = 128, 1536, 2048, 8
+
+    def __init__(self, tokens: int, sort: bool, copies: int, seed_off: int = 0):
+        wl = synth.WORKLOADS["moe_gather_e128_n1536_k2048_top8"]
+        case = synth.gather_case(wl["seed"] + seed_off, tokens=tokens, E=self.E, N=self.N, K=self.K,
+                                 top_k=self.TOPK, sort=sort, with_gs=True)
+        w0, s0 = words_dev(case.w), u8_dev(case.scales)
+        self.w = [w0] + [w0.clone() for _ in range(copies - 1)]
+        self.s = [s0] + [s0.clone() for _ in range(copies - 1)]
+        self.gs = torch.from_numpy(case.gs).to(DEV)
+        self.x = torch.from_numpy(case.x).to(torch.bfloat16).to(DEV)
+        self.lhs = torch.from_numpy(case.lhs).to(DEV)
+        self.rhs = torch.from_numpy(case.rhs).to(DEV)
+        self.R = case.rhs.shape[0]
+        self.out = torch.empty((self.R, 1, self.N), dtype=torch.bfloat16, device=DEV)
+        self.sort = int(sort)
+        self.tokens = tokens
+        self.lib = nv.load_library()
+        distinct = len(np.unique(case.rhs))
+        per_expert = case.w[0].nbytes + case.scales[0].nbytes + 4
+        self.distinct = distinct
+        self.bytes = (distinct * per_expert + self.x.numel() * 2 + 2 * self.R * 4 + self.out.numel() * 2)
+        self.flops = 2.0 * self.R * self.N * self.K
+
+    def launch(self, i):
+        c = i % len(self.w)
+        check(self.lib.nvfp4_gather_qmm(P(self.x), BF16, self.tokens, 1, self.K, P(self.lhs), P(self.rhs),
+                                        self.R, P(self.w[c]), P(self.s[c]), P(self.gs), self.E, self.N,
+                                        self.sort, P(self.out), stream_ptr()), "gather")
+
+
+# ----------------------------------------------------------------------------
+# measurement helpers
+# ----------------------------------------------------------------------------
+
+def timed_graph(work, steps: int, warmup: int):
+    """Warm up eagerly, capture `steps` launches in one HIP graph, replay it
+    once between barriers; returns ms per step."""
+    for i in range(warmup):
+        work.launch(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            work.launch(i)
+    g.replay()                     # first replay: uploads the graph
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def timed_eager(work, steps: int):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        work.launch(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_quantized_matmul_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key: str, launches_bytes: float):
+    """HBM traffic per launch from committed rocprofv3 PMC summaries, if they
+    were taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(decode_bytes: float):
+    """The oracle, untuned, on the host: one full decode workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        blas_threads = 1
+    wl = synth.WORKLOADS["decode_qmv_m1_k5376_n21504_bf16"]
+    case = synth.dense_case(wl["seed"], 1, 5376, 21504, with_gs=True)
+    x = torch.from_numpy(case.x).to(torch.bfloat16).float().numpy()
+    reps, wall, cpu = 0, 0.0, 0.0
+    while reps < 3 and wall < 10.0:
+        t0, c0 = time.perf_counter(), time.process_time()
+        oracle.qmm(x, case.w, case.scales, case.gs[0])
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        reps += 1
+    per = wall / reps
+    return {"value": round(decode_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"full decode workload M=1 K=5376 N=21504 (dequantize + float64 matmul), "
+                      f"{reps} pass(es), {per:.2f} s per pass, mean busy cores {cpu / wall:.2f}"}
+
+
+# ----------------------------------------------------------------------------
+# main
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the NVFP4 matmul path here is single-GPU "
+              "(sharding across GPUs is described in the design notes, not run).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
+    nv.load_library()
+
+    log("decode: building inputs")
+    dec = Decode(copies=8)
+    log("decode: timed graph")
+    ms = timed_graph(dec, steps, warmup)
+    eager_ms = timed_eager(dec, min(steps, 100))
+    value = dec.bytes / (ms * 1e-3) / 1e9
+    # the timed region is K back-to-back launches of the one kernel, so its
+    # average launch duration is the per-step time
+    dur = {"mean_us": ms * 1e3, "launches": steps, "source": "HIP events around the timed graph replay"}
+    achieved = value
+    traffic = traffic_for("decode_qmv", dec.bytes)
+
+    log("prefill")
+    pre = Prefill(dec)
+    pdur = graph_launch_us(pre, 8)
+    ptf = pre.flops / (pdur["mean_us"] * 1e-6) / 1e12
+
+    log("multi-row qmv")
+    mr = MultiRow(16, copies=16)
+    mdur = graph_launch_us(mr, 64)
+    mgbs = mr.bytes / (mdur["mean_us"] * 1e-6) / 1e9
+
+    log("moe gather")
+    gs_sorted = Gather(128, True, copies=3)
+    sdur = graph_launch_us(gs_sorted, 24)
+    sgbs = gs_sorted.bytes / (sdur["mean_us"] * 1e-6) / 1e9
+    gs_dec = Gather(8, False, copies=3, seed_off=8)
+    udur = graph_launch_us(gs_dec, 96)
+    ugbs = gs_dec.bytes / (udur["mean_us"] * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(dec.bytes)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_qmv_m1_k5376_n21504_bf16", "M": 1, "K": 5376, "N": 21504,
+                   "activations": "bf16", "global_scale": True, "weight_copies": 8,
+                   "launch": "one HIP graph of `steps` nvfp4_qmm launches",
+                   "bytes_per_step": dec.bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "qmv_kernel<bf16,4,4,1>",
+                     "kernel_duration": dur},
+        "cpu_baseline": cpu,
+        "eager_ms_per_step": round(eager_ms, 6),
+        "prefill": {"workload": "prefill_gemm_m2048_k5376_n21504_bf16", "value": round(ptf, 2),
+                    "unit": "TFLOP/s", "flops": pre.flops,
+                    "roofline": {"bound": "mfma", "achieved": round(ptf, 2), "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(ptf / BF16_PEAK_TFLOPS, 4),
+                                 "kernel": "gemm_mfma_kernel", "kernel_duration": pdur}},
+        "multirow_m16": {"workload": "multirow_qmv_m16_k4096_n14336_bf16", "value": round(mgbs, 2),
+                         "unit": "GB/s", "frac_hbm": round(mgbs / HBM_PEAK_GBS, 4),
+                         "kernel_duration": mdur, "bytes": mr.bytes},
+        "moe_sorted_prefill": {"workload": "moe_gather_e128_n1536_k2048_top8_b128_sorted",
+                               "value": round(sgbs, 2), "unit": "GB/s",
+                               "frac_hbm": round(sgbs / HBM_PEAK_GBS, 4), "distinct_experts": gs_sorted.distinct,
+                               "kernel_duration": sdur, "bytes": gs_sorted.bytes},
+        "moe_unsorted_decode_b8": {"workload": "moe_gather_e128_n1536_k2048_top8_b8_unsorted",
+                                   "value": round(ugbs, 2), "unit": "GB/s",
+                                   "frac_hbm": round(ugbs / HBM_PEAK_GBS, 4),
+                                   "distinct_experts": gs_dec.distinct, "kernel_duration": udur,
+                                   "bytes": gs_dec.bytes},
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,300 @@
+"""NVFP4 quantized matmul for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libnvfp4.so``: it checks shapes, dtypes,
+devices and contiguity, allocates outputs with PyTorch, and passes raw device
+pointers and the current HIP stream to the C ABI declared in
+``include/nvfp4.h``.  Every step of the computation runs in the library's
+HIP kernels; there is no Python or CPU fallback, and every entry point raises
+if the library has not been built.
+
+Format (mlxcel issue "perf(nvfp4): direct-transcode ModelOpt triplets to MLX
+native", "Technical notes"): uint32 words with eight E2M1 nibbles, one E4M3
+scale byte per 16 elements, and an optional float32 global scale applied as
+global_scale / (448 * 6).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "NVFP4Error", "library_path", "load_library", "transcode", "dequantize", "qmm",
+    "gather_qmm", "select_route", "qmv_max_rows", "status_string",
+    "ROUTE_AUTO", "ROUTE_QMV", "ROUTE_GEMM",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libnvfp4.so"
+
+ROUTE_AUTO, ROUTE_QMV, ROUTE_GEMM = 0, 1, 2
+_ROUTES = {"auto": ROUTE_AUTO, "qmv": ROUTE_QMV, "gemm": ROUTE_GEMM}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+_WORD_DTYPES = (torch.int32, torch.uint32)
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    """A negative status returned by libnvfp4."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG_DIR, _LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libnvfp4.so from the package directory (built in-tree)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m nvfp4_quantized_matmul_amd.build` "
+            "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    sig = {
+        "nvfp4_transcode": [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp],
+        "nvfp4_dequantize": [vp, vp, vp, i64, i64, i64, c_int, vp, vp],
+        "nvfp4_qmm": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
+        "nvfp4_gather_qmm": [vp, c_int, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, i64, c_int, vp, vp],
+        "nvfp4_select_route": [i64, i64, i64, c_int, c_int],
+        "nvfp4_qmv_max_rows": [],
+        "nvfp4_status_string": [c_int],
+        "nvfp4_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = c_int
+    lib.nvfp4_qmv_max_rows.restype = i64
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().nvfp4_status_string(int(status)).decode()
+
+
+def select_route(M: int, K: int, N: int, transpose: bool = True, dtype=torch.bfloat16) -> str:
+    """Route nvfp4_qmm takes for AUTO ("qmv" or "gemm"); host only."""
+    r = load_library().nvfp4_select_route(M, K, N, int(bool(transpose)), _dtype_code(dtype))
+    if r < 0:
+        raise NVFP4Error("nvfp4_select_route", r)
+    return "qmv" if r == ROUTE_QMV else "gemm"
+
+
+def qmv_max_rows() -> int:
+    return int(load_library().nvfp4_qmv_max_rows())
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+def _dtype_code(dtype) -> int:
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}; expected float32, bfloat16 or float16")
+    return _DTYPES[dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise NVFP4Error(fn, status)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*tensors: Optional[torch.Tensor]) -> torch.device:
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def check_planes(w: torch.Tensor, scales: torch.Tensor) -> None:
+    """The scale plane must be w.shape[:-1] + [w.shape[-1] / 2] with one byte
+    per scale (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM",
+    "Changes during review")."""
+    if w.dtype not in _WORD_DTYPES:
+        raise TypeError(f"weight plane must be int32/uint32 words, got {w.dtype}")
+    if scales.dtype != torch.uint8:
+        raise TypeError(f"scale plane must be uint8, got {scales.dtype}")
+    if w.dim() < 1 or w.shape[-1] % 2 != 0:
+        raise ValueError(f"weight plane {tuple(w.shape)} must have an even last axis")
+    want = tuple(w.shape[:-1]) + (w.shape[-1] // 2,)
+    if tuple(scales.shape) != want:
+        raise ValueError(f"scale plane {tuple(scales.shape)} does not match weight plane "
+                         f"{tuple(w.shape)} (expected {want})")
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def transcode(weight: torch.Tensor, weight_scale: torch.Tensor,
+              weight_scale_2: Optional[torch.Tensor] = None, inplace: bool = False
+              ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """ModelOpt NVFP4 triplet -> (uint32 word plane, E4M3 scale plane, gs sidecar).
+
+    weight uint8 [..., rows, cols/2]; weight_scale uint8 [..., rows, cols/16];
+    weight_scale_2 float32 with one value per matrix (numel = prod of the
+    leading dims) or None.  With ``inplace`` the returned planes alias the
+    source storage.
+    """
+    if weight.dtype != torch.uint8 or weight_scale.dtype != torch.uint8:
+        raise TypeError("weight and weight_scale must be uint8")
+    if weight.dim() < 2 or weight.shape[-1] % 8 != 0:
+        raise ValueError("weight must be [..., rows, cols/2] with cols a multiple of 16")
+    lead = tuple(weight.shape[:-2])
+    rows, cols = weight.shape[-2], weight.shape[-1] * 2
+    if tuple(weight_scale.shape) != lead + (rows, cols // 16):
+        raise ValueError(f"weight_scale {tuple(weight_scale.shape)} does not match weight "
+                         f"{tuple(weight.shape)}")
+    batch = 1
+    for d in lead:
+        batch *= d
+    if weight_scale_2 is not None:
+        if weight_scale_2.dtype != torch.float32 or weight_scale_2.numel() != batch:
+            raise ValueError("weight_scale_2 must be float32 with one value per matrix")
+    dev = _require_gpu(weight, weight_scale, weight_scale_2)
+    lib = load_library()
+    if inplace:
+        w_out = weight.view(torch.int32).view(lead + (rows, cols // 8))
+        s_out = weight_scale
+    else:
+        w_out = torch.empty(lead + (rows, cols // 8), dtype=torch.int32, device=dev)
+        s_out = torch.empty_like(weight_scale)
+    gs = None
+    if weight_scale_2 is not None:
+        gs = torch.empty(batch, dtype=torch.float32, device=dev)
+    _check("nvfp4_transcode", lib.nvfp4_transcode(
+        _ptr(weight), _ptr(weight_scale), _ptr(weight_scale_2), batch, rows, cols,
+        _ptr(w_out), _ptr(s_out), _ptr(gs), _stream(dev)))
+    return w_out, s_out, gs
+
+
+def dequantize(w: torch.Tensor, scales: torch.Tensor, gs: Optional[torch.Tensor] = None,
+               dtype=torch.float32) -> torch.Tensor:
+    """Exact expansion of a plane: [..., rows, cols/8] words -> [..., rows, cols].
+    gs (optional) holds one float32 global scale per matrix."""
+    check_planes(w, scales)
+    if w.dim() < 2:
+        raise ValueError("weight plane must be at least 2-D")
+    lead = tuple(w.shape[:-2])
+    rows, cols = w.shape[-2], w.shape[-1] * 8
+    batch = 1
+    for d in lead:
+        batch *= d
+    if gs is not None and (gs.dtype != torch.float32 or gs.numel() != batch):
+        raise ValueError("gs must be float32 with one value per matrix")
+    code = _dtype_code(dtype)
+    dev = _require_gpu(w, scales, gs)
+    lib = load_library()
+    out = torch.empty(lead + (rows, cols), dtype=dtype, device=dev)
+    _check("nvfp4_dequantize", lib.nvfp4_dequantize(
+        _ptr(w), _ptr(scales), _ptr(gs), batch, rows, cols, code, _ptr(out), _stream(dev)))
+    return out
+
+
+def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[torch.Tensor] = None,
+        transpose: bool = True, route: str = "auto", out: Optional[torch.Tensor] = None
+        ) -> torch.Tensor:
+    """out = x @ dequantize(w).T (transpose) or x @ dequantize(w).
+
+    x [..., K] (float32, bfloat16 or float16); w [N, K/8] (transpose) or
+    [K, N/8]; scales as for check_planes; gs float32 with one element or None.
+    The output has x's dtype and shape [..., N].
+    """
+    check_planes(w, scales)
+    if w.dim() != 2:
+        raise ValueError("qmm takes a 2-D weight plane")
+    if transpose:
+        N, K = w.shape[0], w.shape[1] * 8
+    else:
+        K, N = w.shape[0], w.shape[1] * 8
+    if x.shape[-1] != K:
+        raise ValueError(f"x has K={x.shape[-1]}, weight plane implies K={K}")
+    if gs is not None and (gs.dtype != torch.float32 or gs.numel() != 1):
+        raise ValueError("gs must be a float32 tensor with one element")
+    if route not in _ROUTES:
+        raise ValueError(f"route must be one of {sorted(_ROUTES)}")
+    code = _dtype_code(x.dtype)
+    M = 1
+    for d in x.shape[:-1]:
+        M *= d
+    dev = _require_gpu(x, w, scales, gs)
+    lib = load_library()
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=dev)
+    elif out.dtype != x.dtype or tuple(out.shape) != tuple(x.shape[:-1]) + (N,):
+        raise ValueError("out has the wrong dtype or shape")
+    _require_gpu(out)
+    _check("nvfp4_qmm", lib.nvfp4_qmm(
+        _ptr(x), code, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), int(bool(transpose)),
+        _ROUTES[route], _ptr(out), _stream(dev)))
+    return out
+
+
+def gather_qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
+               rhs_indices: torch.Tensor, lhs_indices: Optional[torch.Tensor] = None,
+               gs: Optional[torch.Tensor] = None, sorted_indices: bool = False,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GatherQMM over NVFP4 experts.
+
+    x [X, M, K]; w [E, N, K/8]; scales [E, N, K/16]; rhs_indices int32 [R]
+    (expert per pair); lhs_indices int32 [R] or None (pair r uses x[r]);
+    gs float32 [E] or None.  Returns [R, M, N] in x's dtype; pairs whose
+    expert or row index is out of range give +0.0.
+    """
+    check_planes(w, scales)
+    if w.dim() != 3 or x.dim() != 3:
+        raise ValueError("gather_qmm takes x [X, M, K] and w [E, N, K/8]")
+    E, N, K = w.shape[0], w.shape[1], w.shape[2] * 8
+    X, M = x.shape[0], x.shape[1]
+    if x.shape[2] != K:
+        raise ValueError(f"x has K={x.shape[2]}, weight plane implies K={K}")
+    if rhs_indices.dtype != torch.int32 or rhs_indices.dim() != 1:
+        raise ValueError("rhs_indices must be a 1-D int32 tensor")
+    R = rhs_indices.shape[0]
+    if lhs_indices is not None and (lhs_indices.dtype != torch.int32 or tuple(lhs_indices.shape) != (R,)):
+        raise ValueError("lhs_indices must be int32 shaped like rhs_indices")
+    if gs is not None and (gs.dtype != torch.float32 or gs.numel() != E):
+        raise ValueError("gs must be float32 with one value per expert")
+    code = _dtype_code(x.dtype)
+    dev = _require_gpu(x, w, scales, rhs_indices, lhs_indices, gs)
+    lib = load_library()
+    if out is None:
+        out = torch.empty((R, M, N), dtype=x.dtype, device=dev)
+    elif out.dtype != x.dtype or tuple(out.shape) != (R, M, N):
+        raise ValueError("out has the wrong dtype or shape")
+    _require_gpu(out)
+    _check("nvfp4_gather_qmm", lib.nvfp4_gather_qmm(
+        _ptr(x), code, X, M, K, _ptr(lhs_indices), _ptr(rhs_indices), R, _ptr(w), _ptr(scales),
+        _ptr(gs), E, N, int(bool(sorted_indices)), _ptr(out), _stream(dev)))
+    return out

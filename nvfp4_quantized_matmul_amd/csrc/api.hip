@@ -1,0 +1,174 @@
+// C ABI of libnvfp4: argument validation, route selection and launches.
+//
+// Every check runs on the host before anything is enqueued, mirroring the
+// plane checks of mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/
+// GatherQMM" ("Changes during review" and "Security and performance
+// review"): the scale plane is derived from the weight plane so the two
+// cannot disagree, the quantized axis must be a multiple of 16, grids are
+// bounded, and an empty output launches nothing.
+#include <cstdint>
+#include <cstring>
+
+#include "nvfp4_internal.hpp"
+
+namespace {
+
+// Crossover between the weight-streaming qmv kernels and the GEMM kernels
+// (the pages test qmv up to M = 33 and the GEMM route from M = 64).
+constexpr int64_t kQmvMaxRows = 33;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r) && *r >= 0; }
+
+bool size3(int64_t a, int64_t b, int64_t c, int64_t* r) {
+  int64_t t;
+  return mul_ok(a, b, &t) && mul_ok(t, c, r);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_dtype(int dt) { return dt == NVFP4_F32 || dt == NVFP4_BF16 || dt == NVFP4_F16; }
+
+int64_t dtype_size(nvfp4_dtype_t dt) { return dt == NVFP4_F32 ? 4 : 2; }
+
+int launched() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_version(void) { return (1 << 16) | 0; }
+
+int64_t nvfp4_qmv_max_rows(void) { return kQmvMaxRows; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULLPTR: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape (negative size, quantized axis not a multiple of 16, overflow or inconsistent optional arguments)";
+    case NVFP4_ERR_DTYPE: return "unknown or unsupported dtype";
+    case NVFP4_ERR_GRID: return "launch would exceed a HIP grid limit";
+    case NVFP4_ERR_ROUTE: return "the qmv route needs a transposed weight plane";
+    case NVFP4_ERR_UNSUPPORTED: return "request not implemented";
+    case NVFP4_ERR_HIP: return "HIP runtime error at launch";
+    case NVFP4_ERR_ALIGN: return "pointer not aligned as required";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_select_route(int64_t M, int64_t K, int64_t N, int transpose, nvfp4_dtype_t dtype) {
+  if (M < 0 || K < 0 || N < 0) return NVFP4_ERR_SHAPE;
+  if (transpose != 0 && transpose != 1) return NVFP4_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  if (transpose ? (K % 16) != 0 : (N % 16) != 0) return NVFP4_ERR_SHAPE;
+  if (!transpose) return NVFP4_ROUTE_GEMM;
+  return M <= kQmvMaxRows ? NVFP4_ROUTE_QMV : NVFP4_ROUTE_GEMM;
+}
+
+int nvfp4_transcode(const uint8_t* weight, const uint8_t* weight_scale, const float* weight_scale_2,
+                    int64_t batch, int64_t rows, int64_t cols, uint32_t* w_out, uint8_t* scales_out,
+                    float* gs_out, hipStream_t stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if ((weight_scale_2 == nullptr) != (gs_out == nullptr)) return NVFP4_ERR_SHAPE;
+  int64_t elems;
+  if (!size3(batch, rows, cols, &elems)) return NVFP4_ERR_SHAPE;
+  if (batch == 0) return NVFP4_OK;
+  if (weight_scale_2 && (!aligned(weight_scale_2, 4) || !aligned(gs_out, 4))) return NVFP4_ERR_ALIGN;
+  const int64_t wbytes = elems / 2, sbytes = elems / 16;
+  if (elems > 0) {
+    if (!weight || !weight_scale || !w_out || !scales_out) return NVFP4_ERR_NULLPTR;
+    if (!aligned(w_out, 4)) return NVFP4_ERR_ALIGN;
+    const void* wo = static_cast<const void*>(w_out);
+    if (wo != static_cast<const void*>(weight) && overlaps(wo, wbytes, weight, wbytes)) return NVFP4_ERR_SHAPE;
+    if (scales_out != weight_scale && overlaps(scales_out, sbytes, weight_scale, sbytes)) return NVFP4_ERR_SHAPE;
+  }
+  if (weight_scale_2 && overlaps(gs_out, batch * 4, weight_scale_2, batch * 4) &&
+      static_cast<const void*>(gs_out) != static_cast<const void*>(weight_scale_2))
+    return NVFP4_ERR_SHAPE;
+  nvfp4host::launch_copy_bytes(weight, reinterpret_cast<uint8_t*>(w_out), wbytes, stream);
+  nvfp4host::launch_copy_bytes(weight_scale, scales_out, sbytes, stream);
+  if (weight_scale_2) nvfp4host::launch_sidecar(weight_scale_2, gs_out, batch, stream);
+  return launched();
+}
+
+int nvfp4_dequantize(const uint32_t* w, const uint8_t* scales, const float* gs, int64_t batch,
+                     int64_t rows, int64_t cols, nvfp4_dtype_t out_dtype, void* out,
+                     hipStream_t stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!valid_dtype(out_dtype)) return NVFP4_ERR_DTYPE;
+  int64_t elems, bytes;
+  if (!size3(batch, rows, cols, &elems) || !mul_ok(elems, dtype_size(out_dtype), &bytes)) return NVFP4_ERR_SHAPE;
+  if (elems == 0) return NVFP4_OK;
+  if (!w || !scales || !out) return NVFP4_ERR_NULLPTR;
+  if (!aligned(w, 4) || !aligned(out, 16) || (gs && !aligned(gs, 4))) return NVFP4_ERR_ALIGN;
+  nvfp4host::launch_dequantize(w, scales, gs, batch, rows, cols, out_dtype, out, stream);
+  return launched();
+}
+
+int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N,
+              const uint32_t* w, const uint8_t* scales, const float* gs, int transpose,
+              nvfp4_route_t route, void* out, hipStream_t stream) {
+  const int auto_route = nvfp4_select_route(M, K, N, transpose, dtype);
+  if (auto_route < 0) return auto_route;
+  if (route != NVFP4_ROUTE_AUTO && route != NVFP4_ROUTE_QMV && route != NVFP4_ROUTE_GEMM) return NVFP4_ERR_ROUTE;
+  if (route == NVFP4_ROUTE_QMV && !transpose) return NVFP4_ERR_ROUTE;
+  int64_t t;
+  if (!mul_ok(M, K, &t) || !mul_ok(M, N, &t) || !mul_ok(K, N, &t)) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!out) return NVFP4_ERR_NULLPTR;
+  if (!aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  if (K == 0) {
+    nvfp4host::launch_fill_zero(out, M * N * dtype_size(dtype), stream);
+    return launched();
+  }
+  if (!x || !w || !scales) return NVFP4_ERR_NULLPTR;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scales, 2) || (gs && !aligned(gs, 4))) return NVFP4_ERR_ALIGN;
+  const int r = route == NVFP4_ROUTE_AUTO ? auto_route : (int)route;
+  if (r == NVFP4_ROUTE_QMV) {
+    if ((N + 15) / 16 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    nvfp4host::launch_qmv(x, dtype, M, K, N, w, scales, gs, out, stream);
+  } else if (dtype == NVFP4_BF16 && transpose && K % 32 == 0) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    nvfp4host::launch_gemm_mfma(x, M, K, N, w, scales, gs, out, stream);
+  } else {
+    if ((N + 63) / 64 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
+  }
+  return launched();
+}
+
+int nvfp4_gather_qmm(const void* x, nvfp4_dtype_t dtype, int64_t X, int64_t M, int64_t K,
+                     const int32_t* lhs, const int32_t* rhs, int64_t R, const uint32_t* w,
+                     const uint8_t* scales, const float* gs, int64_t E, int64_t N,
+                     int sorted_indices, void* out, hipStream_t stream) {
+  if (X < 0 || M < 0 || K < 0 || R < 0 || E < 0 || N < 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  int64_t t;
+  if (!size3(X, M, K, &t) || !size3(R, M, N, &t) || !size3(E, N, K, &t)) return NVFP4_ERR_SHAPE;
+  if (R == 0 || M == 0 || N == 0) return NVFP4_OK;
+  if (!rhs || !out) return NVFP4_ERR_NULLPTR;
+  if (!aligned(out, 16) || !aligned(rhs, 4) || (lhs && !aligned(lhs, 4))) return NVFP4_ERR_ALIGN;
+  if (K == 0) {
+    nvfp4host::launch_fill_zero(out, R * M * N * dtype_size(dtype), stream);
+    return launched();
+  }
+  if (!x && X > 0) return NVFP4_ERR_NULLPTR;
+  if ((!w || !scales) && E > 0) return NVFP4_ERR_NULLPTR;
+  if ((x && !aligned(x, 16)) || (w && !aligned(w, 16)) || (scales && !aligned(scales, 2)) ||
+      (gs && !aligned(gs, 4)))
+    return NVFP4_ERR_ALIGN;
+  if ((N + 15) / 16 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+  nvfp4host::launch_gather(x, dtype, X, M, K, lhs, rhs, R, w, scales, gs, E, N, sorted_indices ? 1 : 0,
+                           out, stream);
+  return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,326 @@
+// NVFP4 GEMM kernels for the large-M ("prefill") route.
+//
+// The pages' ROCm design (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/
+// GatherQMM", "Summary") dequantizes the whole plane and then calls a vendor
+// GEMM, applying the global scale after the matmul.  Here the dequantize is
+// fused into the GEMM instead, so no dense plane is written to HBM:
+//
+//  * gemm_mfma_kernel (bf16 activations, transposed plane, K % 32 == 0):
+//    each wavefront decodes its weight rows straight from the packed words
+//    into bf16 MFMA operands (one 32-bit word = the eight k-values one lane
+//    feeds to a 32x32x16 MFMA), while the activation tile is staged in LDS
+//    (double buffered) and shared by the four wavefronts.  Products
+//    e2m1 * e4m3 are exact in bf16, the MFMA accumulates in float32, and
+//    g = gs / 2688 multiplies each output once at the end.
+//  * gemm_generic_kernel: a float32 FMA tiled GEMM used for float32/f16
+//    activations and for non-transposed planes (quantized along N, any K),
+//    with both tiles decoded to float32 in LDS.
+#include "nvfp4_device.hpp"
+#include "nvfp4_internal.hpp"
+
+using namespace nvfp4dev;
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// MFMA kernel
+// ----------------------------------------------------------------------------
+
+constexpr int kBN = 256;       // weight rows (output columns) per block
+constexpr int kBM = 256;       // activation rows per block
+constexpr int kBK = 64;        // k per pipeline stage
+constexpr int kLdsK = kBK + 8; // padded LDS row (bf16 elements)
+constexpr int kMfmaThreads = 256;
+
+__global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_kernel(
+    const __bf16* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
+    const float* __restrict__ gs, __bf16* __restrict__ out, int64_t M, int64_t K, int64_t N,
+    int64_t tiles_m, int64_t tiles_total) {
+  __shared__ __attribute__((aligned(16))) __bf16 xs[2][kBM][kLdsK];
+
+  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs,
+  // so give each XCD a contiguous run of logical tiles (activation tiles
+  // fastest) and the tiles that share weight rows share that XCD's L2.
+  const int64_t per_xcd = (int64_t)gridDim.x / 8;
+  const int64_t logical = ((int64_t)blockIdx.x % 8) * per_xcd + (int64_t)blockIdx.x / 8;
+  if (logical >= tiles_total) return;  // whole block, before any barrier
+  const int64_t m_blk = (logical % tiles_m) * kBM;
+  const int64_t n_blk = (logical / tiles_m) * kBN;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t kw = K / 8, ks = K / 16;
+  const int64_t nslabs = (K + kBK - 1) / kBK;
+
+  // Weight rows fed by this lane, one per 32-row fragment.
+  int64_t wrow[4];
+  bool wok[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int64_t n = n_blk + wn * 128 + a * 32 + l32;
+    wok[a] = n < N;
+    wrow[a] = wok[a] ? n : 0;
+  }
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  uint4 xreg[8];
+  uint4 wcur[4], wnext[4];
+  uint32_t scur[4], snext[4];
+
+  // Activation slab [kBM][kBK] -> registers (zeros outside M or K).
+  auto load_x = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int lin = i * kMfmaThreads + t;
+      const int row = lin >> 3, col = (lin & 7) * 8;
+      const int64_t m = m_blk + row, k = k0 + col;
+      xreg[i] = (m < M && k < K) ? *reinterpret_cast<const uint4*>(x + m * K + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int lin = i * kMfmaThreads + t;
+      const int row = lin >> 3, col = (lin & 7) * 8;
+      *reinterpret_cast<uint4*>(&xs[buf][row][col]) = xreg[i];
+    }
+  };
+  // Weights: lane (row, h) takes words [4h, 4h+4) of the 8-word slab and
+  // the two scale bytes of those words (K % 32 == 0, so a lane's four words
+  // are all inside K or all outside).
+  auto load_w = [&](int64_t k0, uint4 (&wr)[4], uint32_t (&sr)[4]) {
+    const int64_t word0 = k0 / 8 + 4 * h;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      if (wok[a] && word0 < kw) {
+        wr[a] = *reinterpret_cast<const uint4*>(w + wrow[a] * kw + word0);
+        sr[a] = *reinterpret_cast<const uint16_t*>(sc + wrow[a] * ks + word0 / 2);
+      } else {
+        wr[a] = make_uint4(0, 0, 0, 0);
+        sr[a] = 0;
+      }
+    }
+  };
+
+  load_x(0);
+  load_w(0, wcur, scur);
+  store_x(0);
+  __syncthreads();
+
+  for (int64_t s = 0; s < nslabs; ++s) {
+    const int buf = (int)(s & 1);
+    const bool more = s + 1 < nslabs;
+    if (more) {
+      load_x((s + 1) * kBK);
+      load_w((s + 1) * kBK, wnext, snext);
+    }
+    float slo[4], shi[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      slo[a] = e4m3<0>(scur[a]);
+      shi[a] = e4m3<1>(scur[a]);
+    }
+    // MFMA step j: lane half h supplies word 4h+j, i.e. physical k in
+    // [8(4h+j), 8(4h+j)+8) of the slab; the activation operand reads the
+    // same k range, so the contraction covers every k exactly once.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8_t A[4], B[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t word = j == 0 ? wcur[a].x : j == 1 ? wcur[a].y : j == 2 ? wcur[a].z : wcur[a].w;
+        A[a] = decode_word_bf16(word, j < 2 ? slo[a] : shi[a]);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int row = wm * 128 + b * 32 + l32;
+        B[b] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][row][8 * (4 * h + j)]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) {
+      store_x(buf ^ 1);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        wcur[a] = wnext[a];
+        scur[a] = snext[a];
+      }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: C[n][m] fragment, lane holds n = 8*jj + 4h + i, m = l32.
+  const float g = global_factor(gs, 0);
+  const bool vec_ok = (N % 4) == 0;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t m = m_blk + wm * 128 + b * 32 + l32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t n = n_blk + wn * 128 + a * 32 + jj * 8 + h * 4;
+        __bf16 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[a][b][jj * 4 + i] * g);
+        __bf16* p = out + m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, v);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (n + i < N) p[i] = v[i];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Generic float32 kernel
+// ----------------------------------------------------------------------------
+
+constexpr int kGT = 64;   // output tile edge
+constexpr int kGK = 16;   // k per stage (one scale block)
+
+template <typename TX, bool TRANS>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(const TX* __restrict__ x,
+                                                           const uint32_t* __restrict__ w,
+                                                           const uint8_t* __restrict__ sc,
+                                                           const float* __restrict__ gs,
+                                                           TX* __restrict__ out, int64_t M,
+                                                           int64_t K, int64_t N) {
+  __shared__ float xs[kGK][kGT + 4];
+  __shared__ float ws[kGK][kGT + 4];
+  const int t = threadIdx.x;
+  const int tm = t >> 4, tn = t & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * kGT;
+  const float g = global_factor(gs, 0);
+
+  for (int64_t m0 = (int64_t)blockIdx.y * kGT; m0 < M; m0 += (int64_t)gridDim.y * kGT) {
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    for (int64_t k0 = 0; k0 < K; k0 += kGK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = i * 256 + t;
+        const int mm = e >> 4, kk = e & 15;
+        const int64_t m = m0 + mm, k = k0 + kk;
+        xs[kk][mm] = (m < M && k < K) ? load_x(x + m * K + k) : 0.0f;
+      }
+      if (t < 128) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+        if constexpr (TRANS) {
+          // plane [N, K/8]: row n, words k0/8 and k0/8 + 1 (K % 16 == 0)
+          const int nn = t >> 1, wi = t & 1;
+          const int64_t n = n0 + nn;
+          if (n < N) {
+            const float s = e4m3<0>(sc[n * (K / 16) + k0 / 16]);
+            decode_word_f32(w[n * (K / 8) + k0 / 8 + wi], s, v);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ws[wi * 8 + i][nn] = v[i];
+        } else {
+          // plane [K, N/8]: row k, words n0/8 .. n0/8 + 7 (N % 16 == 0)
+          const int kk = t >> 3, wi = t & 7;
+          const int64_t k = k0 + kk;
+          if (k < K && n0 + wi * 8 < N) {
+            const float s = e4m3<0>(sc[k * (N / 16) + n0 / 16 + wi / 2]);
+            decode_word_f32(w[k * (N / 8) + n0 / 8 + wi], s, v);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ws[kk][wi * 8 + i] = v[i];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kGK; ++kk) {
+        float a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] = xs[kk][tm * 4 + i];
+          b[i] = ws[kk][tn * 4 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + tm * 4 + i;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + tn * 4 + j;
+        if (n < N) store_out(out + m * N + n, acc[i][j] * g);
+      }
+    }
+  }
+}
+
+template <typename TX>
+void generic_dispatch(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                      const uint8_t* sc, const float* gs, int transpose, TX* out, hipStream_t s) {
+  const int64_t gx = (N + kGT - 1) / kGT;
+  int64_t gy = (M + kGT - 1) / kGT;
+  if (gy > nvfp4host::kMaxGridY) gy = nvfp4host::kMaxGridY;
+  if (transpose)
+    gemm_generic_kernel<TX, true><<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(x, w, sc, gs, out, M, K, N);
+  else
+    gemm_generic_kernel<TX, false><<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(x, w, sc, gs, out, M, K, N);
+}
+
+}  // namespace
+
+namespace nvfp4host {
+
+void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                      const uint8_t* sc, const float* gs, void* out, hipStream_t s) {
+  const int64_t tiles_m = (M + kBM - 1) / kBM;
+  const int64_t tiles_n = (N + kBN - 1) / kBN;
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t grid = (tiles + 7) / 8 * 8;
+  gemm_mfma_kernel<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+      static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
+}
+
+void launch_gemm_generic(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
+                         const uint32_t* w, const uint8_t* sc, const float* gs, int transpose,
+                         void* out, hipStream_t s) {
+  switch (dt) {
+    case NVFP4_F32:
+      generic_dispatch<float>((const float*)x, M, K, N, w, sc, gs, transpose, (float*)out, s);
+      break;
+    case NVFP4_BF16:
+      generic_dispatch<__bf16>((const __bf16*)x, M, K, N, w, sc, gs, transpose, (__bf16*)out, s);
+      break;
+    case NVFP4_F16:
+      generic_dispatch<_Float16>((const _Float16*)x, M, K, N, w, sc, gs, transpose, (_Float16*)out, s);
+      break;
+  }
+}
+
+}  // namespace nvfp4host

@@ -1,0 +1,43 @@
+// Internal host-side launchers shared between the C-ABI layer and the kernel
+// translation units.  Every launcher assumes its arguments were validated by
+// the C-ABI layer (shapes, alignment, grid limits) and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4host {
+
+// Byte copy dst <- src of n bytes (dst == src is a no-op).
+void launch_copy_bytes(const uint8_t* src, uint8_t* dst, int64_t n, hipStream_t s);
+// Zero n bytes at dst (16-byte aligned), with a kernel rather than a memset
+// so the call is safe inside captured graphs.
+void launch_fill_zero(void* dst, int64_t n, hipStream_t s);
+// gs_out[b] = fl32(ws2[b] * 2688).
+void launch_sidecar(const float* ws2, float* gs_out, int64_t batch, hipStream_t s);
+// Dequantize [batch*rows, cols/8] words into out of dtype.
+void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, int64_t batch,
+                       int64_t rows, int64_t cols, nvfp4_dtype_t dt, void* out, hipStream_t s);
+// Dense qmv: out[M,N] = x[M,K] @ W[N,K]^T (transposed plane).
+void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
+                const uint32_t* w, const uint8_t* sc, const float* gs, void* out, hipStream_t s);
+// MFMA GEMM, bf16 activations, transposed plane.
+void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                      const uint8_t* sc, const float* gs, void* out, hipStream_t s);
+// Generic float32-accumulating GEMM for any dtype and either plane layout.
+void launch_gemm_generic(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
+                         const uint32_t* w, const uint8_t* sc, const float* gs, int transpose,
+                         void* out, hipStream_t s);
+// GatherQMM over experts.
+void launch_gather(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t M, int64_t K,
+                   const int32_t* lhs, const int32_t* rhs, int64_t R, const uint32_t* w,
+                   const uint8_t* sc, const float* gs, int64_t E, int64_t N, int sorted,
+                   void* out, hipStream_t s);
+
+// Grid limits used by the launchers (HIP: gridDim.x < 2^31, y/z < 2^16).
+constexpr int64_t kMaxGridX = 2147483647LL;
+constexpr int64_t kMaxGridY = 65535;
+
+}  // namespace nvfp4host

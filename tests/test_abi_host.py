@@ -1,0 +1,144 @@
+"""Host-side checks of libnvfp4 that need no GPU.
+
+The library must load on a machine without a GPU, export every function
+declared in include/nvfp4.h, and reject invalid requests on the host before
+anything is launched.  No call here reaches a kernel launch.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import nvfp4_quantized_matmul_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, NULLPTR, SHAPE, DTYPE, GRID, ROUTE, UNSUP, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F32, BF16, F16 = 0, 1, 2
+P = ctypes.c_void_p
+FAKE = P(0x100000)       # never dereferenced: every call below fails validation first
+MISALIGNED = P(0x100004)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_qmm", "nvfp4_gather_qmm",
+                 "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.nvfp4_version() >> 16 == 1
+    for code in (OK, NULLPTR, SHAPE, DTYPE, GRID, ROUTE, UNSUP, HIP, ALIGN):
+        s = nv.status_string(code)
+        assert s and s != "unknown status"
+    assert nv.status_string(12345) == "unknown status"
+
+
+def test_route_selection(lib):
+    assert nv.qmv_max_rows() == 33
+    assert nv.select_route(1, 5376, 21504) == "qmv"
+    assert nv.select_route(33, 4096, 14336, dtype=torch.float32) == "qmv"
+    assert nv.select_route(34, 4096, 14336) == "gemm"
+    assert nv.select_route(2048, 5376, 21504) == "gemm"
+    # non-transposed planes always take the GEMM route, any K, N % 16 == 0
+    assert nv.select_route(1, 17, 32, transpose=False) == "gemm"
+    assert lib.nvfp4_select_route(1, 17, 32, 1, BF16) == SHAPE      # quantized axis K=17
+    assert lib.nvfp4_select_route(1, 17, 24, 0, BF16) == SHAPE      # quantized axis N=24
+    assert lib.nvfp4_select_route(-1, 16, 16, 1, BF16) == SHAPE
+    assert lib.nvfp4_select_route(1, 16, 16, 2, BF16) == SHAPE
+    assert lib.nvfp4_select_route(1, 16, 16, 1, 7) == DTYPE
+
+
+def qmm(lib, x=FAKE, dt=BF16, M=4, K=64, N=32, w=FAKE, s=FAKE, gs=None, tr=1, route=0, out=FAKE):
+    return lib.nvfp4_qmm(x, dt, M, K, N, w, s, gs, tr, route, out, None)
+
+
+def test_qmm_validation(lib):
+    assert qmm(lib, x=None) == NULLPTR
+    assert qmm(lib, w=None) == NULLPTR
+    assert qmm(lib, s=None) == NULLPTR
+    assert qmm(lib, out=None) == NULLPTR
+    assert qmm(lib, K=24) == SHAPE                      # quantized axis not a multiple of 16
+    assert qmm(lib, M=-1) == SHAPE
+    assert qmm(lib, dt=9) == DTYPE
+    assert qmm(lib, tr=0, route=1, K=17) == ROUTE       # qmv needs a transposed plane
+    assert qmm(lib, route=5) == ROUTE
+    assert qmm(lib, x=MISALIGNED) == ALIGN
+    assert qmm(lib, w=MISALIGNED) == ALIGN
+    assert qmm(lib, out=MISALIGNED) == ALIGN
+    assert qmm(lib, s=P(0x100001)) == ALIGN
+    assert qmm(lib, gs=P(0x100002)) == ALIGN
+    assert qmm(lib, M=1 << 40, K=1 << 40) == SHAPE      # size overflow
+    # empty outputs launch nothing and succeed, even with NULL buffers
+    assert qmm(lib, M=0, x=None, w=None, s=None, out=None) == OK
+    assert qmm(lib, N=0, x=None, w=None, s=None, out=None) == OK
+
+
+def gather(lib, x=FAKE, dt=BF16, X=2, M=1, K=64, lhs=None, rhs=FAKE, R=4, w=FAKE, s=FAKE,
+           gs=None, E=3, N=32, out=FAKE):
+    return lib.nvfp4_gather_qmm(x, dt, X, M, K, lhs, rhs, R, w, s, gs, E, N, 0, out, None)
+
+
+def test_gather_validation(lib):
+    assert gather(lib, rhs=None) == NULLPTR
+    assert gather(lib, out=None) == NULLPTR
+    assert gather(lib, x=None) == NULLPTR
+    assert gather(lib, w=None) == NULLPTR
+    assert gather(lib, K=40) == SHAPE
+    assert gather(lib, E=-1) == SHAPE
+    assert gather(lib, dt=5) == DTYPE
+    assert gather(lib, rhs=P(0x100002)) == ALIGN
+    assert gather(lib, lhs=P(0x100002)) == ALIGN
+    assert gather(lib, x=MISALIGNED) == ALIGN
+    assert gather(lib, R=0, x=None, rhs=None, w=None, s=None, out=None) == OK
+
+
+def test_dequantize_and_transcode_validation(lib):
+    d = lib.nvfp4_dequantize
+    assert d(FAKE, FAKE, None, 1, 4, 24, F32, FAKE, None) == SHAPE
+    assert d(FAKE, FAKE, None, 1, 4, 32, 9, FAKE, None) == DTYPE
+    assert d(None, FAKE, None, 1, 4, 32, F32, FAKE, None) == NULLPTR
+    assert d(FAKE, FAKE, None, 1, 4, 32, F32, MISALIGNED, None) == ALIGN
+    assert d(None, None, None, 0, 4, 32, F32, None, None) == OK
+    t = lib.nvfp4_transcode
+    assert t(FAKE, FAKE, None, 1, 4, 24, FAKE, FAKE, None, None) == SHAPE
+    # weight_scale_2 and gs_out must be given together
+    assert t(FAKE, FAKE, FAKE, 1, 4, 32, P(0x200000), P(0x300000), None, None) == SHAPE
+    assert t(None, FAKE, None, 1, 4, 32, FAKE, FAKE, None, None) == NULLPTR
+    # a partially overlapping output is refused (exact aliasing is allowed)
+    assert t(P(0x100000), FAKE, None, 1, 4, 32, P(0x100010), P(0x300000), None, None) == SHAPE
+    assert t(None, None, None, 0, 4, 32, None, None, None, None) == OK
+
+
+def test_binding_checks_planes_before_touching_the_gpu():
+    w = torch.zeros((8, 4), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        nv.qmm(torch.zeros((1, 32)), w, torch.zeros((8, 3), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        nv.gather_qmm(torch.zeros((1, 1, 32)), w.view(1, 8, 4), torch.zeros((1, 8, 3), dtype=torch.uint8),
+                      torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        nv.dequantize(w, torch.zeros((8, 2), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        nv.qmm(torch.zeros((1, 32)), w, torch.zeros((8, 2), dtype=torch.uint8))   # CPU tensors

@@ -1,0 +1,397 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars: transcode and dequantize bit-exact; qmm / gather with float32 output
+max|err|/max|ref| <= 1e-5; bf16 (and f16) output <= 1e-2.  Inputs are the
+seeded synthetic workloads of nvfp4_synth; full-size workloads are checked
+on sampled outputs that the oracle computes directly.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantized_matmul_amd as nv
+import nvfp4_synth as synth
+import oracle
+from gpu_util import DEV, TOL, activations, f32, guarded, host, i32, u8, words
+
+pytestmark = pytest.mark.gpu
+
+INT32_MAX = 2 ** 31 - 1
+
+
+def rel(out_t, ref):
+    return oracle.relative_error(host(out_t), ref)
+
+
+def bits32(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def same_f32(got, want):
+    """Bit equality, treating any NaN as equal to any NaN."""
+    got = np.asarray(got, dtype=np.float32)
+    want = np.asarray(want, dtype=np.float32)
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn)
+    assert np.array_equal(bits32(got[~gn]), bits32(want[~wn]))
+
+
+# ----------------------------------------------------------------------------
+# transcode
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,rows,cols,with_ws2", [
+    (None, 512, 1024, False),   # the tiny workload's U8 [512, 512] source
+    (None, 512, 1024, True),
+    (3, 40, 96, True),
+    (2, 7, 16, True),
+])
+def test_transcode_bit_exact(batch, rows, cols, with_ws2):
+    g = synth.rng(100 + rows + cols)
+    wu8, ws, ws2 = synth.modelopt_triplet(g, batch or 1, rows, cols, with_ws2=with_ws2,
+                                          code_range=synth.FINITE_POSITIVE_CODES)
+    if batch is None:
+        wu8, ws = wu8[0], ws[0]
+    want_w, want_s, want_gs = oracle.transcode(wu8, ws, ws2)
+    w, s, gs = nv.transcode(u8(wu8), u8(ws), None if ws2 is None else f32(ws2))
+    torch.cuda.synchronize()
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), want_w)
+    assert np.array_equal(s.cpu().numpy(), want_s)
+    if with_ws2:
+        assert np.array_equal(bits32(gs.cpu().numpy()), bits32(want_gs))
+    else:
+        assert gs is None
+
+
+def test_transcode_in_place_and_guard_bands():
+    g = synth.rng(120)
+    wu8, ws, ws2 = synth.modelopt_triplet(g, 2, 33, 64)
+    want_w, want_s, want_gs = oracle.transcode(wu8, ws, ws2)
+    src_w, src_s = u8(wu8), u8(ws)
+    w, s, gs = nv.transcode(src_w, src_s, f32(ws2), inplace=True)
+    torch.cuda.synchronize()
+    assert w.data_ptr() == src_w.data_ptr() and s.data_ptr() == src_s.data_ptr()
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), want_w)
+    assert np.array_equal(s.cpu().numpy(), want_s)
+    # out-of-place through the C ABI with guarded outputs
+    lib = nv.load_library()
+    w_out, chk_w = guarded((2, 33, 8), torch.int32, fill=0x5A5A5A5A)
+    s_out, chk_s = guarded((2, 33, 4), torch.uint8)
+    g_out, chk_g = guarded((2,), torch.float32)
+    # keep the device inputs referenced until the kernel has run
+    d_w, d_s, d_g = u8(wu8), u8(ws), f32(ws2)
+    st = lib.nvfp4_transcode(ctypes.c_void_p(d_w.data_ptr()), ctypes.c_void_p(d_s.data_ptr()),
+                             ctypes.c_void_p(d_g.data_ptr()), 2, 33, 64,
+                             ctypes.c_void_p(w_out.data_ptr()), ctypes.c_void_p(s_out.data_ptr()),
+                             ctypes.c_void_p(g_out.data_ptr()), None)
+    assert st == 0
+    chk_w(); chk_s(); chk_g()
+    assert np.array_equal(w_out.cpu().numpy().view(np.uint32), want_w)
+    assert np.array_equal(bits32(g_out.cpu().numpy()), bits32(want_gs))
+
+
+# ----------------------------------------------------------------------------
+# dequantize
+# ----------------------------------------------------------------------------
+
+def every_pair_plane():
+    w = np.tile(np.array([0x76543210, 0xFEDCBA98], dtype=np.uint32), (256, 1))
+    scales = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    return w, scales
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("gs", [None, 777.25, 0.5, 2688.0])
+def test_dequantize_every_pair_bit_exact(dtype, gs):
+    w, sc = every_pair_plane()
+    want = oracle.dequantize(w, sc, None if gs is None else np.float32(gs))
+    out = nv.dequantize(words(w), u8(sc), None if gs is None else f32([gs]), dtype=dtype)
+    torch.cuda.synchronize()
+    if dtype == torch.float32:
+        same_f32(out.cpu().numpy(), want)
+    elif dtype == torch.bfloat16:
+        got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+        exp = oracle.f32_to_bf16_bits(want)
+        nan = np.isnan(want)
+        assert np.array_equal(got[~nan], exp[~nan])
+        assert np.all(np.isnan(oracle.bf16_bits_to_f32(got[nan])))
+    else:
+        got = out.cpu().numpy()
+        exp = want.astype(np.float16)
+        nan = np.isnan(want)
+        assert np.array_equal(got[~nan].view(np.uint16), exp[~nan].view(np.uint16))
+        assert np.all(np.isnan(got[nan]))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_batched_ragged_with_guard_bands(dtype):
+    g = synth.rng(130)
+    w = synth.packed_words(g, (3, 37, 6))
+    sc = synth.scale_codes(g, (3, 37, 3), synth.FINITE_POSITIVE_CODES)
+    gs = synth.global_scales(g, 3)
+    want = np.stack([oracle.dequantize(w[b], sc[b], gs[b]) for b in range(3)])
+    lib = nv.load_library()
+    out, check = guarded((3, 37, 48), dtype)
+    d_w, d_s, d_g = words(w), u8(sc), f32(gs)
+    st = lib.nvfp4_dequantize(ctypes.c_void_p(d_w.data_ptr()), ctypes.c_void_p(d_s.data_ptr()),
+                              ctypes.c_void_p(d_g.data_ptr()), 3, 37, 48,
+                              0 if dtype == torch.float32 else 1, ctypes.c_void_p(out.data_ptr()), None)
+    assert st == 0
+    check()
+    if dtype == torch.float32:
+        same_f32(out.cpu().numpy(), want)
+    else:
+        assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16),
+                              oracle.f32_to_bf16_bits(want))
+
+
+def test_dequantize_decode_row_length_bit_exact():
+    """Rows of the decode workload's length (K = 5376), 2048 of them."""
+    g = synth.rng(131)
+    w = synth.packed_words(g, (2048, 672))
+    sc = synth.scale_codes(g, (2048, 336))
+    gs = synth.global_scales(g, 1)
+    want = oracle.dequantize(w, sc, gs[0])
+    out = nv.dequantize(words(w), u8(sc), f32(gs))
+    same_f32(out.cpu().numpy(), want)
+
+
+# ----------------------------------------------------------------------------
+# qmm
+# ----------------------------------------------------------------------------
+
+def run_qmm(case, dtype, route="auto", guard=False):
+    x_t, x_ref = activations(case.x, dtype)
+    gs = None if case.gs is None else case.gs[0]
+    ref = oracle.qmm(x_ref, case.w, case.scales, gs, transpose=case.transpose)
+    out = check = None
+    if guard:
+        out, check = guarded((case.M, case.N), dtype)
+    out = nv.qmm(x_t, words(case.w), u8(case.scales), None if case.gs is None else f32(case.gs),
+                 transpose=case.transpose, route=route, out=out)
+    torch.cuda.synchronize()
+    if check:
+        check()
+    return out, ref
+
+
+@pytest.mark.parametrize("route", ["auto", "qmv", "gemm"])
+def test_tiny_qmv_f32(route):
+    """M=1, K=1024, N=512, float32, no global scale, every finite positive
+    scale code (including subnormal scales)."""
+    w = synth.WORKLOADS["tiny_qmv_m1_k1024_n512_f32"]
+    case = synth.dense_case(w["seed"], 1, 1024, 512, with_gs=False, code_range=w["codes"])
+    out, ref = run_qmm(case, torch.float32, route, guard=True)
+    assert rel(out, ref) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("route", ["auto", "gemm"])
+def test_decode_qmv_full_size(route):
+    """M=1, K=5376, N=21504, bf16 activations and output, scalar global
+    scale -- the decode workload in the launch configuration that is timed."""
+    w = synth.WORKLOADS["decode_qmv_m1_k5376_n21504_bf16"]
+    case = synth.dense_case(w["seed"], 1, 5376, 21504, with_gs=True)
+    out, ref = run_qmm(case, torch.bfloat16, route)
+    assert rel(out, ref) <= TOL[torch.bfloat16]
+
+
+@pytest.fixture(scope="module")
+def multirow_plane():
+    w = synth.WORKLOADS["multirow_qmv_k4096_n14336"]
+    case = synth.dense_case(w["seed"], 33, 4096, 14336, with_gs=True)
+    W = oracle.dequantize(case.w, case.scales, case.gs[0]).astype(np.float64)
+    return case, W
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("M", [3, 6, 16, 33])
+def test_multirow_qmv_full_size(multirow_plane, M, dtype):
+    case, W = multirow_plane
+    x_t, x_ref = activations(case.x[:M], dtype)
+    ref = x_ref.astype(np.float64) @ W.T          # == oracle.qmm on the same planes
+    out = nv.qmm(x_t, words(case.w), u8(case.scales), f32(case.gs))
+    assert nv.select_route(M, 4096, 14336, dtype=dtype) == "qmv"
+    assert rel(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("M", [1, 3, 33, 64])
+@pytest.mark.parametrize("route", ["qmv", "gemm"])
+def test_partial_block_n272(M, dtype, route):
+    case = synth.dense_case(3100 + M, M, 4096, 272, with_gs=True)
+    out, ref = run_qmm(case, dtype, route, guard=True)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("M", [1, 3, 6, 16, 33])
+@pytest.mark.parametrize("with_gs", [False, True])
+def test_non_transposed_k17(M, dtype, with_gs):
+    case = synth.dense_case(3200 + M, M, 17, 32, transpose=False, with_gs=with_gs)
+    out, ref = run_qmm(case, dtype, "auto", guard=True)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("shape", [(300, 1056, 600), (64, 512, 272), (5, 48, 40), (7, 64, 263),
+                                   (257, 96, 520), (1, 16, 16)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("route", ["qmv", "gemm"])
+def test_ragged_shapes(shape, dtype, route):
+    M, K, N = shape
+    case = synth.dense_case(3300 + M + K + N, M, K, N, with_gs=True)
+    out, ref = run_qmm(case, dtype, route, guard=True)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+def test_prefill_gemm_full_size_sampled():
+    """M=2048, K=5376, N=21504 bf16 through the route that is timed; 48
+    sampled activation rows (spread over all row tiles) against the oracle."""
+    wl = synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]
+    case = synth.dense_case(wl["seed"], 2048, 5376, 21504, with_gs=True)
+    assert nv.select_route(2048, 5376, 21504) == "gemm"
+    x_t, x_ref = activations(case.x, torch.bfloat16)
+    out = nv.qmm(x_t, words(case.w), u8(case.scales), f32(case.gs))
+    rows = np.unique(np.concatenate([np.arange(0, 2048, 47), [1, 255, 256, 1023, 2047]]))
+    ref = oracle.qmm(x_ref[rows], case.w, case.scales, case.gs[0])
+    got = host(out)[rows]
+    assert oracle.relative_error(got, ref) <= TOL[torch.bfloat16]
+
+
+def test_global_scale_2688_is_identity():
+    case = synth.dense_case(3400, 4, 256, 96, with_gs=False)
+    x_t, _ = activations(case.x, torch.float32)
+    for route in ("qmv", "gemm"):
+        a = nv.qmm(x_t, words(case.w), u8(case.scales), None, route=route)
+        b = nv.qmm(x_t, words(case.w), u8(case.scales), f32([2688.0]), route=route)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("route", ["qmv", "gemm"])
+def test_nan_scale_propagates_to_its_output_only(route):
+    case = synth.dense_case(3500, 2, 128, 64, with_gs=True)
+    sc = case.scales.copy()
+    sc[5, 3] = 0x7F
+    x_t, x_ref = activations(case.x, torch.bfloat16)
+    out = host(nv.qmm(x_t, words(case.w), u8(sc), f32(case.gs), route=route))
+    assert np.all(np.isnan(out[:, 5]))
+    assert not np.any(np.isnan(np.delete(out, 5, axis=1)))
+
+
+def test_zero_k_gives_zeros():
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((8, 0), dtype=torch.int32, device=DEV)
+    s = torch.zeros((8, 0), dtype=torch.uint8, device=DEV)
+    out = nv.qmm(x, w, s)
+    assert torch.equal(out.float().cpu(), torch.zeros((3, 8)))
+
+
+# ----------------------------------------------------------------------------
+# gather
+# ----------------------------------------------------------------------------
+
+def run_gather(case, dtype, lhs=True, sorted_flag=None, guard=False):
+    x_t, x_ref = activations(case.x, dtype)
+    lhs_np = case.lhs if lhs else None
+    ref = oracle.gather_qmm(x_ref, lhs_np, case.rhs, case.w, case.scales, case.gs)
+    R = case.rhs.shape[0]
+    out = check = None
+    if guard:
+        out, check = guarded((R, case.M, case.N), dtype)
+    out = nv.gather_qmm(x_t, words(case.w), u8(case.scales), i32(case.rhs),
+                        None if lhs_np is None else i32(lhs_np),
+                        None if case.gs is None else f32(case.gs),
+                        sorted_indices=case.sorted_indices if sorted_flag is None else sorted_flag,
+                        out=out)
+    torch.cuda.synchronize()
+    if check:
+        check()
+    return out, ref
+
+
+def assert_zero_rows(out_t, rhs, lhs, E, X):
+    got = out_t.float().cpu().numpy()
+    for r in range(len(rhs)):
+        src = r if lhs is None else int(lhs[r])
+        if not (0 <= int(rhs[r]) < E) or not (0 <= src < X):
+            assert np.all(got[r] == 0.0) and not np.any(np.signbit(got[r])), r
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("sort", [False, True])
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("with_gs", [False, True])
+@pytest.mark.parametrize("K", [96, 48])
+def test_gather_small_full(dtype, sort, M, with_gs, K):
+    case = synth.gather_case(5100 + M + K, tokens=5, E=6, N=80, K=K, top_k=2, sort=sort,
+                             with_gs=with_gs, M=M, out_of_range=(6, 7, INT32_MAX, -1))
+    out, ref = run_gather(case, dtype, guard=True)
+    assert oracle.relative_error(host(out), ref) <= TOL[dtype]
+    assert_zero_rows(out, case.rhs, case.lhs, 6, 5)
+
+
+def test_gather_lhs_out_of_range_and_identity_lhs():
+    case = synth.gather_case(5200, tokens=4, E=5, N=48, K=64, top_k=1, sort=False, M=2)
+    case.lhs = case.lhs.copy()
+    case.lhs[1] = 4            # x has 4 rows: out of range
+    case.lhs[2] = -3
+    out, ref = run_gather(case, torch.float32, guard=True)
+    assert oracle.relative_error(host(out), ref) <= 1e-5
+    assert_zero_rows(out, case.rhs, case.lhs, 5, 4)
+    out, ref = run_gather(case, torch.float32, lhs=False)
+    assert oracle.relative_error(host(out), ref) <= 1e-5
+
+
+def test_gather_sorted_hint_on_unsorted_indices():
+    case = synth.gather_case(5300, tokens=9, E=4, N=64, K=128, top_k=3, sort=False, M=1)
+    a, ref = run_gather(case, torch.bfloat16, sorted_flag=True)
+    b, _ = run_gather(case, torch.bfloat16, sorted_flag=False)
+    assert oracle.relative_error(host(a), ref) <= 1e-2
+    assert oracle.relative_error(host(b), ref) <= 1e-2
+
+
+def moe_reference_sampled(case, x_ref, experts):
+    """Rows of the given in-range experts, computed expert by expert with the
+    oracle's qmm (gather semantics themselves are pinned on small cases)."""
+    rows, refs = [], []
+    for e in experts:
+        rr = np.nonzero(case.rhs == e)[0]
+        if len(rr) == 0:
+            continue
+        xs = x_ref[case.lhs[rr], 0, :]
+        refs.append(oracle.qmm(xs, case.w[e], case.scales[e], case.gs[e]))
+        rows.append(rr)
+    return np.concatenate(rows), np.concatenate(refs)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_moe_sorted_prefill_full_size(dtype):
+    wl = synth.WORKLOADS["moe_gather_e128_n1536_k2048_top8"]
+    case = synth.gather_case(wl["seed"], tokens=128, E=128, N=1536, K=2048, top_k=8, sort=True,
+                             with_gs=True, out_of_range=(128, 129, INT32_MAX))
+    x_t, x_ref = activations(case.x, dtype)
+    out = nv.gather_qmm(x_t, words(case.w), u8(case.scales), i32(case.rhs), i32(case.lhs),
+                        f32(case.gs), sorted_indices=True)
+    experts = np.unique(case.rhs[(case.rhs >= 0) & (case.rhs < 128)])
+    pick = experts[np.linspace(0, len(experts) - 1, 10).astype(int)]
+    rows, ref = moe_reference_sampled(case, x_ref, pick)
+    got = host(out)[rows, 0, :]
+    assert oracle.relative_error(got, ref) <= TOL[dtype]
+    assert_zero_rows(out, case.rhs, case.lhs, 128, 128)
+
+
+@pytest.mark.parametrize("tokens", [1, 2, 4, 8])
+def test_moe_unsorted_decode_full_size(tokens):
+    wl = synth.WORKLOADS["moe_gather_e128_n1536_k2048_top8"]
+    case = synth.gather_case(wl["seed"] + tokens, tokens=tokens, E=128, N=1536, K=2048, top_k=8,
+                             sort=False, with_gs=True, out_of_range=(128, INT32_MAX) if tokens > 1 else ())
+    x_t, x_ref = activations(case.x, torch.bfloat16)
+    out = nv.gather_qmm(x_t, words(case.w), u8(case.scales), i32(case.rhs), i32(case.lhs),
+                        f32(case.gs), sorted_indices=False)
+    experts = np.unique(case.rhs[(case.rhs >= 0) & (case.rhs < 128)])
+    rows, ref = moe_reference_sampled(case, x_ref, experts)
+    got = host(out)[rows, 0, :]
+    assert oracle.relative_error(got, ref) <= TOL[torch.bfloat16]
+    assert_zero_rows(out, case.rhs, case.lhs, 128, tokens)
