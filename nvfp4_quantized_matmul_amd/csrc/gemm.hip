@@ -191,6 +191,217 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// MFMA kernel, K % 64 == 0: weight rows split across the wavefronts, all
+// operands streamed global -> LDS by the gfx950 load-to-LDS path.
+//
+// Block tile: 256 weight rows x 256 activation rows, k in slabs of 64.
+// Wavefront w owns weight rows [64w, 64w+64) of the tile and all 256
+// activation rows, so every packed weight word is decoded exactly once per
+// block (into the A operand of two 32x32x16 MFMAs) and feeds 8 activation
+// fragments.  Per slab, each wavefront issues 11 direct-to-LDS loads (8 of
+// activations, 2 of packed weights, 1 of scale bytes) and nothing passes
+// through registers on the way.  Three LDS stages keep two slabs in flight
+// while a third is multiplied; a stage is released by an explicit wait on
+// the vector-memory counter followed by a plain barrier (a fenced
+// __syncthreads would drain the prefetches).  The activation and weight
+// tiles keep their 16-byte chunks XOR-swizzled by row, which keeps the
+// fragment reads free of bank conflicts without padding.
+// ----------------------------------------------------------------------------
+
+constexpr int kV3BN = 256;
+constexpr int kV3BM = 256;
+constexpr int kV3BK = 64;
+constexpr int kV3LoadsPerSlab = 11;   // direct-to-LDS loads per wavefront per slab
+
+// One pipeline stage in LDS: the activation tile (256 rows x 8 swizzled
+// 16-byte chunks, 32 KiB), the packed words (256 rows x 32 bytes, 8 KiB)
+// and the scale bytes (256 rows x 4 bytes, 1 KiB) of one slab.  Each part is
+// its own __shared__ array so the compiler can tell a stage being read from
+// the stages being filled and does not wait for those loads.
+struct V3Stage {
+  uint4* x;
+  uint4* w;
+  uint32_t* s;
+};
+
+#define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Bank-conflict-free placement of 16-byte chunks: the 16 lanes served in
+// one LDS cycle (consecutive rows, same chunk) land in 16 distinct 16-byte
+// bank groups of 256 bytes, and any 8 consecutive rows in 8 distinct groups
+// of 128 bytes.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int xslot(int row, int chunk) { return row * 8 + (chunk ^ swz(row)); }
+__device__ __forceinline__ int wslot(int row, int half) { return row * 2 + (half ^ ((row >> 3) & 1)); }
+
+// vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
+__device__ __forceinline__ void wait_vmem(bool keep_one_slab) {
+  if (keep_one_slab)
+    __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | kV3LoadsPerSlab);
+  else
+    __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | 0);
+}
+
+struct V3Src {
+  const __bf16* x[8];        // activation chunk per x load, slab 0
+  const uint32_t* w[2];      // packed-word chunk per weight load, slab 0
+  const uint8_t* s;          // scale bytes, slab 0
+};
+
+__device__ __forceinline__ void v3_issue(const V3Stage& st, const V3Src& src, int64_t slab, int wave) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(src.x[i] + slab * kV3BK, NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds(src.w[i] + slab * 8, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src.s + slab * 4, NVFP4_LDS(&st.s[wave * 64]), 4, 0, 0);
+}
+
+// Four 32x32x16 steps over one slab: lane half h supplies word 4h+j (k in
+// [8(4h+j), 8(4h+j)+8)) and the activation fragment reads the same chunk.
+__device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave,
+                                           int l32, int h) {
+  uint4 wr[2];
+  float slo[2], shi[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int row = wave * 64 + a * 32 + l32;
+    wr[a] = st.w[wslot(row, h)];
+    const uint32_t sv = st.s[row] >> (16 * h);
+    slo[a] = e4m3<0>(sv);
+    shi[a] = e4m3<1>(sv);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8_t A[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
+      A[a] = decode_word_bf16(word, j < 2 ? slo[a] : shi[a]);
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bf16x8_t B = __builtin_bit_cast(bf16x8_t, st.x[xslot(b * 32 + l32, 4 * h + j)]);
+      acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0], B, acc[0][b], 0, 0, 0);
+      acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1], B, acc[1][b], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
+    const __bf16* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
+    const float* __restrict__ gs, __bf16* __restrict__ out, int64_t M, int64_t K, int64_t N,
+    int64_t tiles_m, int64_t tiles_total) {
+  __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
+  __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2];
+  __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN];
+  const V3Stage st0{x0, w0, s0}, st1{x1, w1, s1}, st2{x2, w2, s2};
+
+  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
+  // each XCD gets a contiguous run of logical tiles (activation tiles
+  // fastest), so the tiles sharing weight rows share that XCD's L2.
+  const int64_t per_xcd = (int64_t)gridDim.x / 8;
+  const int64_t logical = ((int64_t)blockIdx.x % 8) * per_xcd + (int64_t)blockIdx.x / 8;
+  if (logical >= tiles_total) return;  // whole block, before any barrier
+  const int64_t m_blk = (logical % tiles_m) * kV3BM;
+  const int64_t n_blk = (logical / tiles_m) * kV3BN;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t kw = K / 8, ks = K / 16;
+  const int64_t nslabs = K / kV3BK;
+
+  // Source addresses of this lane's loads for slab 0.  Rows past M or N
+  // re-read the last row (their results are never stored).
+  V3Src src;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = (i * 4 + wave) * 64 + lane;
+    const int r = slot >> 3, c = (slot & 7) ^ swz(r);
+    int64_t m = m_blk + r;
+    if (m >= M) m = M - 1;
+    src.x[i] = x + m * K + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = (i * 4 + wave) * 64 + lane;
+    const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);   // inverse of wslot
+    int64_t n = n_blk + r;
+    if (n >= N) n = N - 1;
+    src.w[i] = w + n * kw + 4 * half;
+  }
+  {
+    int64_t n = n_blk + wave * 64 + lane;
+    if (n >= N) n = N - 1;
+    src.s = sc + n * ks;
+  }
+
+  f32x16_t acc[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  v3_issue(st0, src, 0, wave);
+  v3_issue(st1, src, nslabs > 1 ? 1 : 0, wave);
+
+  // One step: wait for slab s, release the stage read two steps ago, queue
+  // slab s + 2 into it (the last slab again near the end, so the issue is
+  // unconditional and the compiler keeps exact track of what is in
+  // flight), multiply slab s.
+#define NVFP4_V3_STEP(S, CUR, FREE)                                              \
+  do {                                                                           \
+    wait_vmem(true);                                                             \
+    __builtin_amdgcn_s_barrier();                                                \
+    v3_issue(FREE, src, ((S) + 2 < nslabs) ? (S) + 2 : nslabs - 1, wave);        \
+    v3_compute(acc, CUR, wave, l32, h);                                          \
+  } while (0)
+
+  int64_t s = 0;
+  for (; s + 3 <= nslabs; s += 3) {
+    NVFP4_V3_STEP(s, st0, st2);
+    NVFP4_V3_STEP(s + 1, st1, st0);
+    NVFP4_V3_STEP(s + 2, st2, st1);
+  }
+  if (s < nslabs) NVFP4_V3_STEP(s, st0, st2);
+  if (s + 1 < nslabs) NVFP4_V3_STEP(s + 1, st1, st0);
+  wait_vmem(false);   // no load-to-LDS may land after the block ends
+#undef NVFP4_V3_STEP
+
+  // Epilogue: fragment (a, b) holds C[n][m] with n = 8*jj + 4h + i, m = l32.
+  const float g = global_factor(gs, 0);
+  const bool vec_ok = (N % 4) == 0;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int64_t m = m_blk + b * 32 + l32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t n = n_blk + wave * 64 + a * 32 + jj * 8 + h * 4;
+        __bf16 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[a][b][jj * 4 + i] * g);
+        __bf16* p = out + m * N + n;
+        if (vec_ok && n + 3 < N) {
+          *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, v);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (n + i < N) p[i] = v[i];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Generic float32 kernel
 // ----------------------------------------------------------------------------
 
@@ -299,6 +510,14 @@ namespace nvfp4host {
 
 void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                       const uint8_t* sc, const float* gs, void* out, hipStream_t s) {
+  if (K % kV3BK == 0 && (reinterpret_cast<uintptr_t>(sc) & 3) == 0) {
+    const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
+    const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
+    const int64_t grid = (tiles + 7) / 8 * 8;
+    gemm_mfma_v3_kernel<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+        static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
+    return;
+  }
   const int64_t tiles_m = (M + kBM - 1) / kBM;
   const int64_t tiles_n = (N + kBN - 1) / kBN;
   const int64_t tiles = tiles_m * tiles_n;

@@ -77,7 +77,7 @@ __device__ __forceinline__ void decode_word_f32(uint32_t w, float s, float (&v)[
 
 // Sum of x[i] * e2m1(word element i) over the eight elements of one word,
 // x given as four packed bf16 pairs; float32 accumulation starting at acc.
-__device__ __forceinline__ float dot_word_bf16(uint32_t w, const uint32_t (&xp)[4], float acc) {
+__device__ __forceinline__ float dot_word_bf16(uint32_t w, const uint32_t* xp, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<0>(w), __builtin_bit_cast(bf16x2_t, xp[0]), acc, false);
   acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<1>(w), __builtin_bit_cast(bf16x2_t, xp[1]), acc, false);
   acc = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_bf16<2>(w), __builtin_bit_cast(bf16x2_t, xp[2]), acc, false);
@@ -106,6 +106,26 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes of a fully active wavefront with DPP: pairs, quads,
+// half-rows and rows of 16 lanes inside the VALU, then the four row sums
+// through scalar registers.  The result is wave-uniform.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Output element stores (round to nearest even).

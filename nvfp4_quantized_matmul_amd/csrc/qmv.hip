@@ -234,11 +234,189 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------
+// Decode kernel for M = 1: activation-stationary, row-streaming.
+//
+// Lane l owns chunk positions l, l+64, ... (CPL of them) of every weight
+// row, so its 32*CPL activations stay in registers for the whole kernel and
+// every wave load of one row chunk is 1 KiB of contiguous weights.  Each
+// wave owns a run of rows sized so that the whole grid is resident at once
+// (no tail of late waves); inside the run, the loads of row r+1 are in
+// flight while row r is decoded, reduced (DPP) and stored.
+// ----------------------------------------------------------------------------
+
+template <typename TX>
+struct XReg;
+template <>
+struct XReg<__bf16> { uint32_t p[16]; };   // 32 bf16 as 16 packed pairs
+template <>
+struct XReg<float> { float v[32]; };
+template <>
+struct XReg<_Float16> { float v[32]; };
+
+__device__ __forceinline__ void load_xreg(XReg<__bf16>& r, const __bf16* p, bool ok) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = ok ? reinterpret_cast<const uint4*>(p)[i] : make_uint4(0, 0, 0, 0);
+    r.p[4 * i] = v.x; r.p[4 * i + 1] = v.y; r.p[4 * i + 2] = v.z; r.p[4 * i + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ void load_xreg(XReg<float>& r, const float* p, bool ok) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = ok ? reinterpret_cast<const float4*>(p)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    r.v[4 * i] = v.x; r.v[4 * i + 1] = v.y; r.v[4 * i + 2] = v.z; r.v[4 * i + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ void load_xreg(XReg<_Float16>& r, const _Float16* p, bool ok) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) r.v[i] = ok ? (float)p[i] : 0.0f;
+}
+
+// One 16-byte chunk (two scale blocks) against register activations.
+__device__ __forceinline__ float chunk_dot_reg(const uint4& w, uint32_t s, const XReg<__bf16>& xr) {
+  float p0 = dot_word_bf16(w.x, xr.p + 0, 0.0f);
+  p0 = dot_word_bf16(w.y, xr.p + 4, p0);
+  float p1 = dot_word_bf16(w.z, xr.p + 8, 0.0f);
+  p1 = dot_word_bf16(w.w, xr.p + 12, p1);
+  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
+}
+
+template <typename XR>
+__device__ __forceinline__ float chunk_dot_reg_f32(const uint4& w, uint32_t s, const XR& xr) {
+  float p0 = dot_word_f32(w.x, xr.v + 0, 0.0f);
+  p0 = dot_word_f32(w.y, xr.v + 8, p0);
+  float p1 = dot_word_f32(w.z, xr.v + 16, 0.0f);
+  p1 = dot_word_f32(w.w, xr.v + 24, p1);
+  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
+}
+
+__device__ __forceinline__ float chunk_dot_reg(const uint4& w, uint32_t s, const XReg<float>& xr) {
+  return chunk_dot_reg_f32(w, s, xr);
+}
+__device__ __forceinline__ float chunk_dot_reg(const uint4& w, uint32_t s, const XReg<_Float16>& xr) {
+  return chunk_dot_reg_f32(w, s, xr);
+}
+
+template <typename TX, int CPL>
+__global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x,
+                                                        const uint32_t* __restrict__ w,
+                                                        const uint8_t* __restrict__ sc,
+                                                        const float* __restrict__ gs,
+                                                        TX* __restrict__ out, int64_t K, int64_t N,
+                                                        int64_t rows_per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t r_begin = wave_id * rows_per_wave;
+  if (r_begin >= N) return;  // wave-uniform; no barriers in this kernel
+  const int64_t r_end = (r_begin + rows_per_wave) < N ? (r_begin + rows_per_wave) : N;
+  const int64_t kw = K / 8, ks = K / 16, nchunks = kw / 4;
+
+  XReg<TX> xr[CPL];
+  bool ok[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int64_t c = lane + 64 * i;
+    ok[i] = c < nchunks;
+    load_xreg(xr[i], x + (ok[i] ? c : 0) * 32, ok[i]);
+  }
+  const float g = global_factor(gs, 0);
+
+  uint4 wa[CPL], wb[CPL];
+  uint32_t sa[CPL], sb[CPL];
+  auto load_row = [&](int64_t n, uint4 (&wv)[CPL], uint32_t (&sv)[CPL]) {
+    const uint32_t* wr = w + n * kw;
+    const uint8_t* sr = sc + n * ks;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int64_t c = lane + 64 * i;
+      if (ok[i]) {
+        wv[i] = *reinterpret_cast<const uint4*>(wr + c * 4);
+        sv[i] = *reinterpret_cast<const uint16_t*>(sr + c * 2);
+      } else {
+        wv[i] = make_uint4(0, 0, 0, 0);
+        sv[i] = 0;
+      }
+    }
+  };
+  auto row_sum = [&](const uint4 (&wv)[CPL], const uint32_t (&sv)[CPL]) {
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) d += chunk_dot_reg(wv[i], sv[i], xr[i]);
+    return wave_sum_dpp(d);
+  };
+
+  load_row(r_begin, wa, sa);
+  for (int64_t r = r_begin; r < r_end; r += 2) {
+    const bool has1 = r + 1 < r_end;
+    if (has1) load_row(r + 1, wb, sb);
+    const float v0 = row_sum(wa, sa);
+    if (lane == 0) store_out(out + r, v0 * g);
+    if (r + 2 < r_end) load_row(r + 2, wa, sa);
+    if (has1) {
+      const float v1 = row_sum(wb, sb);
+      if (lane == 0) store_out(out + r + 1, v1 * g);
+    }
+  }
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Resident blocks per CU for a kernel (queried once per instantiation).
+template <typename F>
+int64_t blocks_per_cu(F kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n <= 0) n = 1;
+  return n;
+}
+
+template <typename TX, int CPL>
+void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
+                 const float* gs, TX* out, hipStream_t s) {
+  // Size the grid so every wave is resident at once: each wave then owns a
+  // balanced run of rows and no late waves form a tail.
+  static const int64_t per_cu = blocks_per_cu(qmv1_kernel<TX, CPL>);
+  const int64_t target_waves = (int64_t)device_cus() * per_cu * kWaves;
+  int64_t rows = (N + target_waves - 1) / target_waves;
+  if (rows < 1) rows = 1;
+  const int64_t waves = (N + rows - 1) / rows;
+  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  qmv1_kernel<TX, CPL><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(x, w, sc, gs, out, K, N, rows);
+}
+
+// True when the M = 1 decode kernel handles this K (and launches it).
+template <typename TX>
+bool try_qmv1(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
+              const float* gs, TX* out, hipStream_t s) {
+  if (K % 32 != 0) return false;
+  const int64_t cpl = (K / 32 + 63) / 64;
+  switch (cpl) {
+    case 1: qmv1_launch<TX, 1>(x, K, N, w, sc, gs, out, s); return true;
+    case 2: qmv1_launch<TX, 2>(x, K, N, w, sc, gs, out, s); return true;
+    case 3: qmv1_launch<TX, 3>(x, K, N, w, sc, gs, out, s); return true;
+    case 4: qmv1_launch<TX, 4>(x, K, N, w, sc, gs, out, s); return true;
+    default: return false;
+  }
+}
+
 template <typename TX, int VEC>
 void qmv_dispatch(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                   const uint8_t* sc, const float* gs, TX* out, hipStream_t s) {
   constexpr int ROWS = 4;
   const int64_t gx = (N + kWaves * ROWS - 1) / (kWaves * ROWS);
+  if (M == 1 && try_qmv1<TX>(x, K, N, w, sc, gs, out, s)) return;
   if (M == 1) {
     qmv_kernel<TX, VEC, ROWS, 1><<<dim3((unsigned)gx, 1), dim3(kThreads), 0, s>>>(x, w, sc, gs, out, M, K, N);
   } else {

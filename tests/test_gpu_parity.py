@@ -395,3 +395,29 @@ def test_moe_unsorted_decode_full_size(tokens):
     got = host(out)[rows, 0, :]
     assert oracle.relative_error(got, ref) <= TOL[torch.bfloat16]
     assert_zero_rows(out, case.rhs, case.lhs, 128, tokens)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("K", [32, 2048, 6144, 8192, 8224])
+@pytest.mark.parametrize("N", [1, 7, 300, 5000])
+@pytest.mark.parametrize("with_gs", [False, True])
+def test_decode_kernel_shapes(dtype, K, N, with_gs):
+    """M = 1 over every activation-stationary variant (1..4 chunks per lane)
+    and the general kernel beyond them (K = 8224), with row counts that leave
+    partial runs of rows per wave."""
+    # f16 outputs: scales up to 2^3 keep every dot product inside f16 range
+    codes = (0x08, 0x50) if dtype == torch.float16 else synth.NORMAL_POSITIVE_CODES
+    case = synth.dense_case(3600 + K + N, 1, K, N, with_gs=with_gs, code_range=codes)
+    out, ref = run_qmm(case, dtype, "auto", guard=True)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 448])
+@pytest.mark.parametrize("M", [1, 100, 300])
+@pytest.mark.parametrize("N", [40, 300])
+def test_gemm_slab_pipeline_shapes(K, M, N):
+    """bf16 GEMM route with K a multiple of 64: 1..7 slabs of 64 exercise
+    every tail of the three-stage pipeline; M and N leave partial tiles."""
+    case = synth.dense_case(3700 + K + M + N, M, K, N, with_gs=True)
+    out, ref = run_qmm(case, torch.bfloat16, "gemm", guard=True)
+    assert rel(out, ref) <= TOL[torch.bfloat16]
