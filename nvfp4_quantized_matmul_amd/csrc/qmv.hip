@@ -235,168 +235,172 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// Decode kernel for M = 1: activation-stationary, row-streaming.
+// Decode kernel for M = 1.
 //
-// Lane l owns chunk positions l, l+64, ... (CPL of them) of every weight
-// row, so its 32*CPL activations stay in registers for the whole kernel and
-// every wave load of one row chunk is 1 KiB of contiguous weights.  Each
-// wave owns a run of rows sized so that the whole grid is resident at once
-// (no tail of late waves); inside the run, the loads of row r+1 are in
-// flight while row r is decoded, reduced (DPP) and stored.
+// Each wavefront owns R consecutive weight rows and issues every load of
+// its rows (16-byte word chunks and their scale bytes) before anything
+// else, so a block has all of its HBM traffic in flight at once; the
+// activation vector is staged once per block in LDS and read back per chunk.
+// Lane l owns chunk positions l, l+64, ... (CPL of them) of each row, so a
+// wave load is 1 KiB of one row.  Waves are short-lived and the grid has
+// N / (4R) blocks; with ~50 VGPRs eight waves fit per SIMD, so several
+// blocks' loads overlap each other's decode.  Measured against a plain
+// streaming read of the same bytes, this beats a persistent row-streaming
+// kernel whose prefetch depth could not cover HBM latency.
 // ----------------------------------------------------------------------------
 
+// One 16-byte chunk (two scale blocks) against 32 activations.
+__device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const uint4* xl, int c, __bf16*) {
+  uint32_t xp[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = xl[c * 4 + q];
+    xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+  }
+  float p0 = dot_word_bf16(w.x, xp + 0, 0.0f);
+  p0 = dot_word_bf16(w.y, xp + 4, p0);
+  float p1 = dot_word_bf16(w.z, xp + 8, 0.0f);
+  p1 = dot_word_bf16(w.w, xp + 12, p1);
+  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
+}
+
+// float32 activations.
+__device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const uint4* xl, int c, float*) {
+  float xv[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = xl[c * 8 + q];
+    xv[4 * q] = __builtin_bit_cast(float, v.x); xv[4 * q + 1] = __builtin_bit_cast(float, v.y);
+    xv[4 * q + 2] = __builtin_bit_cast(float, v.z); xv[4 * q + 3] = __builtin_bit_cast(float, v.w);
+  }
+  float p0 = dot_word_f32(w.x, xv + 0, 0.0f);
+  p0 = dot_word_f32(w.y, xv + 8, p0);
+  float p1 = dot_word_f32(w.z, xv + 16, 0.0f);
+  p1 = dot_word_f32(w.w, xv + 24, p1);
+  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
+}
+
+// f16 activations, widened to float32 after the LDS read.
+__device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const uint4* xl, int c, _Float16*) {
+  float xv[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = xl[c * 4 + q];
+    const _Float16* h = reinterpret_cast<const _Float16*>(&v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xv[8 * q + j] = (float)h[j];
+  }
+  float p0 = dot_word_f32(w.x, xv + 0, 0.0f);
+  p0 = dot_word_f32(w.y, xv + 8, p0);
+  float p1 = dot_word_f32(w.z, xv + 16, 0.0f);
+  p1 = dot_word_f32(w.w, xv + 24, p1);
+  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
+}
+
+// The activation row is copied to LDS by the load-to-LDS path (no
+// registers involved), 1 KiB per wavefront instruction.  The last piece may
+// run past the row: those lanes re-read the row's last 16 bytes into LDS
+// padding that is never read.
+#define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 template <typename TX>
-struct XReg;
-template <>
-struct XReg<__bf16> { uint32_t p[16]; };   // 32 bf16 as 16 packed pairs
-template <>
-struct XReg<float> { float v[32]; };
-template <>
-struct XReg<_Float16> { float v[32]; };
-
-__device__ __forceinline__ void load_xreg(XReg<__bf16>& r, const __bf16* p, bool ok) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = ok ? reinterpret_cast<const uint4*>(p)[i] : make_uint4(0, 0, 0, 0);
-    r.p[4 * i] = v.x; r.p[4 * i + 1] = v.y; r.p[4 * i + 2] = v.z; r.p[4 * i + 3] = v.w;
+__device__ __forceinline__ int stage_x_lds(uint4* xl, const TX* x, int64_t K, int lane, int wave) {
+  const int64_t n16 = K * (int64_t)sizeof(TX) / 16;
+  const int64_t pieces = (n16 + 63) / 64;
+  int issued = 0;
+  for (int64_t p = wave; p < pieces; p += kWaves) {
+    int64_t q = p * 64 + lane;
+    q = q < n16 ? q : n16 - 1;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(x) + q, NVFP4_LDS(xl + p * 64), 16, 0, 0);
+    ++issued;
   }
+  return issued;
 }
 
-__device__ __forceinline__ void load_xreg(XReg<float>& r, const float* p, bool ok) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 v = ok ? reinterpret_cast<const float4*>(p)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    r.v[4 * i] = v.x; r.v[4 * i + 1] = v.y; r.v[4 * i + 2] = v.z; r.v[4 * i + 3] = v.w;
-  }
+// Bytes of LDS the staged row occupies (whole 1 KiB pieces).
+template <typename TX>
+size_t staged_x_bytes(int64_t K) {
+  const int64_t n16 = K * (int64_t)sizeof(TX) / 16;
+  return (size_t)((n16 + 63) / 64) * 1024;
 }
 
-__device__ __forceinline__ void load_xreg(XReg<_Float16>& r, const _Float16* p, bool ok) {
-#pragma unroll
-  for (int i = 0; i < 32; ++i) r.v[i] = ok ? (float)p[i] : 0.0f;
-}
+// Element type of the staged activations (the activation type itself).
+template <typename TX> struct LdsElem { typedef TX type; };
 
-// One 16-byte chunk (two scale blocks) against register activations.
-__device__ __forceinline__ float chunk_dot_reg(const uint4& w, uint32_t s, const XReg<__bf16>& xr) {
-  float p0 = dot_word_bf16(w.x, xr.p + 0, 0.0f);
-  p0 = dot_word_bf16(w.y, xr.p + 4, p0);
-  float p1 = dot_word_bf16(w.z, xr.p + 8, 0.0f);
-  p1 = dot_word_bf16(w.w, xr.p + 12, p1);
-  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
-}
-
-template <typename XR>
-__device__ __forceinline__ float chunk_dot_reg_f32(const uint4& w, uint32_t s, const XR& xr) {
-  float p0 = dot_word_f32(w.x, xr.v + 0, 0.0f);
-  p0 = dot_word_f32(w.y, xr.v + 8, p0);
-  float p1 = dot_word_f32(w.z, xr.v + 16, 0.0f);
-  p1 = dot_word_f32(w.w, xr.v + 24, p1);
-  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
-}
-
-__device__ __forceinline__ float chunk_dot_reg(const uint4& w, uint32_t s, const XReg<float>& xr) {
-  return chunk_dot_reg_f32(w, s, xr);
-}
-__device__ __forceinline__ float chunk_dot_reg(const uint4& w, uint32_t s, const XReg<_Float16>& xr) {
-  return chunk_dot_reg_f32(w, s, xr);
-}
-
-template <typename TX, int CPL>
+template <typename TX, int CPL, int R>
 __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x,
-                                                        const uint32_t* __restrict__ w,
-                                                        const uint8_t* __restrict__ sc,
+                                                        const uint32_t* w,
+                                                        const uint8_t* sc,
                                                         const float* __restrict__ gs,
-                                                        TX* __restrict__ out, int64_t K, int64_t N,
-                                                        int64_t rows_per_wave) {
+                                                        TX* __restrict__ out, int64_t K, int64_t N) {
+  extern __shared__ uint4 xl[];
   const int lane = threadIdx.x & 63;
-  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t r_begin = wave_id * rows_per_wave;
-  if (r_begin >= N) return;  // wave-uniform; no barriers in this kernel
-  const int64_t r_end = (r_begin + rows_per_wave) < N ? (r_begin + rows_per_wave) : N;
+  const int64_t n0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
   const int64_t kw = K / 8, ks = K / 16, nchunks = kw / 4;
 
-  XReg<TX> xr[CPL];
-  bool ok[CPL];
+  // 1. All weight and scale loads of this wave's rows, issued back to back
+  //    and unconditionally: rows past N re-read row N-1 and chunks past the
+  //    row end re-read its last chunk (neither result is used), so no load
+  //    result has to be merged with a default value before it has arrived.
+  const int nch = (int)nchunks;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // 0. The activation row goes straight to LDS (no registers, so nothing
+  //    below has to wait for it to land before issuing).
+  stage_x_lds(xl, x, K, lane, wave);
+  // 1. All weight and scale loads of this wave's rows, issued back to back
+  //    and unconditionally: rows past N re-read row N-1 and chunks past the
+  //    row end re-read its last chunk (neither result is used), so no load
+  //    result has to be merged with a default value before it has arrived.
+  uint4 wv[R][CPL];
+  uint32_t sv[R][CPL];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int64_t c = lane + 64 * i;
-    ok[i] = c < nchunks;
-    load_xreg(xr[i], x + (ok[i] ? c : 0) * 32, ok[i]);
-  }
-  const float g = global_factor(gs, 0);
-
-  uint4 wa[CPL], wb[CPL];
-  uint32_t sa[CPL], sb[CPL];
-  auto load_row = [&](int64_t n, uint4 (&wv)[CPL], uint32_t (&sv)[CPL]) {
+  for (int r = 0; r < R; ++r) {
+    const int64_t n = (n0 + r) < N ? (n0 + r) : (N - 1);
     const uint32_t* wr = w + n * kw;
     const uint8_t* sr = sc + n * ks;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const int64_t c = lane + 64 * i;
-      if (ok[i]) {
-        wv[i] = *reinterpret_cast<const uint4*>(wr + c * 4);
-        sv[i] = *reinterpret_cast<const uint16_t*>(sr + c * 2);
-      } else {
-        wv[i] = make_uint4(0, 0, 0, 0);
-        sv[i] = 0;
-      }
+      const int c = min(lane + 64 * i, nch - 1);
+      wv[r][i] = *reinterpret_cast<const uint4*>(wr + c * 4);
+      sv[r][i] = *reinterpret_cast<const uint16_t*>(sr + c * 2);
     }
-  };
-  auto row_sum = [&](const uint4 (&wv)[CPL], const uint32_t (&sv)[CPL]) {
-    float d = 0.0f;
+  }
+  // 2. Every wave's activation pieces are in LDS after the barrier (it
+  //    waits for all of this wave's loads, which the decode needs anyway).
+  __syncthreads();
+  // 3. Decode and reduce.
+  float acc[R];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) d += chunk_dot_reg(wv[i], sv[i], xr[i]);
-    return wave_sum_dpp(d);
-  };
-
-  load_row(r_begin, wa, sa);
-  for (int64_t r = r_begin; r < r_end; r += 2) {
-    const bool has1 = r + 1 < r_end;
-    if (has1) load_row(r + 1, wb, sb);
-    const float v0 = row_sum(wa, sa);
-    if (lane == 0) store_out(out + r, v0 * g);
-    if (r + 2 < r_end) load_row(r + 2, wa, sa);
-    if (has1) {
-      const float v1 = row_sum(wb, sb);
-      if (lane == 0) store_out(out + r + 1, v1 * g);
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        acc[r] += chunk_dot_lds(wv[r][i], sv[r][i], xl, c, (typename LdsElem<TX>::type*)nullptr);
     }
   }
-}
-
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+  const float g = global_factor(gs, 0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float v = wave_sum_dpp(acc[r]);
+    if (lane == 0 && n0 + r < N) store_out(out + n0 + r, v * g);
   }
-  return cached[dev];
 }
 
-// Resident blocks per CU for a kernel (queried once per instantiation).
-template <typename F>
-int64_t blocks_per_cu(F kernel) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n <= 0) n = 1;
-  return n;
-}
+constexpr int kQmv1Rows = 2;
 
 template <typename TX, int CPL>
 void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
                  const float* gs, TX* out, hipStream_t s) {
-  // Size the grid so every wave is resident at once: each wave then owns a
-  // balanced run of rows and no late waves form a tail.
-  static const int64_t per_cu = blocks_per_cu(qmv1_kernel<TX, CPL>);
-  const int64_t target_waves = (int64_t)device_cus() * per_cu * kWaves;
-  int64_t rows = (N + target_waves - 1) / target_waves;
-  if (rows < 1) rows = 1;
-  const int64_t waves = (N + rows - 1) / rows;
-  const int64_t blocks = (waves + kWaves - 1) / kWaves;
-  qmv1_kernel<TX, CPL><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(x, w, sc, gs, out, K, N, rows);
+  const int64_t blocks = (N + kWaves * kQmv1Rows - 1) / (kWaves * kQmv1Rows);
+  const size_t lds = staged_x_bytes<TX>(K);
+  qmv1_kernel<TX, CPL, kQmv1Rows><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(x, w, sc, gs, out, K, N);
 }
 
-// True when the M = 1 decode kernel handles this K (and launches it).
+// True when the M = 1 decode kernel handles this K (and launches it):
+// K % 32 == 0 and at most 4 chunks per lane (K <= 8192, LDS <= 32 KiB).
 template <typename TX>
 bool try_qmv1(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
               const float* gs, TX* out, hipStream_t s) {
