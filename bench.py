@@ -5,13 +5,15 @@ Headline (``value``): the decode workload -- qmm with M=1, K=5376, N=21504,
 bf16 activations and output, scalar global scale -- as achieved HBM GB/s
 of algorithmic bytes.  One step is one nvfp4_qmm call (weight stream, scale
 stream, decode, MAC, reduction, epilogue).  The K timed steps are launched
-as one captured HIP graph and rotate over 8 independent copies of the
-weight planes (520 MB > the 256 MB MALL) so weights come from HBM.
+back to back on one stream (the host enqueues ahead of the GPU) and rotate
+over 8 independent copies of the weight planes (520 MB > the 256 MB MALL)
+so weights come from HBM; the same steps replayed as one HIP graph are
+reported beside it.
 
 Also reported, each against its roofline: the prefill GEMM (M=2048,
 TFLOP/s), the multi-row qmv (M=16) and the MoE gather (sorted prefill and
-unsorted decode, GB/s).  Kernel durations come from HIP events around a replayed
-graph of back-to-back launches on the launch stream.  The CPU oracle is timed on the host
+unsorted decode, GB/s).  Kernel durations come from HIP events around back-to-back
+launches on the launch stream.  The CPU oracle is timed on the host
 on the full decode workload (cpu_baseline).
 
 Prints one JSON line.
@@ -64,30 +66,10 @@ def stream_ptr():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def graph_launch_us(work, n: int, reps: int = 3):
-    """Average duration of one launch: `n` launches captured in one HIP
-    graph, replayed between two events on the launch stream; the median of
-    `reps` replays is returned with the spread."""
-    work.launch(0)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(n):
-            work.launch(i)
-    g.replay()
-    torch.cuda.synchronize()
-    per = []
-    for _ in range(reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        e1.synchronize()
-        per.append(1e3 * e0.elapsed_time(e1) / n)
-    per.sort()
-    return {"mean_us": per[len(per) // 2], "min_us": per[0], "max_us": per[-1],
-            "launches_per_replay": n, "replays": reps}
+def eager_launch_us(work, n: int, warmup: int = 3):
+    """Average duration of one launch over `n` back-to-back launches."""
+    ms = timed_eager(work, n, warmup)
+    return {"mean_us": ms * 1e3, "launches": n, "source": "HIP events around back-to-back launches"}
 
 
 def check(status, what):
@@ -115,11 +97,19 @@ class Decode:
         self.lib = nv.load_library()
         self.copies = copies
         self.bytes = (case.w.nbytes + case.scales.nbytes + 4 + self.x.numel() * 2 + self.out.numel() * 2)
+        self.fn = self.lib.nvfp4_qmm
+        self.args = None
 
     def launch(self, i):
         c = i % self.copies
         check(self.lib.nvfp4_qmm(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]),
                                  P(self.gs), 1, 0, P(self.out), stream_ptr()), "decode qmm")
+
+    def prebuilt(self):
+        """Argument tuples for each weight copy, bound to the current stream."""
+        st = stream_ptr()
+        return [(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
+                 P(self.out), st) for c in range(self.copies)]
 
 
 class Prefill:
@@ -134,6 +124,12 @@ class Prefill:
         self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=DEV)
         self.lib = decode.lib
         self.flops = 2.0 * self.M * self.N * self.K
+        self.fn = self.lib.nvfp4_qmm
+
+    def prebuilt(self):
+        st = stream_ptr()
+        return [(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
+                 P(self.out), st) for c in range(len(self.w))]
 
     def launch(self, i):
         c = i % len(self.w)
@@ -158,6 +154,12 @@ class MultiRow:
         self.lib = nv.load_library()
         self.bytes = case.w.nbytes + case.scales.nbytes + 4 + self.x.numel() * 2 + self.out.numel() * 2
         self.flops = 2.0 * M * self.K * self.N
+        self.fn = self.lib.nvfp4_qmm
+
+    def prebuilt(self):
+        st = stream_ptr()
+        return [(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
+                 P(self.out), st) for c in range(len(self.w))]
 
     def launch(self, i):
         c = i % len(self.w)
@@ -190,6 +192,13 @@ class Gather:
         self.distinct = distinct
         self.bytes = (distinct * per_expert + self.x.numel() * 2 + 2 * self.R * 4 + self.out.numel() * 2)
         self.flops = 2.0 * self.R * self.N * self.K
+        self.fn = self.lib.nvfp4_gather_qmm
+
+    def prebuilt(self):
+        st = stream_ptr()
+        return [(P(self.x), BF16, self.tokens, 1, self.K, P(self.lhs), P(self.rhs), self.R, P(self.w[c]),
+                 P(self.s[c]), P(self.gs), self.E, self.N, self.sort, P(self.out), st)
+                for c in range(len(self.w))]
 
     def launch(self, i):
         c = i % len(self.w)
@@ -224,13 +233,26 @@ def timed_graph(work, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps
 
 
-def timed_eager(work, steps: int):
+def timed_eager(work, steps: int, warmup: int):
+    """Warm up, then time `steps` back-to-back launches (prebuilt ctypes
+    arguments, so the host stays ahead of the GPU) between HIP events on the
+    launch stream, bracketed by synchronizes; returns ms per step."""
+    args = work.prebuilt()
+    fn, n = work.fn, len(args)
+    for i in range(warmup):
+        check(fn(*args[i % n]), "warmup")
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    bad = 0
+    e0.record()
     for i in range(steps):
-        work.launch(i)
+        bad |= fn(*args[i % n])
+    e1.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    if bad:
+        raise RuntimeError("a timed launch failed")
+    return e0.elapsed_time(e1) / steps
 
 
 def kernel_source_sha() -> str:
@@ -311,32 +333,33 @@ def main():
 
     log("decode: building inputs")
     dec = Decode(copies=8)
-    log("decode: timed graph")
-    ms = timed_graph(dec, steps, warmup)
-    eager_ms = timed_eager(dec, min(steps, 100))
+    log("decode: timed region")
+    ms = timed_eager(dec, steps, warmup)
+    graph_ms = timed_graph(dec, steps, warmup)
     value = dec.bytes / (ms * 1e-3) / 1e9
     # the timed region is K back-to-back launches of the one kernel, so its
     # average launch duration is the per-step time
-    dur = {"mean_us": ms * 1e3, "launches": steps, "source": "HIP events around the timed graph replay"}
+    dur = {"mean_us": ms * 1e3, "launches": steps,
+           "source": "HIP events around the timed back-to-back launches"}
     achieved = value
     traffic = traffic_for("decode_qmv", dec.bytes)
 
     log("prefill")
     pre = Prefill(dec)
-    pdur = graph_launch_us(pre, 8)
+    pdur = eager_launch_us(pre, 8)
     ptf = pre.flops / (pdur["mean_us"] * 1e-6) / 1e12
 
     log("multi-row qmv")
     mr = MultiRow(16, copies=16)
-    mdur = graph_launch_us(mr, 64)
+    mdur = eager_launch_us(mr, 64)
     mgbs = mr.bytes / (mdur["mean_us"] * 1e-6) / 1e9
 
     log("moe gather")
     gs_sorted = Gather(128, True, copies=3)
-    sdur = graph_launch_us(gs_sorted, 24)
+    sdur = eager_launch_us(gs_sorted, 24)
     sgbs = gs_sorted.bytes / (sdur["mean_us"] * 1e-6) / 1e9
     gs_dec = Gather(8, False, copies=3, seed_off=8)
-    udur = graph_launch_us(gs_dec, 96)
+    udur = eager_launch_us(gs_dec, 96)
     ugbs = gs_dec.bytes / (udur["mean_us"] * 1e-6) / 1e9
 
     cpu = None
@@ -359,30 +382,32 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_qmv_m1_k5376_n21504_bf16", "M": 1, "K": 5376, "N": 21504,
                    "activations": "bf16", "global_scale": True, "weight_copies": 8,
-                   "launch": "one HIP graph of `steps` nvfp4_qmm launches",
+                   "launch": "`steps` back-to-back nvfp4_qmm launches on one stream",
                    "bytes_per_step": dec.bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "qmv_kernel<bf16,4,4,1>",
+                     "traffic": traffic, "kernel": "qmv1_kernel<bf16,3,2>",
                      "kernel_duration": dur},
         "cpu_baseline": cpu,
-        "eager_ms_per_step": round(eager_ms, 6),
+        "graph_ms_per_step": round(graph_ms, 6),
         "prefill": {"workload": "prefill_gemm_m2048_k5376_n21504_bf16", "value": round(ptf, 2),
                     "unit": "TFLOP/s", "flops": pre.flops,
                     "roofline": {"bound": "mfma", "achieved": round(ptf, 2), "peak": BF16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(ptf / BF16_PEAK_TFLOPS, 4),
-                                 "kernel": "gemm_mfma_kernel", "kernel_duration": pdur}},
+                                 "kernel": "gemm_mfma_v3_kernel", "kernel_duration": pdur}},
         "multirow_m16": {"workload": "multirow_qmv_m16_k4096_n14336_bf16", "value": round(mgbs, 2),
                          "unit": "GB/s", "frac_hbm": round(mgbs / HBM_PEAK_GBS, 4),
-                         "kernel_duration": mdur, "bytes": mr.bytes},
+                         "kernel": "skinny_kernel<1>", "kernel_duration": mdur, "bytes": mr.bytes},
         "moe_sorted_prefill": {"workload": "moe_gather_e128_n1536_k2048_top8_b128_sorted",
                                "value": round(sgbs, 2), "unit": "GB/s",
                                "frac_hbm": round(sgbs / HBM_PEAK_GBS, 4), "distinct_experts": gs_sorted.distinct,
-                               "kernel_duration": sdur, "bytes": gs_sorted.bytes},
+                               "kernel": "gather_kernel<bf16,4,4,8>", "kernel_duration": sdur,
+                               "bytes": gs_sorted.bytes},
         "moe_unsorted_decode_b8": {"workload": "moe_gather_e128_n1536_k2048_top8_b8_unsorted",
                                    "value": round(ugbs, 2), "unit": "GB/s",
                                    "frac_hbm": round(ugbs / HBM_PEAK_GBS, 4),
-                                   "distinct_experts": gs_dec.distinct, "kernel_duration": udur,
+                                   "distinct_experts": gs_dec.distinct,
+                                   "kernel": "gather_kernel<bf16,4,4,1>", "kernel_duration": udur,
                                    "bytes": gs_dec.bytes},
         "kernel_source_sha": kernel_source_sha(),
     }

@@ -23,6 +23,10 @@ void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, in
 // Dense qmv: out[M,N] = x[M,K] @ W[N,K]^T (transposed plane).
 void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
                 const uint32_t* w, const uint8_t* sc, const float* gs, void* out, hipStream_t s);
+// MFMA kernel for 2 <= M <= 64, bf16 activations, transposed plane,
+// K % 128 == 0; returns false (launching nothing) for other shapes.
+bool launch_skinny(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                   const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // MFMA GEMM, bf16 activations, transposed plane.
 void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                       const uint8_t* sc, const float* gs, void* out, hipStream_t s);

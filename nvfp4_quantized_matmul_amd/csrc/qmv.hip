@@ -458,6 +458,7 @@ void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N
   const bool vec4 = (K % 32) == 0;
   switch (dt) {
     case NVFP4_BF16:
+      if (M >= 2 && launch_skinny(x, M, K, N, w, sc, gs, out, s)) break;
       if (vec4) qmv_dispatch<__bf16, 4>((const __bf16*)x, M, K, N, w, sc, gs, (__bf16*)out, s);
       else qmv_dispatch<__bf16, 2>((const __bf16*)x, M, K, N, w, sc, gs, (__bf16*)out, s);
       break;
