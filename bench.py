@@ -255,19 +255,24 @@ def timed_eager(work, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps
 
 
-def kernel_source_sha() -> str:
+# sources that define the decode launch (routing, kernel, device helpers)
+DECODE_SOURCES = ("api.hip", "nvfp4_device.hpp", "nvfp4_internal.hpp", "qmv.hip")
+
+
+def kernel_source_sha(files=None) -> str:
+    """Digest of the kernel sources (all of them, or the named files)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_quantized_matmul_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key: str, launches_bytes: float):
+def traffic_for(kernel_key: str):
     """HBM traffic per launch from committed rocprofv3 PMC summaries, if they
-    were taken on the current kernel sources; otherwise None."""
+    were taken on the current decode sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"{kernel_key}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -277,7 +282,7 @@ def traffic_for(kernel_key: str, launches_bytes: float):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != kernel_source_sha():
+    if vals.get("decode_source_sha") != kernel_source_sha(DECODE_SOURCES):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -310,6 +315,29 @@ def cpu_baseline(decode_bytes: float):
                       f"{reps} pass(es), {per:.2f} s per pass, mean busy cores {cpu / wall:.2f}"}
 
 
+COPY_BYTES = 256 << 20
+
+
+def counters_decode(steps: int):
+    """Workload for the FETCH_SIZE / WRITE_SIZE passes: one plain device copy
+    of COPY_BYTES (reads and writes exactly that many bytes, so its counter
+    values give the scale of the counters), then `steps` decode launches
+    rotating over the 8 weight copies, each on a synchronized stream so that
+    every dispatch is counted on its own."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device=DEV).fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    dec = Decode(copies=8)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        dec.launch(i)
+        torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "decode_launches": steps, "decode_bytes": dec.bytes,
+                      "decode_source_sha": kernel_source_sha(DECODE_SOURCES)}), flush=True)
+
+
 # ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
@@ -320,6 +348,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    ap.add_argument("--counters-decode", action="store_true",
+                    help="for hardware-counter runs: a 256 MiB device copy (the calibration of "
+                         "FETCH_SIZE/WRITE_SIZE against known bytes), then `steps` decode launches; "
+                         "prints the launch count and bytes instead of the JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the NVFP4 matmul path here is single-GPU "
@@ -330,6 +362,9 @@ def main():
         sys.exit(2)
     steps, warmup = max(1, args.steps), max(0, args.warmup)
     nv.load_library()
+    if args.counters_decode:
+        counters_decode(steps)
+        return
 
     log("decode: building inputs")
     dec = Decode(copies=8)
@@ -342,7 +377,7 @@ def main():
     dur = {"mean_us": ms * 1e3, "launches": steps,
            "source": "HIP events around the timed back-to-back launches"}
     achieved = value
-    traffic = traffic_for("decode_qmv", dec.bytes)
+    traffic = traffic_for("decode_qmv")
 
     log("prefill")
     pre = Prefill(dec)
