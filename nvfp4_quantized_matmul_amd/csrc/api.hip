@@ -14,8 +14,12 @@
 namespace {
 
 // Crossover between the weight-streaming qmv kernels and the GEMM kernels
-// (the pages test qmv up to M = 33 and the GEMM route from M = 64).
+// (the pages test qmv up to M = 33 and the GEMM route from M = 64).  bf16
+// activations with K % 256 == 0 stay on the qmv route up to M = 64: there
+// the MFMA qmv kernel decodes each weight once for all rows and is several
+// times faster than a GEMM tile that is mostly padding.
 constexpr int64_t kQmvMaxRows = 33;
+constexpr int64_t kQmvMaxRowsMfma = 64;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r) && *r >= 0; }
 
@@ -69,7 +73,9 @@ int nvfp4_select_route(int64_t M, int64_t K, int64_t N, int transpose, nvfp4_dty
   if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
   if (transpose ? (K % 16) != 0 : (N % 16) != 0) return NVFP4_ERR_SHAPE;
   if (!transpose) return NVFP4_ROUTE_GEMM;
-  return M <= kQmvMaxRows ? NVFP4_ROUTE_QMV : NVFP4_ROUTE_GEMM;
+  if (M <= kQmvMaxRows) return NVFP4_ROUTE_QMV;
+  if (dtype == NVFP4_BF16 && M <= kQmvMaxRowsMfma && K % 256 == 0) return NVFP4_ROUTE_QMV;
+  return NVFP4_ROUTE_GEMM;
 }
 
 int nvfp4_transcode(const uint8_t* weight, const uint8_t* weight_scale, const float* weight_scale_2,

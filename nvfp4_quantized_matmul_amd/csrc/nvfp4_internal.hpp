@@ -24,7 +24,8 @@ void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, in
 void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
                 const uint32_t* w, const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // MFMA kernel for 2 <= M <= 64, bf16 activations, transposed plane,
-// K % 128 == 0; returns false (launching nothing) for other shapes.
+// K % 256 == 0, 16-byte aligned x and w, 4-byte aligned scales; returns
+// false (launching nothing) otherwise.
 bool launch_skinny(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                    const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // MFMA GEMM, bf16 activations, transposed plane.
