@@ -436,7 +436,7 @@ def main():
         "moe_sorted_prefill": {"workload": "moe_gather_e128_n1536_k2048_top8_b128_sorted",
                                "value": round(sgbs, 2), "unit": "GB/s",
                                "frac_hbm": round(sgbs / HBM_PEAK_GBS, 4), "distinct_experts": gs_sorted.distinct,
-                               "kernel": "gather_kernel<bf16,4,4,8>", "kernel_duration": sdur,
+                               "kernel": "gather_mfma_kernel<4>", "kernel_duration": sdur,
                                "bytes": gs_sorted.bytes},
         "moe_unsorted_decode_b8": {"workload": "moe_gather_e128_n1536_k2048_top8_b8_unsorted",
                                    "value": round(ugbs, 2), "unit": "GB/s",
