@@ -421,7 +421,7 @@ def main():
                    "bytes_per_step": dec.bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "qmv1_kernel<bf16,3,2>",
+                     "traffic": traffic, "kernel": "qmv1_kernel<bf16,3,1>",
                      "kernel_duration": dur},
         "cpu_baseline": cpu,
         "graph_ms_per_step": round(graph_ms, 6),

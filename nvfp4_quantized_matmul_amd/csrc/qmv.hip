@@ -237,16 +237,17 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 // ----------------------------------------------------------------------------
 // Decode kernel for M = 1.
 //
-// Each wavefront owns R consecutive weight rows and issues every load of
-// its rows (16-byte word chunks and their scale bytes) before anything
-// else, so a block has all of its HBM traffic in flight at once; the
-// activation vector is staged once per block in LDS and read back per chunk.
-// Lane l owns chunk positions l, l+64, ... (CPL of them) of each row, so a
-// wave load is 1 KiB of one row.  Waves are short-lived and the grid has
-// N / (4R) blocks; with ~50 VGPRs eight waves fit per SIMD, so several
-// blocks' loads overlap each other's decode.  Measured against a plain
-// streaming read of the same bytes, this beats a persistent row-streaming
-// kernel whose prefetch depth could not cover HBM latency.
+// Each wavefront owns R consecutive weight rows (R = 1 measured best) and
+// issues every load of its rows (16-byte word chunks and their scale bytes)
+// right after its share of the activation row, which goes to LDS once per
+// block; it then waits for the activation pieces only and decodes each chunk
+// as it lands.  Lane l owns chunk positions l, l+64, ... (CPL of them) of
+// each row, so a wave load is 1 KiB of one row.  Waves are short-lived and
+// the grid has N / (4R) blocks; with ~50 VGPRs eight waves fit per SIMD, so
+// several blocks' loads overlap each other's decode.  Measured against a
+// plain streaming read of the same bytes, this beats a persistent
+// row-streaming kernel whose prefetch depth could not cover HBM latency,
+// and two or more rows per wavefront.
 // ----------------------------------------------------------------------------
 
 // One 16-byte chunk (two scale blocks) against 32 activations.
@@ -327,6 +328,17 @@ size_t staged_x_bytes(int64_t K) {
 // Element type of the staged activations (the activation type itself).
 template <typename TX> struct LdsElem { typedef TX type; };
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw byte-buffer descriptor: loads at offsets >= bytes return 0 without
+// touching memory.
+__device__ __forceinline__ rsrc_t byte_buffer(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// An offset no plane reaches (planes stay below 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 template <typename TX, int CPL, int R>
 __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x,
                                                         const uint32_t* w,
@@ -337,37 +349,40 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
   const int lane = threadIdx.x & 63;
   const int64_t n0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
   const int64_t kw = K / 8, ks = K / 16, nchunks = kw / 4;
-
-  // 1. All weight and scale loads of this wave's rows, issued back to back
-  //    and unconditionally: rows past N re-read row N-1 and chunks past the
-  //    row end re-read its last chunk (neither result is used), so no load
-  //    result has to be merged with a default value before it has arrived.
   const int nch = (int)nchunks;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   // 0. The activation row goes straight to LDS (no registers, so nothing
-  //    below has to wait for it to land before issuing).
+  //    below has to wait for it to land before issuing).  These are this
+  //    wave's first vector-memory operations.
   stage_x_lds(xl, x, K, lane, wave);
-  // 1. All weight and scale loads of this wave's rows, issued back to back
-  //    and unconditionally: rows past N re-read row N-1 and chunks past the
-  //    row end re-read its last chunk (neither result is used), so no load
-  //    result has to be merged with a default value before it has arrived.
+  __builtin_amdgcn_sched_barrier(0);
+  // 1. All weight and scale loads of this wave's rows, back to back, as
+  //    buffer loads: chunks past the row end and rows past N get an
+  //    out-of-range offset and read 0 without a memory access (their
+  //    results are never used), so every lane issues every load and no
+  //    result has to be merged with a default value.
+  const rsrc_t wb = byte_buffer(w, N * kw * 4);
+  const rsrc_t sb = byte_buffer(sc, N * ks);
   uint4 wv[R][CPL];
   uint32_t sv[R][CPL];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t n = (n0 + r) < N ? (n0 + r) : (N - 1);
-    const uint32_t* wr = w + n * kw;
-    const uint8_t* sr = sc + n * ks;
+    const int64_t n = n0 + r;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const int c = min(lane + 64 * i, nch - 1);
-      wv[r][i] = *reinterpret_cast<const uint4*>(wr + c * 4);
-      sv[r][i] = *reinterpret_cast<const uint16_t*>(sr + c * 2);
+      const int c = lane + 64 * i;
+      const bool ok = n < N && c < nch;
+      const uint32_t wo = ok ? (uint32_t)(n * kw * 4 + c * 16) : kOutOfRange;
+      const uint32_t so = ok ? (uint32_t)(n * ks + c * 2) : kOutOfRange;
+      wv[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wb, wo, 0, 0));
+      sv[r][i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sb, so, 0, 0);
     }
   }
-  // 2. Every wave's activation pieces are in LDS after the barrier (it
-  //    waits for all of this wave's loads, which the decode needs anyway).
-  __syncthreads();
+  // 2. Wait only for the activation pieces (issued before the 2 R CPL loads
+  //    above; loads complete in order), then the block barrier makes every
+  //    wave's pieces visible.  The weights are consumed as they arrive.
+  __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (2 * R * CPL));
+  __builtin_amdgcn_s_barrier();
   // 3. Decode and reduce.
   float acc[R];
 #pragma unroll
@@ -389,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
   }
 }
 
-constexpr int kQmv1Rows = 2;
+constexpr int kQmv1Rows = 1;
 
 template <typename TX, int CPL>
 void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
@@ -400,11 +415,12 @@ void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uin
 }
 
 // True when the M = 1 decode kernel handles this K (and launches it):
-// K % 32 == 0 and at most 4 chunks per lane (K <= 8192, LDS <= 32 KiB).
+// K % 32 == 0, at most 4 chunks per lane (K <= 8192, LDS <= 32 KiB) and a
+// weight plane below 2^31 bytes (32-bit buffer offsets).
 template <typename TX>
 bool try_qmv1(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
               const float* gs, TX* out, hipStream_t s) {
-  if (K % 32 != 0) return false;
+  if (K % 32 != 0 || N * (K / 2) >= ((int64_t)1 << 31)) return false;
   const int64_t cpl = (K / 32 + 63) / 64;
   switch (cpl) {
     case 1: qmv1_launch<TX, 1>(x, K, N, w, sc, gs, out, s); return true;
