@@ -381,7 +381,9 @@ def main():
 
     log("prefill")
     pre = Prefill(dec)
-    pdur = eager_launch_us(pre, 8)
+    # ~10 ms of warm-up: the clocks take a few milliseconds of sustained
+    # MFMA load to settle, and a short warm-up times the ramp
+    pdur = eager_launch_us(pre, 16, warmup=20)
     ptf = pre.flops / (pdur["mean_us"] * 1e-6) / 1e12
 
     log("multi-row qmv")

@@ -274,17 +274,27 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    // All eight activation fragments of this step first, into their own
+    // registers, then the multiplies: each read's LDS latency hides behind
+    // the reads after it (with one register reused per fragment, every
+    // read's latency sits before its two multiplies).  The scheduler would
+    // sink each read back to its multiplies, so the order is pinned.
+    // (Reading the next step's fragments during this step's multiplies
+    // measured slower: the extra 32 registers cost more than they hide.)
+    bf16x8_t B[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(bf16x8_t, st.x[xslot(b * 32 + l32, 4 * h + j)]);
     bf16x8_t A[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
       A[a] = decode_word_bf16(word, j < 2 ? slo[a] : shi[a]);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const bf16x8_t B = __builtin_bit_cast(bf16x8_t, st.x[xslot(b * 32 + l32, 4 * h + j)]);
-      acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0], B, acc[0][b], 0, 0, 0);
-      acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1], B, acc[1][b], 0, 0, 0);
+      acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0], B[b], acc[0][b], 0, 0, 0);
+      acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1], B[b], acc[1][b], 0, 0, 0);
     }
   }
 }
