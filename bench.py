@@ -256,7 +256,7 @@ def timed_eager(work, steps: int, warmup: int):
 
 
 # sources that define the decode kernel and its launch configuration
-DECODE_SOURCES = ("nvfp4_device.hpp", "qmv.hip")
+DECODE_SOURCES = ("decode.hip", "nvfp4_device.hpp")
 
 
 def kernel_source_sha(files=None) -> str:

@@ -129,7 +129,7 @@ int nvfp4_dequantize(const uint32_t* w, const uint8_t* scales, const float* gs,
  *   gs      float [1] or NULL; when present every output is multiplied by
  *           g = fl32(gs / 2688) once, after the contraction
  *   route   AUTO picks QMV for transpose = 1 and M <= nvfp4_qmv_max_rows()
- *           (and for BF16 with M <= 64 and K % 256 == 0), GEMM otherwise;
+ *           (and for M <= 64 when K % 256 == 0), GEMM otherwise;
  *           QMV on transpose = 0 is NVFP4_ERR_ROUTE
  *   out     [M, N] of dtype, accumulated in float32
  *
@@ -175,8 +175,8 @@ int nvfp4_gather_qmm(const void* x, nvfp4_dtype_t dtype, int64_t X, int64_t M,
 int nvfp4_select_route(int64_t M, int64_t K, int64_t N, int transpose,
                        nvfp4_dtype_t dtype);
 
-/* Largest M the AUTO route sends to the qmv kernels for every dtype and K
- * (host only); BF16 with K % 256 == 0 goes up to 64. */
+/* Largest M the AUTO route sends to the qmv kernels for every K (host
+ * only); with K % 256 == 0 it goes up to 64. */
 int64_t nvfp4_qmv_max_rows(void);
 
 /* Human-readable text for a status code (host only; static storage). */

@@ -14,10 +14,10 @@
 namespace {
 
 // Crossover between the weight-streaming qmv kernels and the GEMM kernels
-// (the pages test qmv up to M = 33 and the GEMM route from M = 64).  bf16
-// activations with K % 256 == 0 stay on the qmv route up to M = 64: there
-// the MFMA qmv kernel decodes each weight once for all rows and is several
-// times faster than a GEMM tile that is mostly padding.
+// (the pages test qmv up to M = 33 and the GEMM route from M = 64).  With
+// K % 256 == 0 the qmv route goes up to M = 64: there the MFMA qmv kernel
+// decodes each weight once for all rows and is several times faster than a
+// GEMM tile that is mostly padding.
 constexpr int64_t kQmvMaxRows = 33;
 constexpr int64_t kQmvMaxRowsMfma = 64;
 
@@ -74,7 +74,7 @@ int nvfp4_select_route(int64_t M, int64_t K, int64_t N, int transpose, nvfp4_dty
   if (transpose ? (K % 16) != 0 : (N % 16) != 0) return NVFP4_ERR_SHAPE;
   if (!transpose) return NVFP4_ROUTE_GEMM;
   if (M <= kQmvMaxRows) return NVFP4_ROUTE_QMV;
-  if (dtype == NVFP4_BF16 && M <= kQmvMaxRowsMfma && K % 256 == 0) return NVFP4_ROUTE_QMV;
+  if (M <= kQmvMaxRowsMfma && K % 256 == 0) return NVFP4_ROUTE_QMV;
   return NVFP4_ROUTE_GEMM;
 }
 

@@ -20,13 +20,17 @@ void launch_sidecar(const float* ws2, float* gs_out, int64_t batch, hipStream_t 
 // Dequantize [batch*rows, cols/8] words into out of dtype.
 void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, int64_t batch,
                        int64_t rows, int64_t cols, nvfp4_dtype_t dt, void* out, hipStream_t s);
+// Decode kernel (M = 1): returns false, launching nothing, when K is not
+// a multiple of 32, K > 8192 or the weight plane reaches 2^31 bytes.
+bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const uint32_t* w,
+                   const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // Dense qmv: out[M,N] = x[M,K] @ W[N,K]^T (transposed plane).
 void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
                 const uint32_t* w, const uint8_t* sc, const float* gs, void* out, hipStream_t s);
-// MFMA kernel for 2 <= M <= 64, bf16 activations, transposed plane,
-// K % 256 == 0, 16-byte aligned x and w, 4-byte aligned scales; returns
-// false (launching nothing) otherwise.
-bool launch_skinny(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+// MFMA kernel for 2 <= M <= 64 (bf16, f16, or f32 activations split into
+// three bf16 parts), transposed plane, K % 256 == 0, 16-byte aligned x, w
+// and scales; returns false (launching nothing) otherwise.
+bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                    const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // GatherQMM through the MFMA kernel, bf16 activations: each expert's pairs
 // are gathered and multiplied together.  Needs K % 256 == 0, E >= 1, X >= 1,

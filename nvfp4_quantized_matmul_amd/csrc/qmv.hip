@@ -28,6 +28,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+template <typename TX> constexpr nvfp4_dtype_t nvfp4_dtype_of();
+template <> constexpr nvfp4_dtype_t nvfp4_dtype_of<__bf16>() { return NVFP4_BF16; }
+template <> constexpr nvfp4_dtype_t nvfp4_dtype_of<float>() { return NVFP4_F32; }
+template <> constexpr nvfp4_dtype_t nvfp4_dtype_of<_Float16>() { return NVFP4_F16; }
+
 // Packed weights of one chunk (VEC words) and its block-scale bytes.
 template <int VEC>
 struct WChunk {
@@ -234,209 +239,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   }
 }
 
-// ----------------------------------------------------------------------------
-// Decode kernel for M = 1.
-//
-// Each wavefront owns R consecutive weight rows (R = 1 measured best) and
-// issues every load of its rows (16-byte word chunks and their scale bytes)
-// right after its share of the activation row, which goes to LDS once per
-// block; it then waits for the activation pieces only and decodes each chunk
-// as it lands.  Lane l owns chunk positions l, l+64, ... (CPL of them) of
-// each row, so a wave load is 1 KiB of one row.  Waves are short-lived and
-// the grid has N / (4R) blocks; with ~50 VGPRs eight waves fit per SIMD, so
-// several blocks' loads overlap each other's decode.  Measured against a
-// plain streaming read of the same bytes, this beats a persistent
-// row-streaming kernel whose prefetch depth could not cover HBM latency,
-// and two or more rows per wavefront.
-// ----------------------------------------------------------------------------
-
-// One 16-byte chunk (two scale blocks) against 32 activations.
-__device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const uint4* xl, int c, __bf16*) {
-  uint32_t xp[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 v = xl[c * 4 + q];
-    xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
-  }
-  float p0 = dot_word_bf16(w.x, xp + 0, 0.0f);
-  p0 = dot_word_bf16(w.y, xp + 4, p0);
-  float p1 = dot_word_bf16(w.z, xp + 8, 0.0f);
-  p1 = dot_word_bf16(w.w, xp + 12, p1);
-  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
-}
-
-// float32 activations.
-__device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const uint4* xl, int c, float*) {
-  float xv[32];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint4 v = xl[c * 8 + q];
-    xv[4 * q] = __builtin_bit_cast(float, v.x); xv[4 * q + 1] = __builtin_bit_cast(float, v.y);
-    xv[4 * q + 2] = __builtin_bit_cast(float, v.z); xv[4 * q + 3] = __builtin_bit_cast(float, v.w);
-  }
-  float p0 = dot_word_f32(w.x, xv + 0, 0.0f);
-  p0 = dot_word_f32(w.y, xv + 8, p0);
-  float p1 = dot_word_f32(w.z, xv + 16, 0.0f);
-  p1 = dot_word_f32(w.w, xv + 24, p1);
-  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
-}
-
-// f16 activations, widened to float32 after the LDS read.
-__device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const uint4* xl, int c, _Float16*) {
-  float xv[32];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 v = xl[c * 4 + q];
-    const _Float16* h = reinterpret_cast<const _Float16*>(&v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xv[8 * q + j] = (float)h[j];
-  }
-  float p0 = dot_word_f32(w.x, xv + 0, 0.0f);
-  p0 = dot_word_f32(w.y, xv + 8, p0);
-  float p1 = dot_word_f32(w.z, xv + 16, 0.0f);
-  p1 = dot_word_f32(w.w, xv + 24, p1);
-  return __builtin_fmaf(p1, e4m3<1>(s), p0 * e4m3<0>(s));
-}
-
-// The activation row is copied to LDS by the load-to-LDS path (no
-// registers involved), 1 KiB per wavefront instruction.  The last piece may
-// run past the row: those lanes re-read the row's last 16 bytes into LDS
-// padding that is never read.
-#define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-template <typename TX>
-__device__ __forceinline__ int stage_x_lds(uint4* xl, const TX* x, int64_t K, int lane, int wave) {
-  const int64_t n16 = K * (int64_t)sizeof(TX) / 16;
-  const int64_t pieces = (n16 + 63) / 64;
-  int issued = 0;
-  for (int64_t p = wave; p < pieces; p += kWaves) {
-    int64_t q = p * 64 + lane;
-    q = q < n16 ? q : n16 - 1;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(x) + q, NVFP4_LDS(xl + p * 64), 16, 0, 0);
-    ++issued;
-  }
-  return issued;
-}
-
-// Bytes of LDS the staged row occupies (whole 1 KiB pieces).
-template <typename TX>
-size_t staged_x_bytes(int64_t K) {
-  const int64_t n16 = K * (int64_t)sizeof(TX) / 16;
-  return (size_t)((n16 + 63) / 64) * 1024;
-}
-
-// Element type of the staged activations (the activation type itself).
-template <typename TX> struct LdsElem { typedef TX type; };
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw byte-buffer descriptor: loads at offsets >= bytes return 0 without
-// touching memory.
-__device__ __forceinline__ rsrc_t byte_buffer(const void* p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-// An offset no plane reaches (planes stay below 2^31 bytes).
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-template <typename TX, int CPL, int R>
-__global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x,
-                                                        const uint32_t* w,
-                                                        const uint8_t* sc,
-                                                        const float* __restrict__ gs,
-                                                        TX* __restrict__ out, int64_t K, int64_t N) {
-  extern __shared__ uint4 xl[];
-  const int lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
-  const int64_t kw = K / 8, ks = K / 16, nchunks = kw / 4;
-  const int nch = (int)nchunks;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // 0. The activation row goes straight to LDS (no registers, so nothing
-  //    below has to wait for it to land before issuing).  These are this
-  //    wave's first vector-memory operations.
-  stage_x_lds(xl, x, K, lane, wave);
-  __builtin_amdgcn_sched_barrier(0);
-  // 1. All weight and scale loads of this wave's rows, back to back, as
-  //    buffer loads: chunks past the row end and rows past N get an
-  //    out-of-range offset and read 0 without a memory access (their
-  //    results are never used), so every lane issues every load and no
-  //    result has to be merged with a default value.
-  const rsrc_t wb = byte_buffer(w, N * kw * 4);
-  const rsrc_t sb = byte_buffer(sc, N * ks);
-  uint4 wv[R][CPL];
-  uint32_t sv[R][CPL];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t n = n0 + r;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = lane + 64 * i;
-      const bool ok = n < N && c < nch;
-      const uint32_t wo = ok ? (uint32_t)(n * kw * 4 + c * 16) : kOutOfRange;
-      const uint32_t so = ok ? (uint32_t)(n * ks + c * 2) : kOutOfRange;
-      wv[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wb, wo, 0, 0));
-      sv[r][i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sb, so, 0, 0);
-    }
-  }
-  // 2. Wait only for the activation pieces (issued before the 2 R CPL loads
-  //    above; loads complete in order), then the block barrier makes every
-  //    wave's pieces visible.  The weights are consumed as they arrive.
-  __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (2 * R * CPL));
-  __builtin_amdgcn_s_barrier();
-  // 3. Decode and reduce.
-  float acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) {
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        acc[r] += chunk_dot_lds(wv[r][i], sv[r][i], xl, c, (typename LdsElem<TX>::type*)nullptr);
-    }
-  }
-  const float g = global_factor(gs, 0);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float v = wave_sum_dpp(acc[r]);
-    if (lane == 0 && n0 + r < N) store_out(out + n0 + r, v * g);
-  }
-}
-
-constexpr int kQmv1Rows = 1;
-
-template <typename TX, int CPL>
-void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
-                 const float* gs, TX* out, hipStream_t s) {
-  const int64_t blocks = (N + kWaves * kQmv1Rows - 1) / (kWaves * kQmv1Rows);
-  const size_t lds = staged_x_bytes<TX>(K);
-  qmv1_kernel<TX, CPL, kQmv1Rows><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(x, w, sc, gs, out, K, N);
-}
-
-// True when the M = 1 decode kernel handles this K (and launches it):
-// K % 32 == 0, at most 4 chunks per lane (K <= 8192, LDS <= 32 KiB) and a
-// weight plane below 2^31 bytes (32-bit buffer offsets).
-template <typename TX>
-bool try_qmv1(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
-              const float* gs, TX* out, hipStream_t s) {
-  if (K % 32 != 0 || N * (K / 2) >= ((int64_t)1 << 31)) return false;
-  const int64_t cpl = (K / 32 + 63) / 64;
-  switch (cpl) {
-    case 1: qmv1_launch<TX, 1>(x, K, N, w, sc, gs, out, s); return true;
-    case 2: qmv1_launch<TX, 2>(x, K, N, w, sc, gs, out, s); return true;
-    case 3: qmv1_launch<TX, 3>(x, K, N, w, sc, gs, out, s); return true;
-    case 4: qmv1_launch<TX, 4>(x, K, N, w, sc, gs, out, s); return true;
-    default: return false;
-  }
-}
-
 template <typename TX, int VEC>
 void qmv_dispatch(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                   const uint8_t* sc, const float* gs, TX* out, hipStream_t s) {
   constexpr int ROWS = 4;
   const int64_t gx = (N + kWaves * ROWS - 1) / (kWaves * ROWS);
-  if (M == 1 && try_qmv1<TX>(x, K, N, w, sc, gs, out, s)) return;
+  if (M == 1 && nvfp4host::launch_decode(x, nvfp4_dtype_of<TX>(), K, N, w, sc, gs, out, s)) return;
   if (M == 1) {
     qmv_kernel<TX, VEC, ROWS, 1><<<dim3((unsigned)gx, 1), dim3(kThreads), 0, s>>>(x, w, sc, gs, out, M, K, N);
   } else {
@@ -474,15 +282,17 @@ void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N
   const bool vec4 = (K % 32) == 0;
   switch (dt) {
     case NVFP4_BF16:
-      if (M >= 2 && launch_skinny(x, M, K, N, w, sc, gs, out, s)) break;
+      if (M >= 2 && launch_skinny(x, dt, M, K, N, w, sc, gs, out, s)) break;
       if (vec4) qmv_dispatch<__bf16, 4>((const __bf16*)x, M, K, N, w, sc, gs, (__bf16*)out, s);
       else qmv_dispatch<__bf16, 2>((const __bf16*)x, M, K, N, w, sc, gs, (__bf16*)out, s);
       break;
     case NVFP4_F32:
+      if (M >= 2 && launch_skinny(x, dt, M, K, N, w, sc, gs, out, s)) break;
       if (vec4) qmv_dispatch<float, 4>((const float*)x, M, K, N, w, sc, gs, (float*)out, s);
       else qmv_dispatch<float, 2>((const float*)x, M, K, N, w, sc, gs, (float*)out, s);
       break;
     case NVFP4_F16:
+      if (M >= 2 && launch_skinny(x, dt, M, K, N, w, sc, gs, out, s)) break;
       if (vec4) qmv_dispatch<_Float16, 4>((const _Float16*)x, M, K, N, w, sc, gs, (_Float16*)out, s);
       else qmv_dispatch<_Float16, 2>((const _Float16*)x, M, K, N, w, sc, gs, (_Float16*)out, s);
       break;

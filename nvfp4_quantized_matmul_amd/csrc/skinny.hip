@@ -72,12 +72,64 @@ __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Activation types: 16-byte loads per MFMA step (8 activations per lane).
+template <typename TX> struct XLoads { static constexpr int n = sizeof(TX) / 2; };
+
+// Eight elements of one word times the block scale s as exact f16 (every
+// product e2m1 * e4m3 lies in [2^-10, 2688] with at most 6 significant
+// bits, and every E4M3 value is an f16).  One FP4 convert and one packed
+// f16 multiply per pair.
+__device__ __forceinline__ f16x8_t decode_word_f16(uint32_t w, float s) {
+  const _Float16 h = (_Float16)s;
+  const f16x2_t ss = {h, h};
+  const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  const uint32_t d[4] = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                         __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+  return __builtin_bit_cast(f16x8_t, d);
+}
+
+// Eight float32 activations split exactly into three bf16 vectors whose sum
+// is the input: hi keeps the top 8 significand bits (truncation), mid the
+// next 8 of the remainder, lo the rest (at most 8 bits, so exact).  The
+// products with an exact bf16 weight are exact in the MFMA, so three MFMAs
+// give the float32 products.  Infinities and NaNs go whole into hi (a NaN
+// keeps a mantissa bit), with mid and lo zero.
+__device__ __forceinline__ void split3(const uint4 a, const uint4 b, bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
+  const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bool fin = (u[e] & 0x7f800000u) != 0x7f800000u;
+    h[e] = (u[e] & 0xffff0000u) | ((!fin && (u[e] & 0x007fffffu)) ? 0x00400000u : 0u);
+    const float r1 = fin ? __builtin_bit_cast(float, u[e]) - __builtin_bit_cast(float, h[e]) : 0.0f;
+    m[e] = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
+    const float r2 = r1 - __builtin_bit_cast(float, m[e]);
+    l[e] = __builtin_bit_cast(uint32_t, r2);
+  }
+  uint32_t ph[4], pm[4], pl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ph[j] = __builtin_amdgcn_perm(h[2 * j + 1], h[2 * j], 0x07060302u);
+    pm[j] = __builtin_amdgcn_perm(m[2 * j + 1], m[2 * j], 0x07060302u);
+    pl[j] = __builtin_amdgcn_perm(l[2 * j + 1], l[2 * j], 0x07060302u);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, ph);
+  mid = __builtin_bit_cast(bf16x8_t, pm);
+  lo = __builtin_bit_cast(bf16x8_t, pl);
+}
+
 // One pair-group's operands for one lane.
-template <int MF>
+template <int MF, typename TX = __bf16>
 struct PairGroup {
   uint4 w[kTiles][2]; // [tile][chunk]: words 4q..4q+3 of the chunk
   uint4 s[kTiles];    // [tile]: the row's 16 scale bytes of the pair-group
-  uint4 x[MF][8];     // [fragment][step 4c+i]: activations of word 16c+4i+q
+  uint4 x[MF][8][XLoads<TX>::n];  // [fragment][step 4c+i]: activations of word 16c+4i+q
 };
 
 template <int MF>
@@ -85,7 +137,7 @@ struct Sources {
   rsrc_t w, s, x;         // weight plane, scale plane, activations
   uint32_t wo[kTiles];    // byte offset of this lane's weight row in tile t, + 16q
   uint32_t so[kTiles];    // byte offset of its scale row
-  uint32_t xo[MF];        // byte offset of this lane's activation row in fragment f, + 16q
+  uint32_t xo[MF];        // byte offset of this lane's activation row in fragment f, + 8q elements
 };
 
 // Offsets of weight rows n0 + 16t + r (lane r = lane % 16, q = lane / 16).
@@ -102,15 +154,18 @@ __device__ __forceinline__ void set_rows(Sources<MF>& src, int64_t n0, int r16, 
 // activations, then scales and words tile by tile; chunk 1: activations,
 // words), so the in-order load counter lets chunk 0 be multiplied while
 // chunk 1 is still arriving.
-template <int MF>
-__device__ __forceinline__ void load_pg(PairGroup<MF>& p, const Sources<MF>& src, uint32_t pg) {
+template <typename TX, int MF>
+__device__ __forceinline__ void load_pg(PairGroup<MF, TX>& p, const Sources<MF>& src, uint32_t pg) {
+  constexpr uint32_t E = sizeof(TX);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
     for (int f = 0; f < MF; ++f)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)        // bf16 offset 256 pg + 128c + 32i
-        p.x[f][4 * c + i] = load16(src.x, src.xo[f], pg * 512u + c * 256u + i * 64u);
+      for (int i = 0; i < 4; ++i)        // element offset 256 pg + 128c + 32i
+#pragma unroll
+        for (int h = 0; h < XLoads<TX>::n; ++h)
+          p.x[f][4 * c + i][h] = load16(src.x, src.xo[f], (pg * 256u + c * 128u + i * 32u) * E + h * 16u);
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       if (c == 0) p.s[t] = load16(src.s, src.so[t], pg * 16u);           // 16 scale bytes per pair-group
@@ -132,8 +187,8 @@ __device__ __forceinline__ void transpose_q(const uint4 v, uint32_t (&o)[4]) {
   o[3] = d[1];
 }
 
-template <int MF>
-__device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const PairGroup<MF>& p, int half) {
+template <typename TX, int MF>
+__device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const PairGroup<MF, TX>& p, int half) {
   // word 4i+q of chunk c uses scale byte 8c + 2i + q/2: dword 2c + i/2,
   // byte 2(i%2) + q/2
   const uint32_t sh = 8u * (uint32_t)half;
@@ -148,18 +203,36 @@ __device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const Pai
       const float sc[4] = {e4m3<0>(d0), e4m3<2>(d0), e4m3<0>(d1), e4m3<2>(d1)};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8_t A = decode_word_bf16(wd[i], sc[i]);
+        if constexpr (__is_same(TX, _Float16)) {
+          const f16x8_t A = decode_word_f16(wd[i], sc[i]);
 #pragma unroll
-        for (int f = 0; f < MF; ++f)
-          acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              A, __builtin_bit_cast(bf16x8_t, p.x[f][4 * c + i]), acc[t][f], 0, 0, 0);
+          for (int f = 0; f < MF; ++f)
+            acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                A, __builtin_bit_cast(f16x8_t, p.x[f][4 * c + i][0]), acc[t][f], 0, 0, 0);
+        } else if constexpr (__is_same(TX, float)) {
+          const bf16x8_t A = decode_word_bf16(wd[i], sc[i]);
+#pragma unroll
+          for (int f = 0; f < MF; ++f) {
+            bf16x8_t hi, mid, lo;
+            split3(p.x[f][4 * c + i][0], p.x[f][4 * c + i][1], hi, mid, lo);
+            acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, hi, acc[t][f], 0, 0, 0);
+            acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, mid, acc[t][f], 0, 0, 0);
+            acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, lo, acc[t][f], 0, 0, 0);
+          }
+        } else {
+          const bf16x8_t A = decode_word_bf16(wd[i], sc[i]);
+#pragma unroll
+          for (int f = 0; f < MF; ++f)
+            acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A, __builtin_bit_cast(bf16x8_t, p.x[f][4 * c + i][0]), acc[t][f], 0, 0, 0);
+        }
       }
     }
   }
 }
 
 // This wavefront's pair-groups wid, wid + nw, ... into acc.
-template <int MF>
+template <typename TX, int MF>
 __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const Sources<MF>& src, int wid,
                                                int nw, int64_t npg, int half) {
 #pragma unroll
@@ -168,7 +241,7 @@ __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const
     for (int f = 0; f < MF; ++f)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[t][f][i] = 0.0f;
-  PairGroup<MF> p;
+  PairGroup<MF, TX> p;
   for (int64_t pg = wid; pg < npg; pg += nw) {
     load_pg(p, src, (uint32_t)pg);
     // keep every load ahead of the multiply: the scheduler would otherwise
@@ -180,14 +253,15 @@ __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const
 
 // C[n][m] of tile t: element i of lane l is weight row 16t + 4(l/16) + i,
 // activation row l % 16 of the fragment; four bf16 to out row `orow`.
-__device__ __forceinline__ void store4(__bf16* out, int64_t orow, int64_t n, int64_t N, const f32x4_t v,
-                                       float g) {
-  __bf16 o[4];
+template <typename TO>
+__device__ __forceinline__ void store4(TO* out, int64_t orow, int64_t n, int64_t N, const f32x4_t v, float g) {
+  TO o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (__bf16)(v[i] * g);
-  __bf16* po = out + orow * N + n;
+  for (int i = 0; i < 4; ++i) o[i] = (TO)(v[i] * g);
+  TO* po = out + orow * N + n;
   if ((N % 4) == 0 && n + 3 < N) {
-    *reinterpret_cast<uint2*>(po) = __builtin_bit_cast(uint2, o);
+    if constexpr (sizeof(TO) == 4) *reinterpret_cast<uint4*>(po) = __builtin_bit_cast(uint4, o);
+    else *reinterpret_cast<uint2*>(po) = __builtin_bit_cast(uint2, o);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -195,12 +269,12 @@ __device__ __forceinline__ void store4(__bf16* out, int64_t orow, int64_t n, int
   }
 }
 
-template <int MF, int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const __bf16* __restrict__ x,
+template <typename TX, int MF, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict__ x,
                                                           const uint32_t* __restrict__ w,
                                                           const uint8_t* __restrict__ sc,
                                                           const float* __restrict__ gs,
-                                                          __bf16* __restrict__ out, int64_t M,
+                                                          TX* __restrict__ out, int64_t M,
                                                           int64_t K, int64_t N) {
   __shared__ f32x4_t red[MAXW][kTiles * MF][64];
 
@@ -213,13 +287,13 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const __bf16* __restr
   Sources<MF> src;
   src.w = plane(w, N * (K / 2));
   src.s = plane(sc, N * (K / 16));
-  src.x = plane(x, M * K * 2);
+  src.x = plane(x, M * K * (int64_t)sizeof(TX));
   set_rows(src, n0, r16, q, K);
 #pragma unroll
-  for (int f = 0; f < MF; ++f) src.xo[f] = (uint32_t)((16 * f + r16) * K * 2 + 16 * q);
+  for (int f = 0; f < MF; ++f) src.xo[f] = (uint32_t)(((16 * f + r16) * K + 8 * q) * (int64_t)sizeof(TX));
 
   f32x4_t acc[kTiles][MF];
-  run_pairgroups(acc, src, wid, nw, K / kPG, q >> 1);
+  run_pairgroups<TX>(acc, src, wid, nw, K / kPG, q >> 1);
 
   // Partial sums of the wavefronts, added in wavefront order.
 #pragma unroll
@@ -244,13 +318,25 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const __bf16* __restr
 }
 
 // One wavefront per pair-group up to MAXW wavefronts.
-template <int MF, int MAXW>
-void launch_mf(const __bf16* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
-               const float* gs, __bf16* out, hipStream_t s) {
+template <typename TX, int MF, int MAXW>
+void launch_mf(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
+               const float* gs, TX* out, hipStream_t s) {
   const int64_t blocks = (N + kRows - 1) / kRows;
   const int64_t npg = K / kPG;
   const int waves = (int)(npg < MAXW ? npg : MAXW);
-  skinny_kernel<MF, MAXW><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, N);
+  skinny_kernel<TX, MF, MAXW><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, N);
+}
+
+// 16-bit activations: up to four 16-row fragments in one launch.
+template <typename TX>
+void launch_rows16(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
+                   const float* gs, TX* out, hipStream_t s) {
+  switch ((M + 15) / 16) {
+    case 1: launch_mf<TX, 1, 16>(x, M, K, N, w, sc, gs, out, s); break;
+    case 2: launch_mf<TX, 2, 8>(x, M, K, N, w, sc, gs, out, s); break;
+    case 3: launch_mf<TX, 3, 4>(x, M, K, N, w, sc, gs, out, s); break;
+    default: launch_mf<TX, 4, 4>(x, M, K, N, w, sc, gs, out, s); break;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -343,7 +429,7 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(4))) 
           src.xo[0] = (uint32_t)(list_x[j / Mg] * Mg + j % Mg) * xrow_bytes + 16u * q;
         }
         f32x4_t acc[kTiles][1];
-        run_pairgroups(acc, src, wid, nw, K / kPG, q >> 1);
+        run_pairgroups<__bf16>(acc, src, wid, nw, K / kPG, q >> 1);
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) red[wid][t][lane] = acc[t][0];
         __syncthreads();
@@ -370,20 +456,31 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(4))) 
 
 namespace nvfp4host {
 
-bool launch_skinny(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                    const uint8_t* sc, const float* gs, void* out, hipStream_t s) {
   // 16-byte activation, word and scale loads; byte offsets within 32 bits.
   const bool aligned =
       ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(sc)) & 15) == 0;
   if (M < 2 || M > 64 || K % kPG != 0 || !aligned) return false;
-  if ((N + kRows) * (K / 2) >= kMaxPlaneBytes || 64 * K * 2 >= kMaxPlaneBytes) return false;
-  const __bf16* xb = static_cast<const __bf16*>(x);
-  __bf16* ob = static_cast<__bf16*>(out);
-  switch ((M + 15) / 16) {
-    case 1: launch_mf<1, 16>(xb, M, K, N, w, sc, gs, ob, s); break;
-    case 2: launch_mf<2, 8>(xb, M, K, N, w, sc, gs, ob, s); break;
-    case 3: launch_mf<3, 4>(xb, M, K, N, w, sc, gs, ob, s); break;
-    default: launch_mf<4, 4>(xb, M, K, N, w, sc, gs, ob, s); break;
+  if ((N + kRows) * (K / 2) >= kMaxPlaneBytes || 64 * K * 4 >= kMaxPlaneBytes) return false;
+  switch (dt) {
+    case NVFP4_BF16:
+      launch_rows16(static_cast<const __bf16*>(x), M, K, N, w, sc, gs, static_cast<__bf16*>(out), s);
+      break;
+    case NVFP4_F16:
+      launch_rows16(static_cast<const _Float16*>(x), M, K, N, w, sc, gs, static_cast<_Float16*>(out), s);
+      break;
+    case NVFP4_F32: {
+      // float32 activations hold twice the registers: up to 32 rows per launch
+      const float* xf = static_cast<const float*>(x);
+      float* of = static_cast<float*>(out);
+      for (int64_t m0 = 0; m0 < M; m0 += 32) {
+        const int64_t rows = M - m0 < 32 ? M - m0 : 32;
+        if (rows <= 16) launch_mf<float, 1, 8>(xf + m0 * K, rows, K, N, w, sc, gs, of + m0 * N, s);
+        else launch_mf<float, 2, 4>(xf + m0 * K, rows, K, N, w, sc, gs, of + m0 * N, s);
+      }
+      break;
+    }
   }
   return true;
 }

@@ -59,10 +59,10 @@ def test_route_selection(lib):
     assert nv.qmv_max_rows() == 33
     assert nv.select_route(1, 5376, 21504) == "qmv"
     assert nv.select_route(33, 4096, 14336, dtype=torch.float32) == "qmv"
-    assert nv.select_route(34, 4096, 14336, dtype=torch.float32) == "gemm"
-    assert nv.select_route(64, 4096, 14336) == "qmv"                 # bf16, K % 256 == 0
+    assert nv.select_route(34, 4096, 14336, dtype=torch.float32) == "qmv"   # K % 256 == 0
+    assert nv.select_route(64, 4096, 14336) == "qmv"
     assert nv.select_route(65, 4096, 14336) == "gemm"
-    assert nv.select_route(34, 4112, 14336) == "gemm"                # K % 256 != 0
+    assert nv.select_route(34, 4112, 14336, dtype=torch.float32) == "gemm"  # K % 256 != 0
     assert nv.select_route(2048, 5376, 21504) == "gemm"
     # non-transposed planes always take the GEMM route, any K, N % 16 == 0
     assert nv.select_route(1, 17, 32, transpose=False) == "gemm"

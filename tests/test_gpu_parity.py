@@ -455,15 +455,18 @@ def test_gemm_slab_pipeline_shapes(K, M, N):
     assert rel(out, ref) <= TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("K", [256, 512, 1792, 2048, 2304, 4352, 6144])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("K", [256, 512, 2304, 4352, 6144])
 @pytest.mark.parametrize("M", [2, 15, 17, 33, 48, 64])
 @pytest.mark.parametrize("N", [40, 300])
-def test_multirow_mfma_pipeline_shapes(K, M, N):
-    """bf16 qmv route for 2 <= M <= 64 with K a multiple of 256 (the MFMA
-    kernel): 1, 2, 7, 8, 9, 17 and 24 pair-groups of 256 k over eight
-    wavefronts leave idle wavefronts, one, two and three pair-groups per
-    wavefront (both register sets of the prefetch loop, odd and even
-    counts); 1..4 activation fragments; N leaves partial 32-row tiles."""
-    case = synth.dense_case(3800 + K + M + N, M, K, N, with_gs=True)
-    out, ref = run_qmm(case, torch.bfloat16, "qmv", guard=True)
-    assert rel(out, ref) <= TOL[torch.bfloat16]
+def test_multirow_mfma_pipeline_shapes(dtype, K, M, N):
+    """qmv route for 2 <= M <= 64 with K a multiple of 256 (the MFMA
+    kernel): 1, 2, 9, 17 and 24 pair-groups of 256 k over up to 16, 8 or 4
+    wavefronts leave one to six pair-groups per wavefront; 1..4 activation
+    fragments (bf16, f16) or 16-row launches (f32, split into three bf16
+    parts); N leaves partial 64-row tiles.  f16 uses small scale codes so
+    its outputs stay finite."""
+    codes = (0x08, 0x50) if dtype == torch.float16 else synth.NORMAL_POSITIVE_CODES
+    case = synth.dense_case(3800 + K + M + N, M, K, N, with_gs=True, code_range=codes)
+    out, ref = run_qmm(case, dtype, "qmv", guard=True)
+    assert rel(out, ref) <= TOL[dtype]
