@@ -434,7 +434,7 @@ def main():
                                  "kernel": "gemm_mfma_v3_kernel", "kernel_duration": pdur}},
         "multirow_m16": {"workload": "multirow_qmv_m16_k4096_n14336_bf16", "value": round(mgbs, 2),
                          "unit": "GB/s", "frac_hbm": round(mgbs / HBM_PEAK_GBS, 4),
-                         "kernel": "skinny_kernel<1,16>", "kernel_duration": mdur, "bytes": mr.bytes},
+                         "kernel": "skinny_kernel<bf16,1,16>", "kernel_duration": mdur, "bytes": mr.bytes},
         "moe_sorted_prefill": {"workload": "moe_gather_e128_n1536_k2048_top8_b128_sorted",
                                "value": round(sgbs, 2), "unit": "GB/s",
                                "frac_hbm": round(sgbs / HBM_PEAK_GBS, 4), "distinct_experts": gs_sorted.distinct,

@@ -384,27 +384,40 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
 #undef NVFP4_V3_STEP
 
   // Epilogue: fragment (a, b) holds C[n][m] with n = 8*jj + 4h + i, m = l32.
+  // A swap between the lane halves gives lane h the eight consecutive n
+  // 16p + 8h .. 16p + 8h + 7 of jj pair p, stored as one 16-byte write.
   const float g = global_factor(gs, 0);
-  const bool vec_ok = (N % 4) == 0;
+  const bool vec_ok = (N % 8) == 0;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const int64_t m = m_blk + b * 32 + l32;
-      if (m >= M) continue;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t n = n_blk + wave * 64 + a * 32 + jj * 8 + h * 4;
-        __bf16 v[4];
+      for (int p = 0; p < 2; ++p) {
+        uint32_t r0[2], r1[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[a][b][jj * 4 + i] * g);
-        __bf16* p = out + m * N + n;
-        if (vec_ok && n + 3 < N) {
-          *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, v);
+        for (int d = 0; d < 2; ++d) {
+          const __bf16 lo0 = (__bf16)(acc[a][b][(2 * p) * 4 + 2 * d] * g);
+          const __bf16 hi0 = (__bf16)(acc[a][b][(2 * p) * 4 + 2 * d + 1] * g);
+          const __bf16 lo1 = (__bf16)(acc[a][b][(2 * p + 1) * 4 + 2 * d] * g);
+          const __bf16 hi1 = (__bf16)(acc[a][b][(2 * p + 1) * 4 + 2 * d + 1] * g);
+          r0[d] = (uint32_t)__builtin_bit_cast(uint16_t, lo0) | ((uint32_t)__builtin_bit_cast(uint16_t, hi0) << 16);
+          r1[d] = (uint32_t)__builtin_bit_cast(uint16_t, lo1) | ((uint32_t)__builtin_bit_cast(uint16_t, hi1) << 16);
+        }
+        const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r1[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(r0[1], r1[1], false, false);
+        const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        const int64_t n = n_blk + wave * 64 + a * 32 + 16 * p + 8 * h;
+        if (m >= M) continue;
+        __bf16* q = out + m * N + n;
+        if (vec_ok && n + 7 < N) {
+          *reinterpret_cast<uint4*>(q) = v;
         } else {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (n + i < N) p[i] = v[i];
+          for (int i = 0; i < 8; ++i)
+            if (n + i < N) q[i] = __builtin_bit_cast(__bf16, (uint16_t)(wv[i / 2] >> (16 * (i % 2))));
         }
       }
     }
