@@ -141,6 +141,32 @@ int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
               hipStream_t stream);
 
 /*
+ * nvfp4_qmm_batched -- nvfp4_qmm over a batch of weight matrices (mlxcel PR
+ * "native NVFP4 for ROCm QuantizedMatmul/GatherQMM", "Numerical results":
+ * qmm with batched weights, on the qmv route at M = 3 and the GEMM route at
+ * M = 64).  For b in [0, B):
+ *
+ *   out[b] = x[XB == 1 ? 0 : b] @ dequantize(w[b]).T * g[b]   (transpose = 1)
+ *   out[b] = x[XB == 1 ? 0 : b] @ dequantize(w[b])   * g[b]   (transpose = 0)
+ *
+ *   x       [XB, M, K] of dtype, XB = 1 (one activation matrix for every
+ *           weight matrix) or XB = B
+ *   w       transpose = 1: uint32 [B, N, K/8]; transpose = 0: [B, K, N/8]
+ *   scales  uint8 w.shape[:-1] + [w.shape[-1] / 2]
+ *   gs      float [B] or NULL; g[b] = fl32(gs[b] / 2688) (1 without gs)
+ *   out     [B, M, N] of dtype
+ *
+ * Every matrix takes the route nvfp4_qmm would take for (M, K, N).  All
+ * checks, including the alignment nvfp4_qmm needs of every matrix's x, w,
+ * scales and out pointers, run before anything is enqueued: a negative
+ * status launches nothing.  B = 0 is a no-op.
+ */
+int nvfp4_qmm_batched(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B,
+                      int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                      const uint8_t* scales, const float* gs, int transpose,
+                      nvfp4_route_t route, void* out, hipStream_t stream);
+
+/*
  * nvfp4_gather_qmm -- GatherQMM over NVFP4 experts (mlxcel PR "native NVFP4
  * for ROCm QuantizedMatmul/GatherQMM", "Summary": the per-expert global
  * scale, a weight group reloaded only when the expert changes; "Changes

@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "NVFP4Error", "library_path", "load_library", "transcode", "dequantize", "qmm",
-    "gather_qmm", "select_route", "qmv_max_rows", "status_string",
+    "qmm_batched", "gather_qmm", "select_route", "qmv_max_rows", "status_string",
     "ROUTE_AUTO", "ROUTE_QMV", "ROUTE_GEMM",
 ]
 
@@ -66,6 +66,7 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_transcode": [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp],
         "nvfp4_dequantize": [vp, vp, vp, i64, i64, i64, c_int, vp, vp],
         "nvfp4_qmm": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
+        "nvfp4_qmm_batched": [vp, c_int, i64, i64, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_gather_qmm": [vp, c_int, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, i64, c_int, vp, vp],
         "nvfp4_select_route": [i64, i64, i64, c_int, c_int],
         "nvfp4_qmv_max_rows": [],
@@ -257,6 +258,46 @@ def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[tor
     _require_gpu(out)
     _check("nvfp4_qmm", lib.nvfp4_qmm(
         _ptr(x), code, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), int(bool(transpose)),
+        _ROUTES[route], _ptr(out), _stream(dev)))
+    return out
+
+
+def qmm_batched(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
+                gs: Optional[torch.Tensor] = None, transpose: bool = True, route: str = "auto",
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qmm over a batch of weight matrices: out[b] = x[b or 0] @ dequantize(w[b]).T.
+
+    x [XB, M, K] with XB = 1 (shared by every matrix) or XB = B; w [B, N, K/8]
+    (transpose) or [B, K, N/8]; scales as for check_planes; gs float32 [B] or
+    None.  Returns [B, M, N] in x's dtype.
+    """
+    check_planes(w, scales)
+    if w.dim() != 3 or x.dim() != 3:
+        raise ValueError("qmm_batched takes x [XB, M, K] and a 3-D weight plane")
+    B = w.shape[0]
+    if transpose:
+        N, K = w.shape[1], w.shape[2] * 8
+    else:
+        K, N = w.shape[1], w.shape[2] * 8
+    XB, M = x.shape[0], x.shape[1]
+    if x.shape[2] != K:
+        raise ValueError(f"x has K={x.shape[2]}, weight plane implies K={K}")
+    if XB not in (1, B):
+        raise ValueError(f"x batch {XB} must be 1 or the weight batch {B}")
+    if gs is not None and (gs.dtype != torch.float32 or gs.numel() != B):
+        raise ValueError("gs must be float32 with one value per weight matrix")
+    if route not in _ROUTES:
+        raise ValueError(f"route must be one of {sorted(_ROUTES)}")
+    code = _dtype_code(x.dtype)
+    dev = _require_gpu(x, w, scales, gs)
+    lib = load_library()
+    if out is None:
+        out = torch.empty((B, M, N), dtype=x.dtype, device=dev)
+    elif out.dtype != x.dtype or tuple(out.shape) != (B, M, N):
+        raise ValueError("out has the wrong dtype or shape")
+    _require_gpu(out)
+    _check("nvfp4_qmm_batched", lib.nvfp4_qmm_batched(
+        _ptr(x), code, XB, B, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), int(bool(transpose)),
         _ROUTES[route], _ptr(out), _stream(dev)))
     return out
 

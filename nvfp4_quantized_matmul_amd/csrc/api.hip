@@ -44,6 +44,61 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
 }
 
+// What one qmm call launches, decided on the host with every check done.
+struct QmmPlan {
+  enum Kind { kNothing, kZeroFill, kQmv, kGemmMfma, kGemmGeneric } kind;
+};
+
+// All host checks of one nvfp4_qmm call (no launch).
+int qmm_plan(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+             const uint8_t* scales, const float* gs, int transpose, nvfp4_route_t route, const void* out,
+             QmmPlan* plan) {
+  plan->kind = QmmPlan::kNothing;
+  const int auto_route = nvfp4_select_route(M, K, N, transpose, dtype);
+  if (auto_route < 0) return auto_route;
+  if (route != NVFP4_ROUTE_AUTO && route != NVFP4_ROUTE_QMV && route != NVFP4_ROUTE_GEMM) return NVFP4_ERR_ROUTE;
+  if (route == NVFP4_ROUTE_QMV && !transpose) return NVFP4_ERR_ROUTE;
+  int64_t t;
+  if (!mul_ok(M, K, &t) || !mul_ok(M, N, &t) || !mul_ok(K, N, &t)) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!out) return NVFP4_ERR_NULLPTR;
+  if (!aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  if (K == 0) {
+    plan->kind = QmmPlan::kZeroFill;
+    return NVFP4_OK;
+  }
+  if (!x || !w || !scales) return NVFP4_ERR_NULLPTR;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scales, 2) || (gs && !aligned(gs, 4))) return NVFP4_ERR_ALIGN;
+  const int r = route == NVFP4_ROUTE_AUTO ? auto_route : (int)route;
+  if (r == NVFP4_ROUTE_QMV) {
+    if ((N + 15) / 16 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    plan->kind = QmmPlan::kQmv;
+  } else if (dtype == NVFP4_BF16 && transpose && K % 32 == 0) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    plan->kind = QmmPlan::kGemmMfma;
+  } else {
+    if ((N + 63) / 64 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    plan->kind = QmmPlan::kGemmGeneric;
+  }
+  return NVFP4_OK;
+}
+
+// Enqueues what qmm_plan decided (arguments already checked).
+void qmm_launch(const QmmPlan& plan, const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N,
+                const uint32_t* w, const uint8_t* scales, const float* gs, int transpose, void* out,
+                hipStream_t stream) {
+  switch (plan.kind) {
+    case QmmPlan::kNothing: break;
+    case QmmPlan::kZeroFill: nvfp4host::launch_fill_zero(out, M * N * dtype_size(dtype), stream); break;
+    case QmmPlan::kQmv: nvfp4host::launch_qmv(x, dtype, M, K, N, w, scales, gs, out, stream); break;
+    case QmmPlan::kGemmMfma: nvfp4host::launch_gemm_mfma(x, M, K, N, w, scales, gs, out, stream); break;
+    case QmmPlan::kGemmGeneric:
+      nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
+      break;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,33 +176,48 @@ int nvfp4_dequantize(const uint32_t* w, const uint8_t* scales, const float* gs, 
 int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N,
               const uint32_t* w, const uint8_t* scales, const float* gs, int transpose,
               nvfp4_route_t route, void* out, hipStream_t stream) {
-  const int auto_route = nvfp4_select_route(M, K, N, transpose, dtype);
-  if (auto_route < 0) return auto_route;
-  if (route != NVFP4_ROUTE_AUTO && route != NVFP4_ROUTE_QMV && route != NVFP4_ROUTE_GEMM) return NVFP4_ERR_ROUTE;
-  if (route == NVFP4_ROUTE_QMV && !transpose) return NVFP4_ERR_ROUTE;
-  int64_t t;
-  if (!mul_ok(M, K, &t) || !mul_ok(M, N, &t) || !mul_ok(K, N, &t)) return NVFP4_ERR_SHAPE;
-  if (M == 0 || N == 0) return NVFP4_OK;
-  if (!out) return NVFP4_ERR_NULLPTR;
-  if (!aligned(out, 16)) return NVFP4_ERR_ALIGN;
-  if (K == 0) {
-    nvfp4host::launch_fill_zero(out, M * N * dtype_size(dtype), stream);
-    return launched();
+  QmmPlan plan;
+  const int st = qmm_plan(x, dtype, M, K, N, w, scales, gs, transpose, route, out, &plan);
+  if (st != NVFP4_OK) return st;
+  if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
+  qmm_launch(plan, x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
+  return launched();
+}
+
+int nvfp4_qmm_batched(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B, int64_t M, int64_t K,
+                      int64_t N, const uint32_t* w, const uint8_t* scales, const float* gs,
+                      int transpose, nvfp4_route_t route, void* out, hipStream_t stream) {
+  if (B < 0 || XB < 0 || M < 0 || K < 0 || N < 0) return NVFP4_ERR_SHAPE;
+  if (B == 0) return (XB == 0 || XB == 1) ? NVFP4_OK : NVFP4_ERR_SHAPE;
+  if (XB != 1 && XB != B) return NVFP4_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  if (transpose != 0 && transpose != 1) return NVFP4_ERR_SHAPE;
+  if (transpose ? (K % 16) != 0 : (N % 16) != 0) return NVFP4_ERR_SHAPE;
+  // Per-matrix strides (elements of x and out, words of w, bytes of scales);
+  // every total must fit in int64.
+  const int64_t ds = dtype_size(dtype);
+  int64_t xs, ws, ss, os, t;
+  if (!mul_ok(M, K, &xs) || !mul_ok(M, N, &os) || !mul_ok(N, K, &t)) return NVFP4_ERR_SHAPE;
+  ws = t / 8;
+  ss = t / 16;
+  if (!size3(XB, xs, ds, &t) || !size3(B, os, ds, &t) || !size3(B, ws, 4, &t) || !mul_ok(B, ss, &t))
+    return NVFP4_ERR_SHAPE;
+  if (XB == 1) xs = 0;
+  const char* xb = static_cast<const char*>(x);
+  char* ob = static_cast<char*>(out);
+  // Every slice is checked before anything is enqueued.
+  QmmPlan plan{};
+  for (int64_t b = 0; b < B; ++b) {
+    const int st = qmm_plan(xb ? xb + b * xs * ds : nullptr, dtype, M, K, N, w ? w + b * ws : nullptr,
+                            scales ? scales + b * ss : nullptr, gs ? gs + b : nullptr, transpose, route,
+                            ob ? ob + b * os * ds : nullptr, &plan);
+    if (st != NVFP4_OK) return st;
   }
-  if (!x || !w || !scales) return NVFP4_ERR_NULLPTR;
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scales, 2) || (gs && !aligned(gs, 4))) return NVFP4_ERR_ALIGN;
-  const int r = route == NVFP4_ROUTE_AUTO ? auto_route : (int)route;
-  if (r == NVFP4_ROUTE_QMV) {
-    if ((N + 15) / 16 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
-    nvfp4host::launch_qmv(x, dtype, M, K, N, w, scales, gs, out, stream);
-  } else if (dtype == NVFP4_BF16 && transpose && K % 32 == 0) {
-    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
-    nvfp4host::launch_gemm_mfma(x, M, K, N, w, scales, gs, out, stream);
-  } else {
-    if ((N + 63) / 64 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
-    nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
-  }
+  if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
+  for (int64_t b = 0; b < B; ++b)
+    qmm_launch(plan, xb ? xb + b * xs * ds : nullptr, dtype, M, K, N, w ? w + b * ws : nullptr,
+               scales ? scales + b * ss : nullptr, gs ? gs + b : nullptr, transpose, ob + b * os * ds,
+               stream);
   return launched();
 }
 

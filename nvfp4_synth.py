@@ -89,6 +89,35 @@ def dense_case(seed: int, M: int, K: int, N: int, transpose: bool = True,
 
 
 @dataclass
+class BatchedCase:
+    """Planes and activations for one batched-weight qmm call."""
+    B: int
+    XB: int
+    M: int
+    K: int
+    N: int
+    transpose: bool
+    x: np.ndarray                 # float32 [XB, M, K]
+    w: np.ndarray                 # uint32 [B, N, K/8] or [B, K, N/8]
+    scales: np.ndarray            # uint8, w.shape[:-1] + [w.shape[-1] / 2]
+    gs: Optional[np.ndarray]      # float32 [B] or None
+
+
+def batched_case(seed: int, B: int, M: int, K: int, N: int, broadcast_x: bool = False,
+                 transpose: bool = True, with_gs: bool = True,
+                 code_range=NORMAL_POSITIVE_CODES) -> BatchedCase:
+    """B weight matrices and either one activation matrix (broadcast_x) or B."""
+    g = rng(seed)
+    rows, qlen = (N, K) if transpose else (K, N)
+    w = packed_words(g, (B, rows, qlen // 8))
+    sc = scale_codes(g, (B, rows, qlen // 16), code_range)
+    gs = global_scales(g, B) if with_gs else None
+    XB = 1 if broadcast_x else B
+    x = activations(g, (XB, M, K))
+    return BatchedCase(B, XB, M, K, N, transpose, x, w, sc, gs)
+
+
+@dataclass
 class GatherCase:
     """Planes, activations and index pairs for one GatherQMM call."""
     X: int

@@ -20,6 +20,7 @@ from .nvfp4_oracle import (  # noqa: F401
     gather_qmm,
     global_factor,
     qmm,
+    qmm_batched,
     relative_error,
     transcode,
     unpack_nibbles,

@@ -203,6 +203,32 @@ def qmm(x: np.ndarray, w: np.ndarray, scales: np.ndarray, gs=None,
     return x64 @ W
 
 
+def qmm_batched(x: np.ndarray, w: np.ndarray, scales: np.ndarray, gs=None,
+                transpose: bool = True) -> np.ndarray:
+    """Reference qmm over a batch of weight matrices (P3 "Numerical results":
+    qmm with batched weights, checked against x @ dequantize(w).T per matrix).
+
+    x [XB, M, K] with XB = 1 (one activation matrix for every weight matrix)
+    or XB = B; w [B, N, K/8] (transpose) or [B, K, N/8]; scales shaped from w;
+    gs [B] or None, one global scale per weight matrix.
+    out[b] = qmm(x[0 if XB == 1 else b], w[b], scales[b], gs[b]).  Returns
+    float64 [B, M, N].
+    """
+    B = w.shape[0]
+    XB = x.shape[0]
+    if XB not in (1, B):
+        raise ValueError("x batch must be 1 or match the weight batch")
+    parts = []
+    for b in range(B):
+        src = x[0] if XB == 1 else x[b]
+        parts.append(qmm(src, w[b], scales[b], None if gs is None else gs[b], transpose=transpose))
+    if not parts:
+        M = x.shape[1]
+        N = w.shape[1] if transpose else w.shape[2] * NIBBLES_PER_WORD
+        return np.zeros((0, M, N), dtype=np.float64)
+    return np.stack(parts)
+
+
 def gather_qmm(x: np.ndarray, lhs: Optional[np.ndarray], rhs: np.ndarray,
                w: np.ndarray, scales: np.ndarray, gs: Optional[np.ndarray]) -> np.ndarray:
     """Reference GatherQMM over experts (P3 "Summary": GatherQMM with a

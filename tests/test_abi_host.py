@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_qmm", "nvfp4_gather_qmm",
+    for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_qmm", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
         assert want in names
 
@@ -96,6 +96,31 @@ def test_qmm_validation(lib):
     # empty outputs launch nothing and succeed, even with NULL buffers
     assert qmm(lib, M=0, x=None, w=None, s=None, out=None) == OK
     assert qmm(lib, N=0, x=None, w=None, s=None, out=None) == OK
+
+
+def qmm_b(lib, x=FAKE, dt=BF16, XB=3, B=3, M=4, K=64, N=32, w=FAKE, s=FAKE, gs=None, tr=1, route=0,
+          out=FAKE):
+    return lib.nvfp4_qmm_batched(x, dt, XB, B, M, K, N, w, s, gs, tr, route, out, None)
+
+
+def test_qmm_batched_validation(lib):
+    assert qmm_b(lib, x=None) == NULLPTR
+    assert qmm_b(lib, w=None) == NULLPTR
+    assert qmm_b(lib, s=None) == NULLPTR
+    assert qmm_b(lib, out=None) == NULLPTR
+    assert qmm_b(lib, XB=2) == SHAPE                    # x batch must be 1 or B
+    assert qmm_b(lib, B=-1) == SHAPE
+    assert qmm_b(lib, K=24) == SHAPE
+    assert qmm_b(lib, dt=9) == DTYPE
+    assert qmm_b(lib, tr=0, route=1, K=17) == ROUTE
+    assert qmm_b(lib, XB=1, B=1 << 40, M=1 << 20, K=1 << 20) == SHAPE   # total size overflow
+    assert qmm_b(lib, gs=P(0x100002)) == ALIGN
+    # every matrix's pointers are checked before any launch: with M=1, N=4
+    # (bf16) the second output matrix starts 8 bytes in, not 16-aligned
+    assert qmm_b(lib, M=1, N=4) == ALIGN
+    assert qmm_b(lib, B=0, XB=1, x=None, w=None, s=None, out=None) == OK
+    assert qmm_b(lib, B=0, XB=0, x=None, w=None, s=None, out=None) == OK
+    assert qmm_b(lib, M=0, x=None, w=None, s=None, out=None) == OK
 
 
 def gather(lib, x=FAKE, dt=BF16, X=2, M=1, K=64, lhs=None, rhs=FAKE, R=4, w=FAKE, s=FAKE,

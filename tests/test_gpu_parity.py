@@ -246,6 +246,61 @@ def test_ragged_shapes(shape, dtype, route):
     assert rel(out, ref) <= TOL[dtype]
 
 
+# ----------------------------------------------------------------------------
+# qmm over a batch of weight matrices
+# ----------------------------------------------------------------------------
+
+def run_qmm_batched(c, dtype, route="auto", with_gs=True):
+    x_t, x_ref = activations(c.x, dtype)
+    gs = c.gs if with_gs else None
+    ref = oracle.qmm_batched(x_ref, c.w, c.scales, gs, transpose=c.transpose)
+    out, check = guarded((c.B, c.M, c.N), dtype)
+    nv.qmm_batched(x_t, words(c.w), u8(c.scales), None if gs is None else f32(gs),
+                   transpose=c.transpose, route=route, out=out)
+    check()
+    return out, ref
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M,route", [(1, "auto"), (3, "auto"), (3, "qmv"), (3, "gemm"), (64, "auto"),
+                                     (64, "gemm"), (300, "auto")])
+@pytest.mark.parametrize("broadcast_x", [False, True])
+def test_qmm_batched_transposed(dtype, M, route, broadcast_x):
+    """Three weight matrices (N = 272, a partial 256-row tile), each with its
+    own global scale, against their own or one shared activation matrix."""
+    c = synth.batched_case(3400 + M, B=3, M=M, K=512, N=272, broadcast_x=broadcast_x)
+    out, ref = run_qmm_batched(c, dtype, route)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("M", [3, 64])
+@pytest.mark.parametrize("with_gs", [False, True])
+def test_qmm_batched_non_transposed(dtype, M, with_gs):
+    c = synth.batched_case(3500 + M, B=2, M=M, K=40, N=48, transpose=False)
+    out, ref = run_qmm_batched(c, dtype, "auto", with_gs=with_gs)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_qmm_batched_multirow_plane(dtype):
+    """Two matrices of the multi-row workload's shape (K=4096, N=14336) at
+    M=3 through the qmv route, as the pages test batched weights."""
+    c = synth.batched_case(3600, B=2, M=3, K=4096, N=14336)
+    out, ref = run_qmm_batched(c, dtype)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+def test_qmm_batched_empty_and_misaligned():
+    c = synth.batched_case(3700, B=2, M=1, K=32, N=4)
+    x_t, _ = activations(c.x, torch.bfloat16)
+    empty = nv.qmm_batched(x_t[:0], words(c.w[:0]), u8(c.scales[:0]), f32(c.gs[:0]))
+    assert tuple(empty.shape) == (0, 1, 4)
+    # the second output matrix would start 8 bytes in: refused before any launch
+    with pytest.raises(nv.NVFP4Error):
+        nv.qmm_batched(x_t, words(c.w), u8(c.scales), f32(c.gs))
+
+
 def test_prefill_gemm_full_size_sampled():
     """M=2048, K=5376, N=21504 bf16 through the route that is timed; 48
     sampled activation rows (spread over all row tiles) against the oracle."""

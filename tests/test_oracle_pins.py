@@ -310,6 +310,30 @@ def test_qmm_one_hot_picks_a_dequantized_element():
             assert Fraction(float(got[0, n])) == W[n][k]
 
 
+@pytest.mark.parametrize("broadcast_x", [False, True])
+@pytest.mark.parametrize("transpose", [True, False])
+def test_qmm_batched_bruteforce(broadcast_x, transpose):
+    """Each weight matrix with its own global scale, against x[b] (or the
+    one shared x), by exact rational arithmetic."""
+    K = 32 if transpose else 5
+    c = synth.batched_case(24, B=3, M=2, K=K, N=16, broadcast_x=broadcast_x, transpose=transpose,
+                           with_gs=True)
+    got = orc.qmm_batched(c.x, c.w, c.scales, c.gs, transpose=transpose)
+    assert got.shape == (3, 2, 16)
+    for b in range(3):
+        src = 0 if broadcast_x else b
+        want = brute_qmm(c.x[src], c.w[b], c.scales[b], c.gs[b], transpose)
+        for m in range(2):
+            for n in range(16):
+                assert want[m][n].close(got[b, m, n]), (b, m, n)
+
+
+def test_qmm_batched_empty_batch():
+    c = synth.batched_case(25, B=1, M=2, K=32, N=16)
+    got = orc.qmm_batched(c.x, c.w[:0], c.scales[:0], c.gs[:0])
+    assert got.shape == (0, 2, 16)
+
+
 # ----------------------------------------------------------------------------
 # Gather
 # ----------------------------------------------------------------------------
@@ -393,6 +417,8 @@ PIN_TESTS = [
     lambda: test_qmm_transposed_bruteforce(True),
     lambda: test_qmm_nontransposed_k17_bruteforce(True),
     test_gather_rows_and_out_of_range_zeros,
+    lambda: test_qmm_batched_bruteforce(False, True),
+    lambda: test_qmm_batched_bruteforce(True, False),
     test_transcode_reconstructs_source_weights,
 ]
 
@@ -451,7 +477,20 @@ def _mut_gather_no_zero(x, lhs, rhs, w, scales, gs):
     return out
 
 
+def _mut_batched_x0(x, w, scales, gs=None, transpose=True):
+    return np.stack([orc.qmm(x[0], w[b], scales[b], None if gs is None else gs[b], transpose=transpose)
+                     for b in range(w.shape[0])])
+
+
+def _mut_batched_gs0(x, w, scales, gs=None, transpose=True):
+    return np.stack([orc.qmm(x[0] if x.shape[0] == 1 else x[b], w[b], scales[b],
+                             None if gs is None else gs[0], transpose=transpose)
+                     for b in range(w.shape[0])])
+
+
 MUTATIONS = {
+    "batched x always matrix 0": ("qmm_batched", _mut_batched_x0),
+    "batched global scale of matrix 0": ("qmm_batched", _mut_batched_gs0),
     "e4m3 exponent bias 8": ("e4m3_value", _mut_e4m3_bias),
     "e4m3 no NaN code": ("e4m3_value", _mut_e4m3_nan),
     "nibble order high first": ("unpack_nibbles", _mut_nibble_order),
