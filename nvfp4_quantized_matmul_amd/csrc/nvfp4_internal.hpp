@@ -32,11 +32,11 @@ void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N
 // and scales; returns false (launching nothing) otherwise.
 bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
                    const uint8_t* sc, const float* gs, void* out, hipStream_t s);
-// GatherQMM through the MFMA kernel, bf16 activations: each expert's pairs
-// are gathered and multiplied together.  Needs K % 256 == 0, E >= 1, X >= 1,
-// 16-byte aligned x, w and scales; returns false (launching nothing)
-// otherwise.
-bool launch_gather_mfma(const void* x, int64_t X, int64_t M, int64_t K, const int32_t* lhs,
+// GatherQMM through the MFMA kernel (bf16 and f16 activations directly,
+// f32 as three bf16 parts): each expert's pairs are gathered and multiplied
+// together.  Needs K % 256 == 0, E >= 1, X >= 1, 16-byte aligned x, w and
+// scales; returns false (launching nothing) otherwise.
+bool launch_gather_mfma(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t M, int64_t K, const int32_t* lhs,
                         const int32_t* rhs, int64_t R, const uint32_t* w, const uint8_t* sc,
                         const float* gs, int64_t E, int64_t N, void* out, hipStream_t s);
 // MFMA GEMM, bf16 activations, transposed plane.

@@ -304,12 +304,12 @@ void launch_gather(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t M, int64_
                    const uint8_t* sc, const float* gs, int64_t E, int64_t N, int sorted,
                    void* out, hipStream_t s) {
   const bool vec4 = (K % 32) == 0;
+  // At two or more activation rows per expert on average, gathering each
+  // expert's rows into MFMA tiles streams every plane once per 16 rows;
+  // sparser routing (decode) keeps one weight stream per pair.
+  if (R * M >= 2 * E && launch_gather_mfma(x, dt, X, M, K, lhs, rhs, R, w, sc, gs, E, N, out, s)) return;
   switch (dt) {
     case NVFP4_BF16:
-      // At two or more activation rows per expert on average, gathering
-      // each expert's rows into MFMA tiles streams every plane once per 16
-      // rows; sparser routing (decode) keeps one weight stream per pair.
-      if (R * M >= 2 * E && launch_gather_mfma(x, X, M, K, lhs, rhs, R, w, sc, gs, E, N, out, s)) break;
       if (vec4) gather_dispatch<__bf16, 4>((const __bf16*)x, X, M, K, lhs, rhs, R, w, sc, gs, E, N, sorted, (__bf16*)out, s);
       else gather_dispatch<__bf16, 2>((const __bf16*)x, X, M, K, lhs, rhs, R, w, sc, gs, E, N, sorted, (__bf16*)out, s);
       break;

@@ -347,11 +347,17 @@ void launch_rows16(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t*
 // result does not depend on the order of the pairs, so the sorted hint is
 // not needed.  Block row e == E instead writes +0.0 to the pairs whose rhs
 // is outside [0, E) or whose lhs is outside [0, X).
-template <int MAXW>
-__global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(4))) void gather_mfma_kernel(
-    const __bf16* __restrict__ x, int X, int Mg, int64_t K, const int32_t* __restrict__ lhs,
+// Waves per SIMD the gather kernel is compiled for: four keep 16-bit
+// activations within 128 registers; float32 activations (three bf16 parts)
+// need more and take two.
+template <typename TX> constexpr int gather_waves_per_eu() { return sizeof(TX) == 4 ? 2 : 4; }
+
+template <typename TX, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(gather_waves_per_eu<TX>())))
+void gather_mfma_kernel(
+    const TX* __restrict__ x, int X, int Mg, int64_t K, const int32_t* __restrict__ lhs,
     const int32_t* __restrict__ rhs, int R, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
-    const float* __restrict__ gs, int E, int64_t N, __bf16* __restrict__ out) {
+    const float* __restrict__ gs, int E, int64_t N, TX* __restrict__ out) {
   __shared__ f32x4_t red[MAXW][kTiles][64];
   __shared__ int list_r[kScanPerThread * 64 * MAXW], list_x[kScanPerThread * 64 * MAXW];
   __shared__ int wcount[kScanPerThread][MAXW];
@@ -363,13 +369,13 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(4))) 
   const int64_t n0 = (int64_t)blockIdx.x * kRows;
   const int ex = (int)blockIdx.y;                // expert, or E for the zero rows
   const bool zero_rows = ex == E;
-  const uint32_t xrow_bytes = (uint32_t)(K * 2);
+  const uint32_t xrow_bytes = (uint32_t)(K * (int64_t)sizeof(TX));
 
   Sources<1> src;
   if (!zero_rows) {
     src.w = plane(w + (int64_t)ex * N * (K / 8), N * (K / 2));
     src.s = plane(sc + (int64_t)ex * N * (K / 16), N * (K / 16));
-    src.x = plane(x, (int64_t)X * Mg * K * 2);
+    src.x = plane(x, (int64_t)X * Mg * K * (int64_t)sizeof(TX));
     set_rows(src, n0, r16, q, K);
   }
   const float g = zero_rows ? 0.0f : global_factor(gs, ex);
@@ -420,16 +426,16 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(4))) 
       for (int idx = threadIdx.x; idx < rows * kRows; idx += blockDim.x) {
         const int j = idx / kRows;
         const int64_t n = n0 + idx % kRows;
-        if (n < N) out[((int64_t)list_r[j / Mg] * Mg + j % Mg) * N + n] = (__bf16)0.0f;
+        if (n < N) out[((int64_t)list_r[j / Mg] * Mg + j % Mg) * N + n] = (TX)0.0f;
       }
     } else {
       for (int j0 = 0; j0 < rows; j0 += 16) {
         {
           const int j = j0 + r16 < rows ? j0 + r16 : rows - 1;
-          src.xo[0] = (uint32_t)(list_x[j / Mg] * Mg + j % Mg) * xrow_bytes + 16u * q;
+          src.xo[0] = (uint32_t)(list_x[j / Mg] * Mg + j % Mg) * xrow_bytes + (uint32_t)(8 * sizeof(TX)) * q;
         }
         f32x4_t acc[kTiles][1];
-        run_pairgroups<__bf16>(acc, src, wid, nw, K / kPG, q >> 1);
+        run_pairgroups<TX>(acc, src, wid, nw, K / kPG, q >> 1);
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) red[wid][t][lane] = acc[t][0];
         __syncthreads();
@@ -485,20 +491,35 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
   return true;
 }
 
-bool launch_gather_mfma(const void* x, int64_t X, int64_t M, int64_t K, const int32_t* lhs,
+bool launch_gather_mfma(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t M, int64_t K, const int32_t* lhs,
                         const int32_t* rhs, int64_t R, const uint32_t* w, const uint8_t* sc,
                         const float* gs, int64_t E, int64_t N, void* out, hipStream_t s) {
   const bool aligned =
       ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(sc)) & 15) == 0;
+  const int64_t xs = dt == NVFP4_F32 ? 4 : 2;
   if (K % kPG != 0 || K == 0 || E < 1 || X < 1 || !aligned || E + 1 > kMaxGridY) return false;
-  if ((N + kRows) * (K / 2) >= kMaxPlaneBytes || (X * M + 16) * K * 2 >= kMaxPlaneBytes) return false;
+  if ((N + kRows) * (K / 2) >= kMaxPlaneBytes || (X * M + 16) * K * xs >= kMaxPlaneBytes) return false;
   if (R >= (kMaxPlaneBytes >> 1) || E >= kMaxGridY) return false;   // pair indices (+ a scan round) in 32 bits
   const int64_t npg = K / kPG;
   const int waves = (int)(npg < 4 ? npg : 4);
   const dim3 grid((unsigned)((N + kRows - 1) / kRows), (unsigned)(E + 1));
-  gather_mfma_kernel<4><<<grid, dim3(64 * waves), 0, s>>>(static_cast<const __bf16*>(x), (int)X, (int)M, K, lhs,
-                                                          rhs, (int)R, w, sc, gs, (int)E, N,
-                                                          static_cast<__bf16*>(out));
+  switch (dt) {
+    case NVFP4_BF16:
+      gather_mfma_kernel<__bf16, 4><<<grid, dim3(64 * waves), 0, s>>>(
+          static_cast<const __bf16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
+          static_cast<__bf16*>(out));
+      break;
+    case NVFP4_F16:
+      gather_mfma_kernel<_Float16, 4><<<grid, dim3(64 * waves), 0, s>>>(
+          static_cast<const _Float16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
+          static_cast<_Float16*>(out));
+      break;
+    case NVFP4_F32:
+      gather_mfma_kernel<float, 4><<<grid, dim3(64 * waves), 0, s>>>(
+          static_cast<const float*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
+          static_cast<float*>(out));
+      break;
+  }
   return true;
 }
 

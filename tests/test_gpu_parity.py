@@ -407,35 +407,42 @@ def test_gather_sorted_hint_on_unsorted_indices():
     assert oracle.relative_error(host(b), ref) <= 1e-2
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("K", [256, 2304])
 @pytest.mark.parametrize("N", [64, 300])
 @pytest.mark.parametrize("M", [1, 3])
 @pytest.mark.parametrize("sort", [False, True])
-def test_gather_mfma_grouped_experts(K, N, M, sort):
-    """bf16 gather at several rows per expert (the expert-grouped MFMA path,
-    K % 256 == 0): ~14 pairs per expert times M rows needs one to three
-    16-row passes per expert; K = 2304 runs nine pair-groups over eight
-    wavefronts; N = 300 leaves a partial 64-row tile; out-of-range rhs and
-    lhs give exact +0.0 rows; sorted and unsorted pairs agree."""
+def test_gather_mfma_grouped_experts(K, N, M, sort, dtype):
+    """Gather at several rows per expert (the expert-grouped MFMA path,
+    K % 256 == 0; f32 activations as three bf16 parts): ~14 pairs per expert
+    times M rows needs one to three 16-row passes per expert; K = 2304 runs
+    nine pair-groups over four wavefronts; N = 300 leaves a partial 64-row
+    tile; out-of-range rhs and lhs give exact +0.0 rows; sorted and unsorted
+    pairs agree."""
     case = synth.gather_case(5400 + K + N + M, tokens=24, E=5, N=N, K=K, top_k=3, sort=sort,
                              with_gs=(M == 3), M=M, out_of_range=(5, 6, INT32_MAX, -1))
     case.lhs = case.lhs.copy()
     case.lhs[3] = 24           # x has 24 rows: out of range
     case.lhs[10] = -1
-    out, ref = run_gather(case, torch.bfloat16, guard=True)
-    assert oracle.relative_error(host(out), ref) <= TOL[torch.bfloat16]
+    if dtype == torch.float16:  # keep the f16 outputs finite
+        case.scales = np.minimum(case.scales, 0x50).astype(np.uint8)
+    out, ref = run_gather(case, dtype, guard=True)
+    assert oracle.relative_error(host(out), ref) <= TOL[dtype]
     assert_zero_rows(out, case.rhs, case.lhs, 5, 24)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("sort", [False, True])
-def test_gather_mfma_many_scan_rounds(sort):
+def test_gather_mfma_many_scan_rounds(sort, dtype):
     """K = 256 runs the grouped kernel with one wavefront, so its scan of rhs
     takes 64 pairs per round: R = 400 pairs over 3 experts is seven rounds,
     with an expert's pairs split across rounds when unsorted."""
     case = synth.gather_case(5500 + int(sort), tokens=200, E=3, N=80, K=256, top_k=2, sort=sort,
                              with_gs=True, M=1, out_of_range=(3, INT32_MAX))
-    out, ref = run_gather(case, torch.bfloat16, guard=True)
-    assert oracle.relative_error(host(out), ref) <= TOL[torch.bfloat16]
+    if dtype == torch.float16:  # keep the f16 outputs finite
+        case.scales = np.minimum(case.scales, 0x50).astype(np.uint8)
+    out, ref = run_gather(case, dtype, guard=True)
+    assert oracle.relative_error(host(out), ref) <= TOL[dtype]
     assert_zero_rows(out, case.rhs, case.lhs, 3, 200)
 
 
