@@ -21,6 +21,9 @@ from .nvfp4_oracle import (  # noqa: F401
     global_factor,
     qmm,
     qmm_batched,
+    quantize,
+    e2m1_round,
+    e4m3_round,
     relative_error,
     transcode,
     unpack_nibbles,

@@ -36,7 +36,11 @@ Readings where the pages are silent (each listed in the design notes):
   global scale and for the dequantized reference;
 * the contraction is carried out in float64 (stricter than the pages' f32
   reference) so the oracle's own rounding does not eat the error budget;
-* gather rows whose expert or lhs index is out of range are +0.0.
+* gather rows whose expert or lhs index is out of range are +0.0;
+* quantize takes each matrix's largest |w| as its global scale unless one is
+  given, rounds the block scale amax * 448 / gs to E4M3 and each w / d to
+  E2M1 by round-to-nearest-even in float32 (saturating at 448 and 6), and
+  keeps the sign of values that round to zero.
 
 Every function below works on numpy arrays; bf16 tensors are represented as
 their uint16 bit patterns.
@@ -175,6 +179,113 @@ def dequantize(w: np.ndarray, scales: np.ndarray, gs=None) -> np.ndarray:
 def dequantize_bf16_bits(w: np.ndarray, scales: np.ndarray, gs=None) -> np.ndarray:
     """Dequantize, then round the float32 values to bf16 (uint16 bits)."""
     return f32_to_bf16_bits(dequantize(w, scales, gs))
+
+
+# ----------------------------------------------------------------------------
+# Quantize (dense -> planes + global scale)
+# ----------------------------------------------------------------------------
+
+# Largest finite E4M3 value: the block-scale range the global scale maps the
+# matrix maximum onto (P3 "Summary": block scales are encoded as scale times
+# 448 * 6 / global_scale).
+E4M3_MAX = 448.0
+
+
+def _nearest_code(value: float, candidates) -> int:
+    """Index of the candidate nearest to value; on a tie the even index (the
+    one whose lowest mantissa bit is 0): round to nearest, ties to even."""
+    best, best_d = 0, None
+    for i, c in enumerate(candidates):
+        d = abs(value - c)
+        if best_d is None or d < best_d or (d == best_d and i % 2 == 0):
+            best, best_d = i, d
+    return best
+
+
+_E4M3_FINITE = [e4m3_value(c) for c in range(0x7F)]       # codes 0x00 .. 0x7E, increasing
+
+
+def e4m3_round(value: float) -> int:
+    """E4M3 code of a non-negative float32 value: the nearest finite E4M3
+    value, ties to the even code, above 448 saturating to 448; NaN gives the
+    NaN code 0x7F."""
+    v = float(value)
+    if v != v:
+        return 0x7F
+    if v >= E4M3_MAX:
+        return 0x7E
+    return _nearest_code(v, _E4M3_FINITE)
+
+
+def e2m1_round(value: float) -> int:
+    """E2M1 nibble of a float32 value: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4,
+    6 in magnitude, ties to the even index, above 6 saturating to 6; the sign
+    bit (nibble bit 3) is the value's sign bit, so a negative value that
+    rounds to zero gives -0."""
+    v = float(value)
+    sign = 8 if np.signbit(np.float32(v)) else 0
+    a = abs(v)
+    if a >= E2M1_MAGNITUDES[-1]:
+        return sign | 7
+    return sign | _nearest_code(a, E2M1_MAGNITUDES)
+
+
+def quantize(w: np.ndarray, gs=None):
+    """Dense float32 matrices -> (words, scale codes, global scales), quantized
+    along the last axis in blocks of 16 (P1 "Technical notes": E2M1 values,
+    one E4M3 scale per 16 elements, eight nibbles per little-endian word;
+    P3 "Summary": the block scales are encoded as scale times 448 * 6 /
+    global_scale, and dequantize multiplies by global_scale / (448 * 6)).
+
+    w is [..., rows, cols] (cols % 16 == 0); gs is None (then gs of each
+    matrix is its largest |w|) or one float32 per matrix.  In float32, per
+    16-block with largest magnitude a:
+
+    * code = E4M3 nearest (ties to even, saturating) of fl32(a * fl32(448 / gs)),
+      0 when a or gs is 0;
+    * d = fl32(e4m3(code) * fl32(gs / 2688)), the block's dequantized scale;
+    * nibble = E2M1 nearest (ties to even, saturating, signed) of fl32(w / d),
+      or just the sign of w when d is 0 or NaN.
+
+    Returns uint32 [..., rows, cols/8], uint8 [..., rows, cols/16] and
+    float32 [batch] (batch = product of the leading axes).
+    """
+    W = np.ascontiguousarray(w, dtype=np.float32)
+    if W.ndim < 2 or W.shape[-1] % GROUP_SIZE != 0:
+        raise ValueError("w must be [..., rows, cols] with cols a multiple of 16")
+    lead = W.shape[:-2]
+    rows, cols = W.shape[-2], W.shape[-1]
+    mats = W.reshape((-1, rows, cols))
+    batch = mats.shape[0]
+    if gs is None:
+        gsv = np.array([np.abs(m).max() if m.size else 0.0 for m in mats], dtype=np.float32)
+    else:
+        gsv = np.asarray(gs, dtype=np.float32).reshape(batch)
+    words = np.zeros((batch, rows, cols // NIBBLES_PER_WORD), dtype=np.uint32)
+    codes = np.zeros((batch, rows, cols // GROUP_SIZE), dtype=np.uint8)
+    for b in range(batch):
+        g_b = gsv[b]
+        t = np.float32(np.float32(E4M3_MAX) / g_b) if g_b != 0 else np.float32(0)
+        g = global_factor(g_b)
+        for r in range(rows):
+            for k in range(cols // GROUP_SIZE):
+                block = mats[b, r, k * GROUP_SIZE:(k + 1) * GROUP_SIZE]
+                a = np.float32(np.abs(block).max())
+                if a == 0 or g_b == 0:
+                    code = 0
+                else:
+                    code = e4m3_round(np.float32(a * t))
+                codes[b, r, k] = code
+                d = np.float32(np.float32(e4m3_value(code)) * g)
+                for j, v in enumerate(block):
+                    if d == 0 or d != d:
+                        nib = 8 if np.signbit(v) else 0
+                    else:
+                        nib = e2m1_round(np.float32(v / d))
+                    col = k * GROUP_SIZE + j
+                    words[b, r, col // NIBBLES_PER_WORD] |= np.uint32(nib) << np.uint32(4 * (col % NIBBLES_PER_WORD))
+    return (words.reshape(lead + (rows, cols // NIBBLES_PER_WORD)),
+            codes.reshape(lead + (rows, cols // GROUP_SIZE)), gsv)
 
 
 # ----------------------------------------------------------------------------

@@ -335,6 +335,88 @@ def test_qmm_batched_empty_batch():
 
 
 # ----------------------------------------------------------------------------
+# Quantize
+# ----------------------------------------------------------------------------
+
+def read_quantize_fixture():
+    cases = []
+    for line in open(os.path.join(GOLDEN, "quantize_rounding.txt")).read().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        gs, vals, code, nibs = [p.strip() for p in line.split("|")]
+        cases.append((np.float32(gs), np.array([float(v) for v in vals.split()], dtype=np.float32),
+                      int(code, 16), [int(n, 16) for n in nibs.split()]))
+    return cases
+
+
+def block_nibbles(words_row):
+    """The 16 nibbles of one block, element j from bits [4j, 4j+4) of word j // 8."""
+    return [(int(words_row[j // 8]) >> (4 * (j % 8))) & 0xF for j in range(16)]
+
+
+def test_quantize_rounding_fixture():
+    cases = read_quantize_fixture()
+    assert len(cases) == 6
+    for gs, vals, code, nibs in cases:
+        w, sc, g = orc.quantize(vals.reshape(1, 16), gs=[gs])
+        assert int(sc[0, 0]) == code, (gs, vals, hex(int(sc[0, 0])))
+        assert block_nibbles(w[0]) == nibs, (gs, vals, block_nibbles(w[0]))
+        assert g[0] == gs
+
+
+def test_quantize_dequantize_round_trip_is_exact():
+    """Planes whose every block holds a +-6 (so the block maximum is 6 times
+    its scale) come back unchanged, signed zeros included, through
+    dequantize -> quantize with the same global scale."""
+    g = synth.rng(26)
+    w = synth.packed_words(g, (2, 5, 8))                 # 2 matrices, 5 rows, 64 columns
+    nib = [[[(int(w[b, r, c // 8]) >> (4 * (c % 8))) & 0xF for c in range(64)] for r in range(5)]
+           for b in range(2)]
+    for b in range(2):
+        for r in range(5):
+            for blk in range(4):
+                c = blk * 16 + int(g.integers(0, 16))
+                six = 0x7 | (nib[b][r][c] & 0x8)      # +6 or -6 somewhere in each block
+                word = int(w[b, r, c // 8]) & ~(0xF << (4 * (c % 8))) | (six << (4 * (c % 8)))
+                w[b, r, c // 8] = np.uint32(word)
+    sc = synth.scale_codes(g, (2, 5, 4), synth.FINITE_POSITIVE_CODES)
+    gs = synth.global_scales(g, 2)
+    dense = np.stack([orc.dequantize(w[b], sc[b], gs[b]) for b in range(2)])
+    w2, sc2, gs2 = orc.quantize(dense, gs=gs)
+    assert np.array_equal(sc2, sc)
+    assert np.array_equal(w2, w)
+    assert np.array_equal(gs2, gs)
+
+
+def test_quantize_picks_the_nearest_value_for_its_scale():
+    """Every element's dequantized value is the closest of the 16 signed E2M1
+    multiples of its block's dequantized scale (brute force), and the default
+    global scale is the matrix's largest magnitude, which lands on code 448."""
+    g = synth.rng(27)
+    dense = (synth.activations(g, (3, 64)) * np.float32(7.5)).astype(np.float32)
+    w, sc, gs = orc.quantize(dense)
+    assert gs[0] == np.abs(dense).max()
+    assert int(sc.max()) == 0x7E
+    back = orc.dequantize(w, sc, gs[0])
+    gf = Fraction(float(orc.global_factor(gs[0])))
+    for r in range(3):
+        for c in range(64):
+            d = Fraction(float(np.float32(Fraction(float(orc.e4m3_value(int(sc[r, c // 16])))) * gf)))
+            x = Fraction(float(dense[r, c]))
+            best = min(abs(x - sgn * Fraction(m) * d) for m in orc.E2M1_MAGNITUDES for sgn in (1, -1))
+            got = abs(x - Fraction(float(back[r, c])))
+            # the dequantized value rounds fl32(e2m1 * e4m3) * g once more: allow one f32 ulp of it
+            assert got <= best + abs(Fraction(float(back[r, c]))) * Fraction(1, 2 ** 23), (r, c)
+
+
+def test_quantize_all_zero_matrix():
+    w, sc, gs = orc.quantize(np.zeros((2, 32), dtype=np.float32))
+    assert gs[0] == 0 and not sc.any() and not w.any()
+    w, sc, gs = orc.quantize(np.full((1, 16), -0.0, dtype=np.float32))
+    assert w[0, 0] == 0x88888888 and w[0, 1] == 0x88888888 and sc[0, 0] == 0
+
+
+# ----------------------------------------------------------------------------
 # Gather
 # ----------------------------------------------------------------------------
 
@@ -419,6 +501,8 @@ PIN_TESTS = [
     test_gather_rows_and_out_of_range_zeros,
     lambda: test_qmm_batched_bruteforce(False, True),
     lambda: test_qmm_batched_bruteforce(True, False),
+    test_quantize_rounding_fixture,
+    test_quantize_dequantize_round_trip_is_exact,
     test_transcode_reconstructs_source_weights,
 ]
 
@@ -488,7 +572,33 @@ def _mut_batched_gs0(x, w, scales, gs=None, transpose=True):
                      for b in range(w.shape[0])])
 
 
+def _mut_e2m1_ties_away(value):
+    v = float(value)
+    sign = 8 if np.signbit(np.float32(v)) else 0
+    a = abs(v)
+    best, best_d = 0, None
+    for i, c in enumerate(orc.E2M1_MAGNITUDES):
+        d = abs(a - c)
+        if best_d is None or d <= best_d:          # ties go up
+            best, best_d = i, d
+    return sign | best
+
+
+def _mut_e4m3_truncate(value):
+    v = float(value)
+    if v != v:
+        return 0x7F
+    best = 0
+    for c in range(0x7F):
+        if orc.e4m3_value(c) <= v:
+            best = c
+    return best
+
+
 MUTATIONS = {
+    "quantize E2M1 ties away from zero": ("e2m1_round", _mut_e2m1_ties_away),
+    "quantize E4M3 scale truncated": ("e4m3_round", _mut_e4m3_truncate),
+    "quantize scale range 6 instead of 448": ("E4M3_MAX", 6.0),
     "batched x always matrix 0": ("qmm_batched", _mut_batched_x0),
     "batched global scale of matrix 0": ("qmm_batched", _mut_batched_gs0),
     "e4m3 exponent bias 8": ("e4m3_value", _mut_e4m3_bias),
