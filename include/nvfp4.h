@@ -117,6 +117,37 @@ int nvfp4_dequantize(const uint32_t* w, const uint8_t* scales, const float* gs,
                      nvfp4_dtype_t out_dtype, void* out, hipStream_t stream);
 
 /*
+ * nvfp4_quantize -- dense matrices to packed planes and global scales
+ * (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM", "Summary":
+ * block scales are encoded as scale * 448 * 6 / global_scale, so that
+ * dequantize's global_scale / (448 * 6) restores them; mlxcel issue
+ * "perf(nvfp4): direct-transcode ModelOpt triplets to MLX native",
+ * "Technical notes": E2M1 values, one E4M3 scale per 16, eight nibbles per
+ * little-endian word).
+ *
+ *   w           [batch, rows, cols] of dtype (F32, BF16 or F16), 16-byte
+ *               aligned; quantized along cols (cols % 16 == 0)
+ *   gs_in       float [batch] or NULL: the global scale of each matrix;
+ *               NULL takes each matrix's largest |w|
+ *   w_out       uint32 [batch, rows, cols/8] (8-byte aligned)
+ *   scales_out  uint8  [batch, rows, cols/16]
+ *   gs_out      float [batch]: the global scales used (computed, or copied
+ *               from gs_in); required when gs_in is NULL, else may be NULL
+ *
+ * In float32, for each block of 16 with largest magnitude a:
+ *   code   = E4M3 nearest (ties to even) of fl32(a * fl32(448 / gs)),
+ *            saturating at 448; 0 when a or gs is 0 (NaN in the block: 0x7F)
+ *   d      = fl32(e4m3(code) * fl32(gs / 2688))
+ *   nibble = E2M1 nearest (ties to even) of fl32(w / d), saturating at 6,
+ *            carrying w's sign bit; only the sign when d is 0 or NaN.
+ * Inputs and outputs must not overlap.
+ */
+int nvfp4_quantize(const void* w, nvfp4_dtype_t dtype, int64_t batch,
+                   int64_t rows, int64_t cols, const float* gs_in,
+                   uint32_t* w_out, uint8_t* scales_out, float* gs_out,
+                   hipStream_t stream);
+
+/*
  * nvfp4_qmm -- out = x @ dequantize(w).T (transpose = 1) or
  * x @ dequantize(w) (transpose = 0) (mlxcel PR "native NVFP4 for ROCm
  * QuantizedMatmul/GatherQMM", "Summary" and "Changes during review").

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "NVFP4Error", "library_path", "load_library", "transcode", "dequantize", "qmm",
+    "NVFP4Error", "library_path", "load_library", "transcode", "dequantize", "quantize", "qmm",
     "qmm_batched", "gather_qmm", "select_route", "qmv_max_rows", "status_string",
     "ROUTE_AUTO", "ROUTE_QMV", "ROUTE_GEMM",
 ]
@@ -65,6 +65,7 @@ def load_library() -> ctypes.CDLL:
     sig = {
         "nvfp4_transcode": [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp],
         "nvfp4_dequantize": [vp, vp, vp, i64, i64, i64, c_int, vp, vp],
+        "nvfp4_quantize": [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp],
         "nvfp4_qmm": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_qmm_batched": [vp, c_int, i64, i64, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_gather_qmm": [vp, c_int, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, i64, c_int, vp, vp],
@@ -221,6 +222,32 @@ def dequantize(w: torch.Tensor, scales: torch.Tensor, gs: Optional[torch.Tensor]
     _check("nvfp4_dequantize", lib.nvfp4_dequantize(
         _ptr(w), _ptr(scales), _ptr(gs), batch, rows, cols, code, _ptr(out), _stream(dev)))
     return out
+
+
+def quantize(w: torch.Tensor, gs: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Dense [..., rows, cols] (float32, bfloat16 or float16; cols % 16 == 0)
+    -> (int32 words [..., rows, cols/8], uint8 E4M3 scales [..., rows, cols/16],
+    float32 global scales, one per matrix).  gs (float32, one per matrix) sets
+    the global scales; by default each matrix's largest |w| is used."""
+    if w.dim() < 2 or w.shape[-1] % 16 != 0:
+        raise ValueError("w must be [..., rows, cols] with cols a multiple of 16")
+    lead = tuple(w.shape[:-2])
+    rows, cols = w.shape[-2], w.shape[-1]
+    batch = 1
+    for d in lead:
+        batch *= d
+    if gs is not None and (gs.dtype != torch.float32 or gs.numel() != batch):
+        raise ValueError("gs must be float32 with one value per matrix")
+    code = _dtype_code(w.dtype)
+    dev = _require_gpu(w, gs)
+    lib = load_library()
+    w_out = torch.empty(lead + (rows, cols // 8), dtype=torch.int32, device=dev)
+    s_out = torch.empty(lead + (rows, cols // 16), dtype=torch.uint8, device=dev)
+    gs_out = torch.empty(batch, dtype=torch.float32, device=dev)
+    _check("nvfp4_quantize", lib.nvfp4_quantize(
+        _ptr(w), code, batch, rows, cols, _ptr(gs), _ptr(w_out), _ptr(s_out), _ptr(gs_out), _stream(dev)))
+    return w_out, s_out, gs_out
 
 
 def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[torch.Tensor] = None,

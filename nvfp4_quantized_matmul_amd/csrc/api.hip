@@ -173,6 +173,30 @@ int nvfp4_dequantize(const uint32_t* w, const uint8_t* scales, const float* gs, 
   return launched();
 }
 
+int nvfp4_quantize(const void* w, nvfp4_dtype_t dtype, int64_t batch, int64_t rows, int64_t cols,
+                   const float* gs_in, uint32_t* w_out, uint8_t* scales_out, float* gs_out, hipStream_t stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  int64_t elems, bytes;
+  if (!size3(batch, rows, cols, &elems) || !mul_ok(elems, dtype_size(dtype), &bytes)) return NVFP4_ERR_SHAPE;
+  if (batch == 0) return NVFP4_OK;
+  if (!gs_in && !gs_out) return NVFP4_ERR_NULLPTR;
+  if ((gs_in && !aligned(gs_in, 4)) || (gs_out && !aligned(gs_out, 4))) return NVFP4_ERR_ALIGN;
+  if (elems > 0) {
+    if (!w || !w_out || !scales_out) return NVFP4_ERR_NULLPTR;
+    if (!aligned(w, 16) || !aligned(w_out, 8)) return NVFP4_ERR_ALIGN;
+    if (overlaps(w, bytes, w_out, elems / 2) || overlaps(w, bytes, scales_out, elems / 16) ||
+        overlaps(w_out, elems / 2, scales_out, elems / 16))
+      return NVFP4_ERR_SHAPE;
+    if (gs_out && (overlaps(gs_out, batch * 4, w, bytes) || overlaps(gs_out, batch * 4, w_out, elems / 2) ||
+                   overlaps(gs_out, batch * 4, scales_out, elems / 16)))
+      return NVFP4_ERR_SHAPE;
+  }
+  if (gs_in && gs_out && gs_in != gs_out && overlaps(gs_in, batch * 4, gs_out, batch * 4)) return NVFP4_ERR_SHAPE;
+  nvfp4host::launch_quantize(w, dtype, batch, rows, cols, gs_in, w_out, scales_out, gs_out, stream);
+  return launched();
+}
+
 int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N,
               const uint32_t* w, const uint8_t* scales, const float* gs, int transpose,
               nvfp4_route_t route, void* out, hipStream_t stream) {

@@ -20,6 +20,11 @@ void launch_sidecar(const float* ws2, float* gs_out, int64_t batch, hipStream_t 
 // Dequantize [batch*rows, cols/8] words into out of dtype.
 void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, int64_t batch,
                        int64_t rows, int64_t cols, nvfp4_dtype_t dt, void* out, hipStream_t s);
+// Quantize [batch, rows, cols] dense values (cols % 16 == 0) into words,
+// scale codes and (when gs_in is NULL) per-matrix global scales in gs_out;
+// with gs_in, gs_out (if not NULL) receives a copy of it.
+void launch_quantize(const void* w, nvfp4_dtype_t dt, int64_t batch, int64_t rows, int64_t cols,
+                     const float* gs_in, uint32_t* w_out, uint8_t* sc_out, float* gs_out, hipStream_t s);
 // Decode kernel (M = 1): returns false, launching nothing, when K is not
 // a multiple of 32, K > 8192 or the weight plane reaches 2^31 bytes.
 bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const uint32_t* w,

@@ -37,7 +37,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_qmm", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
+    for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_batched",
+                 "nvfp4_gather_qmm",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
         assert want in names
 
@@ -140,6 +141,27 @@ def test_gather_validation(lib):
     assert gather(lib, lhs=P(0x100002)) == ALIGN
     assert gather(lib, x=MISALIGNED) == ALIGN
     assert gather(lib, R=0, x=None, rhs=None, w=None, s=None, out=None) == OK
+
+
+def quant(lib, w=FAKE, dt=F32, batch=2, rows=4, cols=32, gs_in=None, w_out=P(0x200000), s_out=P(0x300000),
+          gs_out=P(0x400000)):
+    return lib.nvfp4_quantize(w, dt, batch, rows, cols, gs_in, w_out, s_out, gs_out, None)
+
+
+def test_quantize_validation(lib):
+    assert quant(lib, w=None) == NULLPTR
+    assert quant(lib, w_out=None) == NULLPTR
+    assert quant(lib, s_out=None) == NULLPTR
+    assert quant(lib, gs_out=None) == NULLPTR            # no gs_in: gs_out is where gs goes
+    assert quant(lib, cols=24) == SHAPE
+    assert quant(lib, rows=-1) == SHAPE
+    assert quant(lib, dt=7) == DTYPE
+    assert quant(lib, w=MISALIGNED) == ALIGN
+    assert quant(lib, w_out=P(0x200004)) == ALIGN
+    assert quant(lib, gs_out=P(0x400002)) == ALIGN
+    assert quant(lib, batch=1 << 40, rows=1 << 20, cols=1 << 20) == SHAPE
+    assert quant(lib, w_out=FAKE) == SHAPE                # output overlapping the input
+    assert quant(lib, batch=0, w=None, w_out=None, s_out=None, gs_out=None) == OK
 
 
 def test_dequantize_and_transcode_validation(lib):

@@ -160,6 +160,89 @@ def test_dequantize_decode_row_length_bit_exact():
 
 
 # ----------------------------------------------------------------------------
+# quantize
+# ----------------------------------------------------------------------------
+
+def dense_weights(seed, shape, lo=-20, hi=4):
+    """N(0,1) rows scaled by 2^k, k uniform in [lo, hi], so block scales span
+    zero, subnormal and large E4M3 codes within one matrix."""
+    g = synth.rng(seed)
+    base = synth.activations(g, shape)
+    k = g.integers(lo, hi + 1, size=shape[:-1] + (1,))
+    return (base * np.exp2(k)).astype(np.float32), g
+
+
+def quantize_both(dense, dtype, gs=None):
+    x_t, x_ref = activations(dense, dtype)
+    lead = dense.shape[:-2]
+    want_w, want_s, want_g = oracle.quantize(x_ref, gs)
+    w, s, g = nv.quantize(x_t, None if gs is None else f32(np.asarray(gs, dtype=np.float32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), want_s)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), want_w)
+    same_f32(g.cpu().numpy(), want_g)
+    return w, s, g
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", [(1, 16), (37, 48), (3, 5, 256), (8, 5376)])
+@pytest.mark.parametrize("given_gs", [False, True])
+def test_quantize_bit_exact(dtype, shape, given_gs):
+    """Codes, words and global scales equal the oracle's bit for bit, for
+    float32, bf16 and f16 inputs, one or several matrices, computed or given
+    global scales (given ones below the matrix maximum saturate at 448)."""
+    dense, g = dense_weights(3800 + sum(shape), shape)
+    batch = int(np.prod(shape[:-2])) if len(shape) > 2 else 1
+    gs = synth.global_scales(g, batch, lo=0.5, hi=20.0) if given_gs else None
+    quantize_both(dense, dtype, gs)
+
+
+def test_quantize_special_values():
+    """Zeros and -0, a NaN, an infinity, values at E2M1 and E4M3 ties."""
+    dense = np.zeros((6, 32), dtype=np.float32)
+    dense[0, 3] = -0.0
+    dense[1, :16] = [6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -0.25, -0.75, -5, -6, 0.3, 5.5, 0, -0.0]
+    dense[2, 5] = np.nan
+    dense[2, 20] = 1.5
+    dense[3, 17] = np.inf
+    dense[3, 18] = -2.0
+    dense[4, :16] = np.float32(1.0625)
+    dense[5, 16] = np.float32(0.0048828125)
+    dense[5, 0] = np.float32(0.0009765625)
+    quantize_both(dense, torch.float32, gs=[2688.0])
+    quantize_both(dense[4:], torch.float32, gs=[448.0])
+    quantize_both(dense, torch.float32)                 # gs = NaN (the matrix holds one)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_round_trip_through_the_library(dtype):
+    """Planes whose blocks each hold a +-6 come back unchanged through the
+    library's dequantize and quantize (with the same global scale)."""
+    g = synth.rng(3900)
+    nib = g.integers(0, 16, size=(64, 512)).astype(np.uint32)
+    pos = g.integers(0, 16, size=(64, 32))
+    for r in range(64):
+        for b in range(32):
+            c = 16 * b + pos[r, b]
+            nib[r, c] = 0x7 | (nib[r, c] & 0x8)
+    shifts = (np.arange(8, dtype=np.uint32) * 4)
+    words_np = (nib.reshape(64, 64, 8) << shifts).sum(axis=-1, dtype=np.uint64).astype(np.uint32)
+    sc = synth.scale_codes(g, (64, 32), synth.NORMAL_POSITIVE_CODES)
+    gs = synth.global_scales(g, 1, lo=0.5, hi=20.0)
+    dense = nv.dequantize(words(words_np), u8(sc), f32(gs), dtype=dtype)
+    w2, s2, g2 = nv.quantize(dense, f32(gs))
+    torch.cuda.synchronize()
+    if dtype == torch.float32:
+        assert np.array_equal(w2.cpu().numpy().view(np.uint32), words_np)
+        assert np.array_equal(s2.cpu().numpy(), sc)
+    else:
+        # bf16 rounds the dequantized values; the library must still match the oracle
+        want_w, want_s, _ = oracle.quantize(dense.float().cpu().numpy(), gs)
+        assert np.array_equal(w2.cpu().numpy().view(np.uint32), want_w)
+        assert np.array_equal(s2.cpu().numpy(), want_s)
+
+
+# ----------------------------------------------------------------------------
 # qmm
 # ----------------------------------------------------------------------------
 
