@@ -12,7 +12,9 @@ reported beside it.
 
 Also reported, each against its roofline: the prefill GEMM (M=2048,
 TFLOP/s), the multi-row qmv (M=16) and the MoE gather (sorted prefill and
-unsorted decode, GB/s).  Kernel durations come from HIP events around back-to-back
+unsorted decode, GB/s); under ``other_configs`` the tiny qmv's latency,
+multi-row qmv at every M in f32 and bf16, MoE unsorted decode at B = 1..8,
+batched-weight qmm and the load-time transcode / dequantize / quantize.  Kernel durations come from HIP events around back-to-back
 launches on the launch stream.  The CPU oracle is timed on the host
 on the full decode workload (cpu_baseline).
 
@@ -290,6 +292,100 @@ def traffic_for(kernel_key: str):
         return None
 
 
+def timed_us(fn, n: int, warmup: int = 3) -> float:
+    """Microseconds per call of fn(i) over n back-to-back calls through the
+    Python binding, between events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def other_configs():
+    """The remaining configurations, each as microseconds per call and the
+    rate against its roofline: the tiny qmv (latency), multi-row qmv at every
+    M in f32 and bf16, MoE unsorted decode at B = 1, 2, 4, 8, batched-weight
+    qmm, and the load-time transcode, dequantize and quantize."""
+    out = {}
+    lib = nv.load_library()
+    # tiny qmv: M=1, K=1024, N=512, f32, no global scale (launch-latency bound)
+    wl = synth.WORKLOADS["tiny_qmv_m1_k1024_n512_f32"]
+    c = synth.dense_case(wl["seed"], 1, 1024, 512, with_gs=False, code_range=wl["codes"])
+    x = torch.from_numpy(c.x).to(DEV)
+    w, s = words_dev(c.w), u8_dev(c.scales)
+    y = torch.empty((1, 512), dtype=torch.float32, device=DEV)
+    us = timed_us(lambda i: nv.qmm(x, w, s, out=y), 200, warmup=20)
+    out["tiny_qmv_m1_k1024_n512_f32"] = {"us": round(us, 3), "bytes": 301056,
+                                         "note": "fits in L2; latency, not bandwidth, bounds it"}
+    # multi-row: one plane, 16 copies (530 MB), every M and dtype
+    wl = synth.WORKLOADS["multirow_qmv_k4096_n14336"]
+    c = synth.dense_case(wl["seed"], 33, 4096, 14336, with_gs=True)
+    w0, s0 = words_dev(c.w), u8_dev(c.scales)
+    ws = [w0] + [w0.clone() for _ in range(15)]
+    ss = [s0] + [s0.clone() for _ in range(15)]
+    gs = torch.from_numpy(c.gs).to(DEV)
+    rows = []
+    for dt, name, size in ((torch.bfloat16, "bf16", 2), (torch.float32, "f32", 4)):
+        for M in wl["Ms"]:
+            xm = torch.from_numpy(c.x[:M]).to(dt).to(DEV)
+            ym = torch.empty((M, 14336), dtype=dt, device=DEV)
+            us = timed_us(lambda i: nv.qmm(xm, ws[i % 16], ss[i % 16], gs, out=ym), 64)
+            nbytes = c.w.nbytes + c.scales.nbytes + 4 + M * 4096 * size + M * 14336 * size
+            rows.append({"M": M, "dtype": name, "us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
+                         "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "route": nv.select_route(M, 4096, 14336, dtype=dt)})
+    out["multirow_qmv_k4096_n14336"] = rows
+    del ws, ss
+    # batched weights: two matrices of the multi-row shape at M = 3 (qmv) and 64
+    bc = synth.batched_case(3600, B=2, M=64, K=4096, N=14336)
+    bw, bs, bg = words_dev(bc.w), u8_dev(bc.scales), torch.from_numpy(bc.gs).to(DEV)
+    brow = []
+    for M in (3, 64):
+        xb = torch.from_numpy(np.ascontiguousarray(bc.x[:, :M])).to(torch.bfloat16).to(DEV)
+        yb = torch.empty((2, M, 14336), dtype=torch.bfloat16, device=DEV)
+        us = timed_us(lambda i: nv.qmm_batched(xb, bw, bs, bg, out=yb), 32)
+        nbytes = bc.w.nbytes + bc.scales.nbytes + 8 + xb.numel() * 2 + yb.numel() * 2
+        brow.append({"B": 2, "M": M, "dtype": "bf16", "us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
+                     "note": "planes fit the MALL (cache-warm)"})
+    out["batched_qmm_b2_k4096_n14336"] = brow
+    # MoE unsorted decode at B = 1, 2, 4, 8
+    mrow = []
+    for B in synth.WORKLOADS["moe_gather_e128_n1536_k2048_top8"]["decode_tokens"]:
+        g = Gather(B, False, copies=3, seed_off=B)
+        us = eager_launch_us(g, 96)["mean_us"]
+        mrow.append({"B": B, "distinct_experts": g.distinct, "us": round(us, 3),
+                     "GB_s": round(g.bytes / us / 1e3, 1), "frac_hbm": round(g.bytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del g
+    out["moe_unsorted_decode"] = mrow
+    # load time at the decode plane's shape [21504, 5376]: transcode (byte move
+    # of both planes), dequantize to bf16, quantize from bf16
+    gq = synth.rng(6000)
+    wu8, wsc, ws2 = synth.modelopt_triplet(gq, 1, 21504, 5376, with_ws2=True)
+    tw, tsc, tws2 = torch.from_numpy(wu8[0]).to(DEV), torch.from_numpy(wsc[0]).to(DEV), torch.from_numpy(ws2).to(DEV)
+    plane_bytes = wu8[0].nbytes + wsc[0].nbytes
+    us = timed_us(lambda i: nv.transcode(tw, tsc, tws2), 16)
+    load = {"transcode": {"us": round(us, 2), "GB_s": round(2 * plane_bytes / us / 1e3, 1),
+                          "bytes": 2 * plane_bytes}}
+    pw, ps, pg = nv.transcode(tw, tsc, tws2)
+    us = timed_us(lambda i: nv.dequantize(pw, ps, pg, dtype=torch.bfloat16), 16)
+    dq_bytes = plane_bytes + 21504 * 5376 * 2
+    load["dequantize_bf16"] = {"us": round(us, 2), "GB_s": round(dq_bytes / us / 1e3, 1), "bytes": dq_bytes}
+    dense = nv.dequantize(pw, ps, pg, dtype=torch.bfloat16)
+    us = timed_us(lambda i: nv.quantize(dense), 16)
+    q_bytes = 2 * 21504 * 5376 * 2 + plane_bytes
+    load["quantize_bf16"] = {"us": round(us, 2), "GB_s": round(q_bytes / us / 1e3, 1), "bytes": q_bytes,
+                             "note": "two passes over the dense input (matrix maximum, then blocks)"}
+    out["load_time_21504x5376"] = load
+    return out
+
+
 def cpu_baseline(decode_bytes: float):
     """The oracle, untuned, on the host: one full decode workload."""
     import oracle
@@ -399,6 +495,9 @@ def main():
     udur = eager_launch_us(gs_dec, 96)
     ugbs = gs_dec.bytes / (udur["mean_us"] * 1e-6) / 1e9
 
+    log("other configurations")
+    others = other_configs()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -446,6 +545,7 @@ def main():
                                    "distinct_experts": gs_dec.distinct,
                                    "kernel": "gather_kernel<bf16,4,4,1>", "kernel_duration": udur,
                                    "bytes": gs_dec.bytes},
+        "other_configs": others,
         "kernel_source_sha": kernel_source_sha(),
     }
     print(json.dumps(line), flush=True)

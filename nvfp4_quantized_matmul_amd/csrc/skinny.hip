@@ -477,13 +477,17 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
       launch_rows16(static_cast<const _Float16*>(x), M, K, N, w, sc, gs, static_cast<_Float16*>(out), s);
       break;
     case NVFP4_F32: {
-      // float32 activations hold twice the registers: up to 32 rows per launch
+      // float32 activations (three bf16 parts) hold more registers per row
+      // fragment: 179 / 280 / 380 / 460 for one to four fragments, all one
+      // wavefront per SIMD without spills, so every M <= 64 is one launch
+      // and the weight plane is read once.
       const float* xf = static_cast<const float*>(x);
       float* of = static_cast<float*>(out);
-      for (int64_t m0 = 0; m0 < M; m0 += 32) {
-        const int64_t rows = M - m0 < 32 ? M - m0 : 32;
-        if (rows <= 16) launch_mf<float, 1, 8>(xf + m0 * K, rows, K, N, w, sc, gs, of + m0 * N, s);
-        else launch_mf<float, 2, 4>(xf + m0 * K, rows, K, N, w, sc, gs, of + m0 * N, s);
+      switch ((M + 15) / 16) {
+        case 1: launch_mf<float, 1, 8>(xf, M, K, N, w, sc, gs, of, s); break;
+        case 2: launch_mf<float, 2, 4>(xf, M, K, N, w, sc, gs, of, s); break;
+        case 3: launch_mf<float, 3, 4>(xf, M, K, N, w, sc, gs, of, s); break;
+        default: launch_mf<float, 4, 4>(xf, M, K, N, w, sc, gs, of, s); break;
       }
       break;
     }
