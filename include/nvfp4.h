@@ -172,6 +172,30 @@ int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
               hipStream_t stream);
 
 /*
+ * nvfp4_qmm_ws -- nvfp4_qmm with a caller-owned workspace (device, 16-byte
+ * aligned, not overlapping x or out).  When the GEMM route has few output
+ * tiles for the device (small M, e.g. a prefill chunk of a few hundred rows),
+ * the contraction over K is split among several blocks per tile, their
+ * float32 partials are kept in the workspace and added in a fixed order by a
+ * second kernel, which applies g and rounds; this needs at least
+ * nvfp4_qmm_workspace_size() bytes.  With less (or NULL, 0) it is nvfp4_qmm.
+ * Results equal nvfp4_qmm's up to float32 summation order.
+ */
+int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
+                 int64_t N, const uint32_t* w, const uint8_t* scales,
+                 const float* gs, int transpose, nvfp4_route_t route,
+                 void* workspace, int64_t workspace_bytes, void* out,
+                 hipStream_t stream);
+
+/*
+ * nvfp4_qmm_workspace_size -- bytes of workspace nvfp4_qmm_ws uses for this
+ * call on the current device (0: it would not split), or a negative status
+ * for an invalid request.  Host only.
+ */
+int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
+                                 nvfp4_dtype_t dtype, nvfp4_route_t route);
+
+/*
  * nvfp4_qmm_batched -- nvfp4_qmm over a batch of weight matrices (mlxcel PR
  * "native NVFP4 for ROCm QuantizedMatmul/GatherQMM", "Numerical results":
  * qmm with batched weights, on the qmv route at M = 3 and the GEMM route at

@@ -68,6 +68,8 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_quantize": [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp],
         "nvfp4_qmm": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_qmm_batched": [vp, c_int, i64, i64, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
+        "nvfp4_qmm_ws": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, i64, vp, vp],
+        "nvfp4_qmm_workspace_size": [i64, i64, i64, c_int, c_int, c_int],
         "nvfp4_gather_qmm": [vp, c_int, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, i64, c_int, vp, vp],
         "nvfp4_select_route": [i64, i64, i64, c_int, c_int],
         "nvfp4_qmv_max_rows": [],
@@ -79,6 +81,7 @@ def load_library() -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = c_int
     lib.nvfp4_qmv_max_rows.restype = i64
+    lib.nvfp4_qmm_workspace_size.restype = i64
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -255,6 +258,9 @@ def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[tor
         ) -> torch.Tensor:
     """out = x @ dequantize(w).T (transpose) or x @ dequantize(w).
 
+    When the GEMM route would leave most compute units idle (few output tiles)
+    the call goes through nvfp4_qmm_ws with a workspace from torch's allocator.
+
     x [..., K] (float32, bfloat16 or float16); w [N, K/8] (transpose) or
     [K, N/8]; scales as for check_planes; gs float32 with one element or None.
     The output has x's dtype and shape [..., N].
@@ -283,8 +289,20 @@ def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[tor
     elif out.dtype != x.dtype or tuple(out.shape) != tuple(x.shape[:-1]) + (N,):
         raise ValueError("out has the wrong dtype or shape")
     _require_gpu(out)
+    tr = int(bool(transpose))
+    ws_bytes = int(lib.nvfp4_qmm_workspace_size(M, K, N, tr, code, _ROUTES[route]))
+    if ws_bytes < 0:
+        raise NVFP4Error("nvfp4_qmm_workspace_size", ws_bytes)
+    if ws_bytes > 0:
+        # split GEMM for few output tiles: the partials live in a workspace
+        # from torch's allocator (the library itself never allocates)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        _check("nvfp4_qmm_ws", lib.nvfp4_qmm_ws(
+            _ptr(x), code, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), tr, _ROUTES[route],
+            _ptr(ws), ws_bytes, _ptr(out), _stream(dev)))
+        return out
     _check("nvfp4_qmm", lib.nvfp4_qmm(
-        _ptr(x), code, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), int(bool(transpose)),
+        _ptr(x), code, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), tr,
         _ROUTES[route], _ptr(out), _stream(dev)))
     return out
 

@@ -87,12 +87,14 @@ int qmm_plan(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N
 // Enqueues what qmm_plan decided (arguments already checked).
 void qmm_launch(const QmmPlan& plan, const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N,
                 const uint32_t* w, const uint8_t* scales, const float* gs, int transpose, void* out,
-                hipStream_t stream) {
+                hipStream_t stream, void* ws = nullptr, int64_t ws_bytes = 0) {
   switch (plan.kind) {
     case QmmPlan::kNothing: break;
     case QmmPlan::kZeroFill: nvfp4host::launch_fill_zero(out, M * N * dtype_size(dtype), stream); break;
     case QmmPlan::kQmv: nvfp4host::launch_qmv(x, dtype, M, K, N, w, scales, gs, out, stream); break;
-    case QmmPlan::kGemmMfma: nvfp4host::launch_gemm_mfma(x, M, K, N, w, scales, gs, out, stream); break;
+    case QmmPlan::kGemmMfma:
+      nvfp4host::launch_gemm_mfma(x, M, K, N, w, scales, gs, out, stream, ws, ws_bytes);
+      break;
     case QmmPlan::kGemmGeneric:
       nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
       break;
@@ -205,6 +207,38 @@ int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t 
   if (st != NVFP4_OK) return st;
   if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
   qmm_launch(plan, x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
+  return launched();
+}
+
+int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose, nvfp4_dtype_t dtype,
+                                 nvfp4_route_t route) {
+  const int auto_route = nvfp4_select_route(M, K, N, transpose, dtype);
+  if (auto_route < 0) return auto_route;
+  if (route != NVFP4_ROUTE_AUTO && route != NVFP4_ROUTE_QMV && route != NVFP4_ROUTE_GEMM) return NVFP4_ERR_ROUTE;
+  int64_t t;
+  if (!mul_ok(M, K, &t) || !mul_ok(M, N, &t) || !mul_ok(K, N, &t)) return NVFP4_ERR_SHAPE;
+  const int r = route == NVFP4_ROUTE_AUTO ? auto_route : (int)route;
+  if (r != NVFP4_ROUTE_GEMM || dtype != NVFP4_BF16 || !transpose || K % 32 != 0 || M == 0 || N == 0) return 0;
+  return nvfp4host::gemm_workspace_bytes(M, K, N);
+}
+
+int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                 const uint8_t* scales, const float* gs, int transpose, nvfp4_route_t route, void* workspace,
+                 int64_t workspace_bytes, void* out, hipStream_t stream) {
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return NVFP4_ERR_SHAPE;
+  if (workspace && !aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  QmmPlan plan;
+  const int st = qmm_plan(x, dtype, M, K, N, w, scales, gs, transpose, route, out, &plan);
+  if (st != NVFP4_OK) return st;
+  if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
+  if (workspace && plan.kind == QmmPlan::kGemmMfma) {
+    int64_t mn;
+    const int64_t osz = dtype_size(dtype);
+    if (mul_ok(M, N, &mn) && (overlaps(workspace, workspace_bytes, out, mn * osz) ||
+                              overlaps(workspace, workspace_bytes, x, M * K * osz)))
+      return NVFP4_ERR_SHAPE;
+  }
+  qmm_launch(plan, x, dtype, M, K, N, w, scales, gs, transpose, out, stream, workspace, workspace_bytes);
   return launched();
 }
 

@@ -15,6 +15,8 @@
 //  * gemm_generic_kernel: a float32 FMA tiled GEMM used for float32/f16
 //    activations and for non-transposed planes (quantized along N, any K),
 //    with both tiles decoded to float32 in LDS.
+#include <atomic>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.hpp"
 
@@ -299,10 +301,14 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
   }
 }
 
+// kSplit: the block multiplies slabs [split * per_split, ...) of its tile
+// only and writes the unscaled float32 partial to ws[split][M][N]; a second
+// kernel adds the partials in split order, applies g and rounds.
+template <bool kSplit>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     const __bf16* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
     const float* __restrict__ gs, __bf16* __restrict__ out, int64_t M, int64_t K, int64_t N,
-    int64_t tiles_m, int64_t tiles_total) {
+    int64_t tiles_m, int64_t tiles_total, int64_t per_split, float* __restrict__ ws) {
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
   __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2];
   __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN];
@@ -311,18 +317,25 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
   // each XCD gets a contiguous run of logical tiles (activation tiles
   // fastest), so the tiles sharing weight rows share that XCD's L2.
+  // With a split, logical = split * tiles_total + tile: an XCD's run holds
+  // neighbouring tiles of one split.
   const int64_t per_xcd = (int64_t)gridDim.x / 8;
   const int64_t logical = ((int64_t)blockIdx.x % 8) * per_xcd + (int64_t)blockIdx.x / 8;
-  if (logical >= tiles_total) return;  // whole block, before any barrier
-  const int64_t m_blk = (logical % tiles_m) * kV3BM;
-  const int64_t n_blk = (logical / tiles_m) * kV3BN;
+  const int64_t all_slabs = K / kV3BK;
+  const int64_t split = kSplit ? logical / tiles_total : 0;
+  const int64_t tile = kSplit ? logical - split * tiles_total : logical;
+  const int64_t first_slab = split * per_split;
+  if (tile >= tiles_total || first_slab >= all_slabs) return;  // whole block, before any barrier
+  const int64_t m_blk = (tile % tiles_m) * kV3BM;
+  const int64_t n_blk = (tile / tiles_m) * kV3BN;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int64_t kw = K / 8, ks = K / 16;
-  const int64_t nslabs = K / kV3BK;
+  const int64_t nslabs = kSplit ? (all_slabs - first_slab < per_split ? all_slabs - first_slab : per_split)
+                                : all_slabs;
 
   // Source addresses of this lane's loads for slab 0.  Rows past M or N
   // re-read the last row (their results are never stored).
@@ -347,6 +360,13 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     int64_t n = n_blk + wave * 64 + lane;
     if (n >= N) n = N - 1;
     src.s = sc + n * ks;
+  }
+  if (kSplit) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) src.x[i] += first_slab * kV3BK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) src.w[i] += first_slab * 8;
+    src.s += first_slab * 4;
   }
 
   f32x16_t acc[2][8];
@@ -383,6 +403,34 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   wait_vmem(false);   // no load-to-LDS may land after the block ends
 #undef NVFP4_V3_STEP
 
+  if constexpr (kSplit) {
+    // Partial: fragment (a, b) holds C[n][m] with n = 8*jj + 4h + i, m =
+    // l32; four consecutive n per jj go out as one 16-byte store.
+    float* wsp = ws + split * M * N;
+    const bool vec4 = (N % 4) == 0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int64_t m = m_blk + b * 32 + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int64_t n = n_blk + wave * 64 + a * 32 + jj * 8 + h * 4;
+          float* p = wsp + m * N + n;
+          if (vec4 && n + 3 < N) {
+            *reinterpret_cast<float4*>(p) =
+                make_float4(acc[a][b][jj * 4], acc[a][b][jj * 4 + 1], acc[a][b][jj * 4 + 2], acc[a][b][jj * 4 + 3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (n + i < N) p[i] = acc[a][b][jj * 4 + i];
+          }
+        }
+      }
+    }
+    return;
+  }
   // Epilogue: fragment (a, b) holds C[n][m] with n = 8*jj + 4h + i, m = l32.
   // A swap between the lane halves gives lane h the eight consecutive n
   // 16p + 8h .. 16p + 8h + 7 of jj pair p, stored as one 16-byte write.
@@ -419,6 +467,31 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
           for (int i = 0; i < 8; ++i)
             if (n + i < N) q[i] = __builtin_bit_cast(__bf16, (uint16_t)(wv[i / 2] >> (16 * (i % 2))));
         }
+      }
+    }
+  }
+}
+
+// out = round(g * sum over splits of ws[split]), splits added in order.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws, int64_t splits,
+                                                           int64_t MN, const float* __restrict__ gs,
+                                                           __bf16* __restrict__ out) {
+  const float g = global_factor(gs, 0);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < MN; e += stride * 4) {
+    if (e + 3 < MN) {
+      float4 v = *reinterpret_cast<const float4*>(ws + e);
+      for (int64_t sp = 1; sp < splits; ++sp) {
+        const float4 u = *reinterpret_cast<const float4*>(ws + sp * MN + e);
+        v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+      }
+      const __bf16 o[4] = {(__bf16)(v.x * g), (__bf16)(v.y * g), (__bf16)(v.z * g), (__bf16)(v.w * g)};
+      *reinterpret_cast<uint2*>(out + e) = __builtin_bit_cast(uint2, o);
+    } else {
+      for (int64_t i = e; i < MN; ++i) {
+        float v = ws[i];
+        for (int64_t sp = 1; sp < splits; ++sp) v += ws[sp * MN + i];
+        out[i] = (__bf16)(v * g);
       }
     }
   }
@@ -527,18 +600,75 @@ void generic_dispatch(const TX* x, int64_t M, int64_t K, int64_t N, const uint32
     gemm_generic_kernel<TX, false><<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(x, w, sc, gs, out, M, K, N);
 }
 
+// Compute units of the current device (cached per device; 256 if the
+// runtime cannot say).
+int64_t device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
 
 namespace nvfp4host {
 
+// Splits of K for the MFMA GEMM: with few tiles most compute units would
+// idle, so the slabs of each tile are shared among `splits` blocks and their
+// float32 partials added afterwards.  Model: rounds of blocks times the
+// per-block time (slab time plus a fixed start-up and epilogue cost), plus
+// the partials' traffic; returns 1 when splitting does not pay.
+int64_t gemm_splits(int64_t M, int64_t K, int64_t N) {
+  if (K % kV3BK != 0) return 1;
+  const int64_t tiles = ((M + kV3BM - 1) / kV3BM) * ((N + kV3BN - 1) / kV3BN);
+  const int64_t nslabs = K / kV3BK;
+  const int64_t cus = device_cu_count();
+  const double slab_us = 1.4, block_us = 20.0, bytes_per_us = 4.0e6;
+  int64_t best = 1;
+  double best_t = 0.0;
+  for (int64_t sp = 1; sp <= 8 && sp <= nslabs / 4; ++sp) {
+    const int64_t per = (nslabs + sp - 1) / sp;
+    const double rounds = (double)((tiles * sp + cus - 1) / cus);
+    double t = rounds * (per * slab_us + block_us);
+    if (sp > 1) t += (double)(sp * 4 + 2) * (double)M * (double)N / bytes_per_us;
+    if (sp == 1 || t < best_t) {
+      best = sp;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
-                      const uint8_t* sc, const float* gs, void* out, hipStream_t s) {
+                      const uint8_t* sc, const float* gs, void* out, hipStream_t s, void* ws,
+                      int64_t ws_bytes) {
   if (K % kV3BK == 0 && (reinterpret_cast<uintptr_t>(sc) & 3) == 0) {
     const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
     const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
+    const int64_t sp = ws ? gemm_splits(M, K, N) : 1;
+    if (sp > 1 && ws_bytes >= sp * M * N * 4 && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
+      const int64_t nslabs = K / kV3BK;
+      const int64_t per = (nslabs + sp - 1) / sp;
+      const int64_t grid = (tiles * sp + 7) / 8 * 8;
+      gemm_mfma_v3_kernel<true><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+          static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, per,
+          static_cast<float*>(ws));
+      const int64_t MN = M * N;
+      int64_t rgrid = (MN / 4 + 255) / 256;
+      if (rgrid > 4096) rgrid = 4096;
+      if (rgrid < 1) rgrid = 1;
+      split_reduce_kernel<<<dim3((unsigned)rgrid), dim3(256), 0, s>>>(static_cast<const float*>(ws), sp, MN, gs,
+                                                                     static_cast<__bf16*>(out));
+      return;
+    }
     const int64_t grid = (tiles + 7) / 8 * 8;
-    gemm_mfma_v3_kernel<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-        static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
+    gemm_mfma_v3_kernel<false><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+        static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, 0, nullptr);
     return;
   }
   const int64_t tiles_m = (M + kBM - 1) / kBM;
@@ -547,6 +677,11 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
   const int64_t grid = (tiles + 7) / 8 * 8;
   gemm_mfma_kernel<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
       static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
+}
+
+int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  const int64_t sp = gemm_splits(M, K, N);
+  return sp > 1 ? sp * M * N * 4 : 0;
 }
 
 void launch_gemm_generic(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,

@@ -44,9 +44,17 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
 bool launch_gather_mfma(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t M, int64_t K, const int32_t* lhs,
                         const int32_t* rhs, int64_t R, const uint32_t* w, const uint8_t* sc,
                         const float* gs, int64_t E, int64_t N, void* out, hipStream_t s);
-// MFMA GEMM, bf16 activations, transposed plane.
+// MFMA GEMM, bf16 activations, transposed plane.  With a workspace of at
+// least gemm_workspace_bytes(M, K, N) bytes (16-byte aligned) the slabs of K
+// are split among several blocks per tile when that pays (few tiles), and
+// the float32 partials added by a second kernel; otherwise one block per
+// tile.
 void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
-                      const uint8_t* sc, const float* gs, void* out, hipStream_t s);
+                      const uint8_t* sc, const float* gs, void* out, hipStream_t s, void* ws = nullptr,
+                      int64_t ws_bytes = 0);
+// Workspace the split GEMM wants for this shape on the current device (0:
+// no split).
+int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 // Generic float32-accumulating GEMM for any dtype and either plane layout.
 void launch_gemm_generic(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
                          const uint32_t* w, const uint8_t* sc, const float* gs, int transpose,

@@ -37,8 +37,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_batched",
-                 "nvfp4_gather_qmm",
+    for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_ws",
+                 "nvfp4_qmm_workspace_size", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
         assert want in names
 
@@ -97,6 +97,26 @@ def test_qmm_validation(lib):
     # empty outputs launch nothing and succeed, even with NULL buffers
     assert qmm(lib, M=0, x=None, w=None, s=None, out=None) == OK
     assert qmm(lib, N=0, x=None, w=None, s=None, out=None) == OK
+
+
+def test_qmm_workspace_size_and_validation(lib):
+    ws = lib.nvfp4_qmm_workspace_size
+    ws.restype = ctypes.c_int64
+    # few output tiles on the GEMM route: a split workspace of splits * M * N floats
+    small = ws(128, 5376, 21504, 1, BF16, 0)
+    assert small > 0 and small % (128 * 21504 * 4) == 0
+    assert ws(2048, 5376, 21504, 1, BF16, 0) == 0            # enough tiles: no split
+    assert ws(16, 5376, 21504, 1, BF16, 0) == 0              # qmv route
+    assert ws(128, 5376, 21504, 1, F32, 0) == 0              # generic GEMM: no split
+    assert ws(128, 5376, 21504, 1, BF16, 1) == 0             # forced qmv
+    assert ws(128, 24, 64, 1, BF16, 0) == SHAPE
+    qws = lib.nvfp4_qmm_ws
+    args = lambda **k: (k.get("x", FAKE), BF16, 4, 64, 32, FAKE, FAKE, None, 1, 0,
+                        k.get("ws", FAKE), k.get("nb", 1024), k.get("out", FAKE), None)
+    assert qws(*args(nb=-1)) == SHAPE
+    assert qws(*args(ws=None, nb=16)) == SHAPE
+    assert qws(*args(ws=MISALIGNED)) == ALIGN
+    assert qws(*args(x=None)) == NULLPTR
 
 
 def qmm_b(lib, x=FAKE, dt=BF16, XB=3, B=3, M=4, K=64, N=32, w=FAKE, s=FAKE, gs=None, tr=1, route=0,

@@ -384,6 +384,68 @@ def test_qmm_batched_empty_and_misaligned():
         nv.qmm_batched(x_t, words(c.w), u8(c.scales), f32(c.gs))
 
 
+# ----------------------------------------------------------------------------
+# GEMM with K split among blocks (few output tiles)
+# ----------------------------------------------------------------------------
+
+def qmm_ws_raw(x_t, w_t, s_t, gs_t, M, K, N, ws_bytes, out):
+    lib = nv.load_library()
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV) if ws_bytes else None
+    st = lib.nvfp4_qmm_ws(ctypes.c_void_p(x_t.data_ptr()), 1, M, K, N, ctypes.c_void_p(w_t.data_ptr()),
+                          ctypes.c_void_p(s_t.data_ptr()), None if gs_t is None else ctypes.c_void_p(gs_t.data_ptr()),
+                          1, 0, None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+                          ctypes.c_void_p(out.data_ptr()), None)
+    assert st == 0
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("M,K,N", [(65, 2048, 1024), (200, 2048, 300), (256, 1024, 520), (96, 4352, 264)])
+def test_gemm_split_k_small_shapes(M, K, N):
+    """Few output tiles: the binding passes a workspace and K is split
+    (up to 8 ways; K = 4352 leaves a shorter last split); full comparison."""
+    case = synth.dense_case(3950 + M + K, M, K, N, with_gs=True)
+    lib = nv.load_library()
+    assert lib.nvfp4_qmm_workspace_size(M, K, N, 1, 1, 0) > 0
+    out, ref = run_qmm(case, torch.bfloat16, "gemm", guard=True)
+    assert rel(out, ref) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("M", [65, 128, 256])
+def test_gemm_split_k_prefill_shape_sampled(M):
+    """The prefill plane (K=5376, N=21504) at chunk sizes that split three
+    ways: sampled rows against the oracle, all rows against the unsplit
+    path (float32 summation order only)."""
+    wl = synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]
+    case = synth.dense_case(wl["seed"] + M, M, 5376, 21504, with_gs=True)
+    x_t, x_ref = activations(case.x, torch.bfloat16)
+    w_t, s_t, gs_t = words(case.w), u8(case.scales), f32(case.gs)
+    lib = nv.load_library()
+    ws_bytes = int(lib.nvfp4_qmm_workspace_size(M, 5376, 21504, 1, 1, 0))
+    assert ws_bytes == 3 * M * 21504 * 4
+    split = qmm_ws_raw(x_t, w_t, s_t, gs_t, M, 5376, 21504, ws_bytes,
+                       torch.empty((M, 21504), dtype=torch.bfloat16, device=DEV))
+    whole = qmm_ws_raw(x_t, w_t, s_t, gs_t, M, 5376, 21504, 0,
+                       torch.empty((M, 21504), dtype=torch.bfloat16, device=DEV))
+    assert oracle.relative_error(host(split), host(whole)) <= TOL[torch.bfloat16]
+    rows = sorted(set([0, M - 1] + list(np.linspace(0, M - 1, 12).astype(int))))
+    W = oracle.dequantize(case.w, case.scales, case.gs[0]).astype(np.float64)
+    ref = x_ref[rows].astype(np.float64) @ W.T
+    assert oracle.relative_error(host(split)[rows], ref) <= TOL[torch.bfloat16]
+
+
+def test_gemm_split_k_workspace_too_small_falls_back():
+    M, K, N = 128, 2048, 1024
+    case = synth.dense_case(3990, M, K, N, with_gs=True)
+    x_t, x_ref = activations(case.x, torch.bfloat16)
+    ref = oracle.qmm(x_ref, case.w, case.scales, case.gs[0])
+    lib = nv.load_library()
+    need = int(lib.nvfp4_qmm_workspace_size(M, K, N, 1, 1, 0))
+    out = qmm_ws_raw(x_t, words(case.w), u8(case.scales), f32(case.gs), M, K, N, need // 2,
+                     torch.empty((M, N), dtype=torch.bfloat16, device=DEV))
+    assert rel(out, ref) <= TOL[torch.bfloat16]
+
+
 def test_prefill_gemm_full_size_sampled():
     """M=2048, K=5376, N=21504 bf16 through the route that is timed; 48
     sampled activation rows (spread over all row tiles) against the oracle."""
