@@ -677,3 +677,53 @@ def test_multirow_mfma_pipeline_shapes(dtype, K, M, N):
     case = synth.dense_case(3800 + K + M + N, M, K, N, with_gs=True, code_range=codes)
     out, ref = run_qmm(case, dtype, "qmv", guard=True)
     assert rel(out, ref) <= TOL[dtype]
+
+
+# ----------------------------------------------------------------------------
+# Seeded random sweep over shapes, dtypes, routes and global scales
+# ----------------------------------------------------------------------------
+
+def _sweep_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kmul = int(g.choice([16, 32, 64, 256]))
+        K = kmul * int(g.integers(1, 4096 // kmul + 1))
+        M = int(g.choice([1, 2, 3, int(g.integers(4, 34)), int(g.integers(34, 65)), int(g.integers(65, 400))]))
+        N = int(g.integers(1, 700))
+        dtype = [torch.float32, torch.bfloat16, torch.float16][int(g.integers(0, 3))]
+        route = ["auto", "qmv", "gemm"][int(g.integers(0, 3))]
+        cases.append((i, M, K, N, dtype, route, bool(g.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,K,N,dtype,route,with_gs", _sweep_cases(48, 2024))
+def test_qmm_random_sweep(i, M, K, N, dtype, route, with_gs):
+    case = synth.dense_case(7000 + i, M, K, N, with_gs=with_gs)
+    if dtype == torch.float16:   # keep f16 outputs finite
+        case.scales = np.minimum(case.scales, 0x48).astype(np.uint8)
+    out, ref = run_qmm(case, dtype, route, guard=True)
+    assert rel(out, ref) <= TOL[dtype], (M, K, N, dtype, route)
+
+
+def _gather_sweep(n, seed):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        K = int(g.choice([32, 256, 512, 2048, 48]))
+        out.append((i, int(g.integers(1, 40)), int(g.integers(1, 12)), int(g.integers(1, 300)), K,
+                    int(g.integers(1, 4)), bool(g.integers(0, 2)), int(g.integers(1, 4)),
+                    [torch.float32, torch.bfloat16, torch.float16][int(g.integers(0, 3))]))
+    return out
+
+
+@pytest.mark.parametrize("i,tokens,E,N,K,top_k,sort,M,dtype", _gather_sweep(24, 2025))
+def test_gather_random_sweep(i, tokens, E, N, K, top_k, sort, M, dtype):
+    top_k = min(top_k, E)
+    case = synth.gather_case(7500 + i, tokens=tokens, E=E, N=N, K=K, top_k=top_k, sort=sort, with_gs=bool(i % 2),
+                             M=M, out_of_range=(E, 2 ** 31 - 1) if i % 3 == 0 else ())
+    if dtype == torch.float16:
+        case.scales = np.minimum(case.scales, 0x48).astype(np.uint8)
+    out, ref = run_gather(case, dtype, guard=True)
+    assert oracle.relative_error(host(out), ref) <= TOL[dtype], (tokens, E, N, K, top_k, M, dtype)
+    assert_zero_rows(out, case.rhs, case.lhs, E, tokens)
