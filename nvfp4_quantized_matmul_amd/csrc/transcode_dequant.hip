@@ -119,16 +119,48 @@ template <typename TI> __device__ __forceinline__ float widen(TI v) { return (fl
 // magnitudes with NaN above every number (as a float max that propagates NaN).
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu; }
 
-// Largest |w| of each matrix into gs_bits[b] (zeroed beforehand), as bits.
+// The 16 bytes at p as float values (8 bf16/f16 or 4 f32).
 template <typename TI>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const TI* __restrict__ w, int64_t per_mat,
+__device__ __forceinline__ void unpack16(const uint4& raw, float (&v)[16 / sizeof(TI)]) {
+  const TI* h = reinterpret_cast<const TI*>(&raw);
+#pragma unroll
+  for (int j = 0; j < (int)(16 / sizeof(TI)); ++j) v[j] = widen(h[j]);
+}
+
+template <typename TI>
+__device__ __forceinline__ uint32_t chunk_amax_bits(const uint4& raw) {
+  float v[16 / sizeof(TI)];
+  unpack16<TI>(raw, v);
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < (int)(16 / sizeof(TI)); ++j) m = max(m, abs_bits(v[j]));
+  return m;
+}
+
+// Largest |w| of each matrix into gs_bits[b] (zeroed beforehand), as bits:
+// for non-negative floats the unsigned order of the bit patterns is the
+// numeric order, and a NaN pattern sits above +inf, so NaN propagates.  Each
+// matrix is a whole number of 16-byte chunks (its length is a multiple of 16
+// elements) and starts 16-byte aligned; a lane keeps four chunk loads in
+// flight.
+template <typename TI>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const TI* __restrict__ w, int64_t chunks_per_mat,
                                                        int64_t batch, uint32_t* __restrict__ gs_bits) {
   __shared__ uint32_t part[kThreads / 64];
+  const int64_t st = (int64_t)gridDim.x * kThreads;
   for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
-    const TI* m = w + b * per_mat;
+    const uint4* m = reinterpret_cast<const uint4*>(w) + b * chunks_per_mat;
     uint32_t mx = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < per_mat; i += (int64_t)gridDim.x * kThreads)
-      mx = max(mx, abs_bits(widen(m[i])));
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 3 * st < chunks_per_mat; i += 4 * st) {
+      const uint4 r0 = m[i];
+      const uint4 r1 = m[i + st];
+      const uint4 r2 = m[i + 2 * st];
+      const uint4 r3 = m[i + 3 * st];
+      mx = max(max(mx, chunk_amax_bits<TI>(r0)), chunk_amax_bits<TI>(r1));
+      mx = max(max(mx, chunk_amax_bits<TI>(r2)), chunk_amax_bits<TI>(r3));
+    }
+    for (; i < chunks_per_mat; i += st) mx = max(mx, chunk_amax_bits<TI>(m[i]));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mx;
@@ -146,73 +178,101 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const TI* __restrict__ w
 // E4M3 code of a non-negative float: nearest value, ties to the even code;
 // 448 and above saturate to 448 (0x7E); NaN gives 0x7F.
 __device__ __forceinline__ uint32_t e4m3_nearest(float x) {
-  if (!(x == x)) return 0x7Fu;
-  if (x >= 448.0f) return 0x7Eu;
-  if (x < 0.015625f) return (uint32_t)__builtin_rintf(x * 512.0f);   // subnormals m * 2^-9; 8 is 2^-6
   int e;
   const float frac = __builtin_frexpf(x, &e);                         // x = frac * 2^e, frac in [0.5, 1)
-  uint32_t mant = (uint32_t)__builtin_rintf((frac * 2.0f - 1.0f) * 8.0f);
-  int ex = e - 1;                                                      // x = (1 + f) * 2^ex, ex in [-6, 8]
-  if (mant == 8u) {
-    mant = 0u;
-    ++ex;
-  }
-  const uint32_t code = ((uint32_t)(ex + 7) << 3) | mant;
-  return code > 0x7Eu ? 0x7Eu : code;
+  const uint32_t mant = (uint32_t)__builtin_rintf((frac * 2.0f - 1.0f) * 8.0f);   // 0..8; 8 carries
+  const uint32_t normal = ((uint32_t)(e - 1 + 7) << 3) + mant;        // x = (1 + f) * 2^(e-1), e-1 in [-6, 8]
+  const uint32_t sub = (uint32_t)__builtin_rintf(x * 512.0f);         // subnormals m * 2^-9; 8 is 2^-6
+  uint32_t code = x < 0.015625f ? sub : normal;
+  code = code > 0x7Eu ? 0x7Eu : code;
+  code = x >= 448.0f ? 0x7Eu : code;
+  return x == x ? code : 0x7Fu;
 }
 
-// E2M1 magnitude index (0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to a >= 0, ties
-// to the even index, saturating at 6: one step per midpoint crossed, a tie
-// at a midpoint counting toward the even side.
-__device__ __forceinline__ uint32_t e2m1_nearest(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-         (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-}
+// One lane per 16-byte chunk of the input, so sizeof(TI) consecutive lanes
+// hold one 16-element block: 16/sizeof(TI) elements each.  The lanes of a
+// block share its largest magnitude through a cross-lane exchange, each
+// encodes its own elements into 4*16/sizeof(TI) bits of the block's two
+// little-endian words (element j at bits 4j of the 64), and the first lane
+// writes the scale byte.  A workgroup takes kQuantUnroll * kThreads chunks
+// and issues all their loads before any arithmetic, which keeps enough bytes
+// in flight per CU to cover memory latency.  Tiles go in reverse order of
+// address: the matrix-maximum pass that precedes this one sweeps forwards, so
+// the part of the input still held by the last-level cache is read first.
+constexpr int kQuantUnroll = 4;
 
-// One thread per 16-element block.
 template <typename TI>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const TI* __restrict__ w, int64_t nblocks,
-                                                           int64_t blocks_per_mat, const float* __restrict__ gs,
+__device__ __forceinline__ void quantize_chunk(const uint4& raw, int64_t c, float gsb,
+                                               uint32_t* __restrict__ w_out, uint8_t* __restrict__ sc_out) {
+  constexpr int L = (int)sizeof(TI);   // lanes per block
+  constexpr int E = 16 / L;            // elements per lane
+  float v[E];
+  unpack16<TI>(raw, v);
+  uint32_t am = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) am = max(am, abs_bits(v[j]));
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 64));
+  const int64_t blk = c / L;
+  const float amax = __builtin_bit_cast(float, am);
+  const uint32_t code = (amax != 0.0f && gsb != 0.0f) ? e4m3_nearest(amax * (448.0f / gsb)) : 0u;
+  const float d = e4m3<0>(code) * (gsb / kGlobalDivisor);
+  const bool no_scale = !(d != 0.0f && d == d);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) bits |= (__builtin_bit_cast(uint32_t, v[j]) >> 31) << (4 * j + 3);
+  if (!no_scale) {
+    // |v| / d rounded once in float32 (correctly rounded division), then to
+    // the nearest E2M1 magnitude by the hardware converter: ties to even,
+    // saturating at 6 (the clamp keeps infinities in its finite range).
+    float q[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) q[j] = __builtin_fminf(__builtin_fabsf(v[j]) / d, 8.0f);
+    uint32_t mags = 0;
+    mags = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(mags, q[0], q[1], 1.0f, 0);
+    mags = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(mags, q[2], q[3], 1.0f, 1);
+    if constexpr (E == 8) {
+      mags = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(mags, q[4], q[5], 1.0f, 2);
+      mags = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(mags, q[6], q[7], 1.0f, 3);
+    }
+    bits |= mags;
+  }
+  if constexpr (L == 2)
+    w_out[c] = bits;
+  else
+    reinterpret_cast<uint16_t*>(w_out)[c] = (uint16_t)bits;
+  if (c % L == 0) sc_out[blk] = (uint8_t)code;
+}
+
+// Grid: x over tiles of one matrix, y over matrices, so each workgroup's
+// global scale is one uniform value.
+template <typename TI>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const TI* __restrict__ w, int64_t chunks_per_mat,
+                                                           int64_t batch, const float* __restrict__ gs,
                                                            uint32_t* __restrict__ w_out,
                                                            uint8_t* __restrict__ sc_out) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks; blk += stride) {
-    float v[16];
-    if constexpr (sizeof(TI) == 4) {
-      const float4* p = reinterpret_cast<const float4*>(w + blk * 16);
+  constexpr int64_t kTile = (int64_t)kThreads * kQuantUnroll;
+  const int64_t tiles = (chunks_per_mat + kTile - 1) / kTile;
+  for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    const float gsb = gs[b];
+    const int64_t mat0 = b * chunks_per_mat;
+    const uint4* src = reinterpret_cast<const uint4*>(w) + mat0;
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+      const int64_t base = (tiles - 1 - t) * kTile + threadIdx.x;
+      uint4 raw[kQuantUnroll];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 t = p[q];
-        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+      for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t c = base + u * kThreads;
+        raw[u] = c < chunks_per_mat ? src[c] : make_uint4(0u, 0u, 0u, 0u);
       }
-    } else {
-      const uint4* p = reinterpret_cast<const uint4*>(w + blk * 16);
+      // chunks_per_mat is a multiple of sizeof(TI) and so is every chunk
+      // index's lane offset: the lanes of one block are all in or all out.
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint4 t = p[q];
-        const TI* h = reinterpret_cast<const TI*>(&t);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[8 * q + j] = widen(h[j]);
+      for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t c = base + u * kThreads;
+        if (c < chunks_per_mat) quantize_chunk<TI>(raw[u], mat0 + c, gsb, w_out, sc_out);
       }
     }
-    uint32_t am = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) am = max(am, abs_bits(v[j]));
-    const float amax = __builtin_bit_cast(float, am);
-    const float gsb = gs[blk / blocks_per_mat];
-    uint32_t code = 0;
-    if (amax != 0.0f && gsb != 0.0f) code = e4m3_nearest(amax * (448.0f / gsb));
-    const float d = e4m3<0>(code) * (gsb / kGlobalDivisor);
-    const bool no_scale = !(d != 0.0f && d == d);
-    uint32_t word[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t sign = (__builtin_bit_cast(uint32_t, v[j]) >> 31) << 3;
-      const uint32_t mag = no_scale ? 0u : e2m1_nearest(__builtin_fabsf(v[j] / d));
-      word[j >> 3] |= (sign | mag) << (4 * (j & 7));
-    }
-    *reinterpret_cast<uint2*>(w_out + blk * 2) = make_uint2(word[0], word[1]);
-    sc_out[blk] = (uint8_t)code;
   }
 }
 
@@ -282,20 +342,23 @@ static void quantize_typed(const TI* w, int64_t batch, int64_t rows, int64_t col
   if (!gs_in) {
     launch_fill_zero(gs_out, batch * 4, s);
     if (per_mat > 0) {
-      const int64_t gx = grid_for(per_mat, kThreads * 8, 1024);
+      const int64_t chunks = per_mat * (int64_t)sizeof(TI) / 16;
+      const int64_t gx = grid_for(chunks, kThreads * 16, 2048);
       const int64_t gy = batch < 65535 ? batch : 65535;
       amax_kernel<TI><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s>>>(
-          w, per_mat, batch, reinterpret_cast<uint32_t*>(gs_out));
+          w, chunks, batch, reinterpret_cast<uint32_t*>(gs_out));
     }
     gs = gs_out;
   } else if (gs_out && gs_out != gs_in) {
     copy_floats_kernel<<<dim3((unsigned)grid_for(batch, kThreads, 1 << 16)), dim3(kThreads), 0, s>>>(gs_in, gs_out,
                                                                                                       batch);
   }
-  const int64_t nblocks = batch * per_mat / 16;
-  if (nblocks == 0) return;
-  quantize_kernel<TI><<<dim3((unsigned)grid_for(nblocks, kThreads, 1 << 20)), dim3(kThreads), 0, s>>>(
-      w, nblocks, per_mat / 16, gs, w_out, sc_out);
+  const int64_t chunks = per_mat * (int64_t)sizeof(TI) / 16;
+  if (chunks == 0) return;
+  const int64_t gx = grid_for(chunks, kThreads * kQuantUnroll, 1 << 16);
+  const int64_t gy = batch < 65535 ? batch : 65535;
+  quantize_kernel<TI><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s>>>(w, chunks, batch, gs, w_out,
+                                                                                  sc_out);
 }
 
 void launch_quantize(const void* w, nvfp4_dtype_t dt, int64_t batch, int64_t rows, int64_t cols,

@@ -214,6 +214,38 @@ def test_quantize_special_values():
     quantize_both(dense, torch.float32)                 # gs = NaN (the matrix holds one)
 
 
+def test_quantize_e2m1_thresholds():
+    """Every E2M1 rounding midpoint (0.25 .. 5) and its two float32
+    neighbours, as quotients of block scales that are not powers of two
+    (normal and subnormal E4M3), with either sign; then saturation of
+    quotients beyond 6 (and of an infinity) under a small global scale, and
+    tiny or subnormal elements that keep only their sign."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    rows = []
+    for sc in [1.0, 1.125, 0.8125, 3.5, 0.01171875, 88.0]:
+        d = np.float32(sc)
+        vals = []
+        for t in mids:
+            c = np.float32(np.float32(t) * d)
+            vals += [np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))]
+        vals += [np.float32(0.0)] * (30 - len(vals))
+        for sign in (1.0, -1.0):
+            row = np.zeros(32, dtype=np.float32)
+            row[0] = row[16] = np.float32(6.0) * d
+            row[1:16] = np.float32(sign) * np.asarray(vals[:15], dtype=np.float32)
+            row[17:32] = np.float32(sign) * np.asarray(vals[15:30], dtype=np.float32)
+            rows.append(row)
+    quantize_both(np.stack(rows), torch.float32, gs=[2688.0])
+
+    sat = np.zeros((2, 32), dtype=np.float32)
+    sat[0, :16] = [100, 7.0, 6.5, -50, np.inf, 3, -np.inf, 1e30, 0.2, -0.2, 5, 6, 0, -0.0, 1, 2]
+    sat[1, :16] = np.float32(6.0)
+    sat[1, 1:5] = [1e-30, -1e-30, 1e-40, -1e-40]
+    sat[1, 16:] = np.float32(-3.0)
+    quantize_both(sat, torch.float32, gs=[1.0])
+    quantize_both(sat[1:], torch.float32, gs=[2688.0])
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_quantize_round_trip_through_the_library(dtype):
     """Planes whose blocks each hold a +-6 come back unchanged through the
