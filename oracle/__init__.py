@@ -17,10 +17,13 @@ from .nvfp4_oracle import (  # noqa: F401
     e2m1_value,
     e4m3_value,
     f32_to_bf16_bits,
+    GLU_ACTIVATIONS,
     gather_qmm,
+    glu_activation,
     global_factor,
     qmm,
     qmm_batched,
+    qmm_glu,
     quantize,
     e2m1_round,
     e4m3_round,

@@ -40,7 +40,13 @@ Readings where the pages are silent (each listed in the design notes):
 * quantize takes each matrix's largest |w| as its global scale unless one is
   given, rounds the block scale amax * 448 / gs to E4M3 and each w / d to
   E2M1 by round-to-nearest-even in float32 (saturating at 448 and 6), and
-  keeps the sign of values that round to zero.
+  keeps the sign of values that round to zero;
+* the gated MLP projection of P2 ("Hypothesis", "Activation-path
+  follow-up": the scaled gate/up MLP of the Gemma and Llama 4 paths with its
+  GeGLU activation) is act(x @ Wg.T) * (x @ Wu.T), each plane with its own
+  global scale, the activation applied to the gate projection; the pages do
+  not define the activation, so the oracle offers GELU in its erf form, the
+  tanh approximation that Gemma's GeGLU uses, and SiLU (Llama's SwiGLU).
 
 Every function below works on numpy arrays; bf16 tensors are represented as
 their uint16 bit patterns.
@@ -48,6 +54,7 @@ their uint16 bit patterns.
 
 from __future__ import annotations
 
+import math
 from typing import Optional
 
 import numpy as np
@@ -338,6 +345,57 @@ def qmm_batched(x: np.ndarray, w: np.ndarray, scales: np.ndarray, gs=None,
         N = w.shape[1] if transpose else w.shape[2] * NIBBLES_PER_WORD
         return np.zeros((0, M, N), dtype=np.float64)
     return np.stack(parts)
+
+
+# ----------------------------------------------------------------------------
+# Gated MLP projection
+# ----------------------------------------------------------------------------
+
+GLU_ACTIVATIONS = ("gelu_tanh", "gelu", "silu")
+
+
+def glu_activation(z, act: str) -> np.ndarray:
+    """Gate activation in float64.
+
+    gelu:      z * Phi(z), Phi the standard normal distribution function
+               (Hendrycks and Gimpel, "Gaussian Error Linear Units", the exact
+               form), written as erfc(-z / sqrt 2) / 2, which keeps its
+               relative accuracy where 1 + erf(z / sqrt 2) would cancel.
+    gelu_tanh: the same paper's approximation
+               z / 2 * (1 + tanh(sqrt(2 / pi) * (z + 0.044715 * z^3))).
+    silu:      z * sigmoid(z) (the sigmoid-weighted linear unit, "Swish"
+               with beta = 1).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    if act == "gelu":
+        erfc = np.vectorize(math.erfc, otypes=[np.float64])
+        return 0.5 * z * erfc(-z / math.sqrt(2.0))
+    if act == "gelu_tanh":
+        inner = math.sqrt(2.0 / math.pi) * (z + 0.044715 * z * z * z)
+        return 0.5 * z * (1.0 + np.tanh(inner))
+    if act == "silu":
+        with np.errstate(over="ignore"):
+            return z / (1.0 + np.exp(-z))
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def qmm_glu(x: np.ndarray, w_gate: np.ndarray, s_gate: np.ndarray, gs_gate,
+            w_up: np.ndarray, s_up: np.ndarray, gs_up, act: str) -> np.ndarray:
+    """Gated projection of an MLP against two NVFP4 planes (P2 "Hypothesis"
+    and "Activation-path follow-up": the gate/up projections of the scaled
+    MLP, each with its global-scale sidecar, and the GeGLU activation):
+
+        out = act(x @ dequantize(w_gate).T) * (x @ dequantize(w_up).T)
+
+    w_gate and w_up are transposed planes [F, K/8] of the same shape.  Both
+    projections are the float64 ``qmm`` above; the activation and the
+    product are taken in float64.  Returns float64 [M, F].
+    """
+    if w_gate.shape != w_up.shape:
+        raise ValueError("gate and up planes differ in shape")
+    gate = qmm(x, w_gate, s_gate, gs_gate, transpose=True)
+    up = qmm(x, w_up, s_up, gs_up, transpose=True)
+    return glu_activation(gate, act) * up
 
 
 def gather_qmm(x: np.ndarray, lhs: Optional[np.ndarray], rhs: np.ndarray,

@@ -480,6 +480,89 @@ def test_transcode_without_second_scale():
     assert gs is None and words.shape == (1, 2, 2)
 
 
+# ----------------------------------------------------------------------------
+# Gated MLP projection
+# ----------------------------------------------------------------------------
+
+# The standard normal distribution function at a few points, as printed in
+# tables of Phi.
+PHI_TABLE = {0.0: 0.5, 1.0: 0.8413447460685429, -1.0: 0.15865525393145707,
+             2.0: 0.9772498680518208, -2.5: 0.006209665325776132, 3.0: 0.9986501019683699}
+
+
+def test_gelu_is_z_times_the_normal_distribution_function():
+    for z, phi in PHI_TABLE.items():
+        got = float(orc.glu_activation(np.array([z]), "gelu")[0])
+        assert abs(got - z * phi) <= 1e-15 * max(1.0, abs(z)), z
+    from scipy.stats import norm
+    zs = np.linspace(-12.0, 12.0, 481)
+    assert np.allclose(orc.glu_activation(zs, "gelu"), zs * norm.cdf(zs), rtol=1e-13, atol=1e-300)
+
+
+def library_activation(z, act):
+    t = torch.as_tensor(np.asarray(z, dtype=np.float64))
+    if act == "gelu":
+        return torch.nn.functional.gelu(t, approximate="none").numpy()
+    if act == "gelu_tanh":
+        return torch.nn.functional.gelu(t, approximate="tanh").numpy()
+    return torch.nn.functional.silu(t).numpy()
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh", "silu"])
+def test_activations_match_library_routines(act):
+    zs = np.concatenate([np.linspace(-30.0, 30.0, 2401), [-700.0, -88.0, 1e-300, -1e-300, 0.0, 88.0, 700.0]])
+    got = orc.glu_activation(zs, act)
+    want = library_activation(zs, act)
+    # torch forms the erf GELU as 1 + erf(z / sqrt 2), which cancels to 0
+    # below z ~ -8.3 (true values < 1e-16): an absolute floor covers that tail.
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-15), act
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh", "silu"])
+def test_activation_odd_part_is_the_identity(act):
+    """act(z) = z * c(z) with c(-z) = 1 - c(z) for all three, so
+    act(z) - act(-z) = z."""
+    zs = np.linspace(-9.0, 9.0, 361)
+    d = orc.glu_activation(zs, act) - orc.glu_activation(-zs, act)
+    assert np.allclose(d, zs, rtol=1e-14, atol=1e-14)
+
+
+def test_gelu_forms_differ():
+    """The tanh form is an approximation: close to the erf form, not equal."""
+    zs = np.linspace(-5.0, 5.0, 201)
+    d = np.abs(orc.glu_activation(zs, "gelu") - orc.glu_activation(zs, "gelu_tanh"))
+    assert 1e-5 < d.max() < 1e-3
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh", "silu"])
+def test_qmm_glu_bruteforce(act):
+    """Gate and up planes with their own global scales: exact rational
+    projections, the library activation on the gate, times the up."""
+    g = synth.dense_case(25, M=2, K=32, N=3, with_gs=True, code_range=synth.FINITE_POSITIVE_CODES)
+    u = synth.dense_case(26, M=2, K=32, N=3, with_gs=True, code_range=synth.FINITE_POSITIVE_CODES)
+    got = orc.qmm_glu(g.x, g.w, g.scales, g.gs[0], u.w, u.scales, u.gs[0], act)
+    gate = brute_qmm(g.x, g.w, g.scales, g.gs[0], True)
+    up = brute_qmm(g.x, u.w, u.scales, u.gs[0], True)
+    assert got.shape == (2, 3)
+    want = np.zeros((2, 3))
+    for m in range(2):
+        for f in range(3):
+            a = library_activation(np.array([float(gate[m][f].value)]), act)[0]
+            want[m, f] = a * float(up[m][f].value)
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want)), (got, want)
+
+
+def test_qmm_glu_without_global_scales_and_shape_check():
+    g = synth.dense_case(27, M=1, K=16, N=2, with_gs=False)
+    u = synth.dense_case(28, M=1, K=16, N=2, with_gs=False)
+    got = orc.qmm_glu(g.x, g.w, g.scales, None, u.w, u.scales, None, "silu")
+    gate = orc.qmm(g.x, g.w, g.scales)
+    up = orc.qmm(g.x, u.w, u.scales)
+    assert np.allclose(got, gate / (1.0 + np.exp(-gate)) * up, rtol=1e-15, atol=0)
+    with pytest.raises(ValueError):
+        orc.qmm_glu(g.x, g.w, g.scales, None, u.w[:1], u.scales[:1], None, "silu")
+
+
 def test_relative_error_metric():
     ref = np.array([1.0, -4.0, 2.0])
     out = np.array([1.0, -4.5, 2.0])
@@ -504,6 +587,10 @@ PIN_TESTS = [
     test_quantize_rounding_fixture,
     test_quantize_dequantize_round_trip_is_exact,
     test_transcode_reconstructs_source_weights,
+    lambda: test_qmm_glu_bruteforce("gelu_tanh"),
+    lambda: test_activations_match_library_routines("gelu_tanh"),
+    lambda: test_activations_match_library_routines("gelu"),
+    lambda: test_activations_match_library_routines("silu"),
 ]
 
 
@@ -595,6 +682,41 @@ def _mut_e4m3_truncate(value):
     return best
 
 
+def _mut_glu_act_on_up(x, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, act):
+    gate = orc.qmm(x, w_gate, s_gate, gs_gate)
+    up = orc.qmm(x, w_up, s_up, gs_up)
+    return gate * orc.glu_activation(up, act)
+
+
+def _mut_glu_shared_gs(x, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, act):
+    gate = orc.qmm(x, w_gate, s_gate, gs_gate)
+    up = orc.qmm(x, w_up, s_up, gs_gate)
+    return orc.glu_activation(gate, act) * up
+
+
+_glu_activation = orc.glu_activation
+
+
+def _mut_gelu_tanh_no_cubic(z, act):
+    if act == "gelu_tanh":
+        z = np.asarray(z, dtype=np.float64)
+        return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * z))
+    return _glu_activation(z, act)
+
+
+def _mut_silu_sigmoid_only(z, act):
+    if act == "silu":
+        return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+    return _glu_activation(z, act)
+
+
+def _mut_gelu_no_sqrt2(z, act):
+    if act == "gelu":
+        z = np.asarray(z, dtype=np.float64)
+        return 0.5 * z * np.vectorize(math.erfc)(-z)
+    return _glu_activation(z, act)
+
+
 MUTATIONS = {
     "quantize E2M1 ties away from zero": ("e2m1_round", _mut_e2m1_ties_away),
     "quantize E4M3 scale truncated": ("e4m3_round", _mut_e4m3_truncate),
@@ -610,6 +732,11 @@ MUTATIONS = {
     "E2M1 table swapped": ("E2M1_MAGNITUDES", (0.0, 0.5, 1.0, 1.5, 2.0, 4.0, 3.0, 6.0)),
     "non-transposed operand reversed": ("qmm", _mut_qmm_transpose),
     "gather out-of-range wraps": ("gather_qmm", _mut_gather_no_zero),
+    "glu activation on the up projection": ("qmm_glu", _mut_glu_act_on_up),
+    "glu up projection with the gate's global scale": ("qmm_glu", _mut_glu_shared_gs),
+    "gelu tanh form without the cubic term": ("glu_activation", _mut_gelu_tanh_no_cubic),
+    "silu as the sigmoid alone": ("glu_activation", _mut_silu_sigmoid_only),
+    "gelu erf argument not divided by sqrt 2": ("glu_activation", _mut_gelu_no_sqrt2),
 }
 
 
