@@ -11,11 +11,13 @@ so weights come from HBM; the same steps replayed as one HIP graph are
 reported beside it.
 
 Also reported, each against its roofline: the prefill GEMM (M=2048,
-TFLOP/s), the multi-row qmv (M=16) and the MoE gather (sorted prefill and
-unsorted decode, GB/s); under ``other_configs`` the tiny qmv's latency,
-multi-row qmv at every M in f32 and bf16, MoE unsorted decode at B = 1..8,
-batched-weight qmm and the load-time transcode / dequantize / quantize.  Kernel durations come from HIP events around back-to-back
-launches on the launch stream.  The CPU oracle is timed on the host
+TFLOP/s), the fused gate/up MLP projection at the same shape, the
+multi-row qmv (M=16) and the MoE gather (sorted prefill and unsorted
+decode, GB/s); under ``other_configs`` the tiny qmv's latency, multi-row
+qmv at every M in f32 and bf16, MoE unsorted decode at B = 1..8,
+batched-weight qmm and the load-time transcode / dequantize / quantize.
+Kernel durations come from HIP events around back-to-back launches on the
+launch stream.  The CPU oracle is timed on the host
 on the full decode workload (cpu_baseline).
 
 Prints one JSON line.
@@ -137,6 +139,28 @@ class Prefill:
         c = i % len(self.w)
         check(self.lib.nvfp4_qmm(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]),
                                  P(self.gs), 1, 0, P(self.out), stream_ptr()), "prefill qmm")
+
+
+class MlpGateUp:
+    """Gated MLP projection act(x Wg^T) * (x Wu^T), tanh GELU, at the prefill
+    MLP shape M=2048, K=5376, F=21504, bf16, one global scale per plane; the
+    gate and up planes of launch c are the weight copies 2c and 2c+1."""
+    M, K, F = 2048, 5376, 21504
+
+    def __init__(self, pre: Prefill, decode: Decode):
+        self.x = pre.x
+        self.w, self.s, self.gs = decode.w, decode.s, decode.gs
+        self.out = torch.empty((self.M, self.F), dtype=torch.bfloat16, device=DEV)
+        self.lib = decode.lib
+        self.flops = 2 * 2.0 * self.M * self.K * self.F
+        self.fn = self.lib.nvfp4_qmm_glu
+
+    def prebuilt(self):
+        st = stream_ptr()
+        pairs = len(self.w) // 2
+        return [(P(self.x), BF16, self.M, self.K, self.F, P(self.w[2 * c]), P(self.s[2 * c]), P(self.gs),
+                 P(self.w[2 * c + 1]), P(self.s[2 * c + 1]), P(self.gs), 0, None, 0, P(self.out), st)
+                for c in range(pairs)]
 
 
 class MultiRow:
@@ -482,6 +506,24 @@ def main():
     pdur = eager_launch_us(pre, 16, warmup=20)
     ptf = pre.flops / (pdur["mean_us"] * 1e-6) / 1e12
 
+    log("mlp gate/up")
+    mlp = MlpGateUp(pre, dec)
+    gdur = eager_launch_us(mlp, 16, warmup=8)
+    gtf = mlp.flops / (gdur["mean_us"] * 1e-6) / 1e12
+    # the same projection unfused, for comparison: two library qmm launches
+    # (gate, up) and the activation and product as torch elementwise ops
+    gate_t = torch.empty_like(mlp.out)
+    up_t = torch.empty_like(mlp.out)
+
+    def unfused(i):
+        c = i % (len(dec.w) // 2)
+        nv.qmm(pre.x, dec.w[2 * c], dec.s[2 * c], dec.gs, out=gate_t)
+        nv.qmm(pre.x, dec.w[2 * c + 1], dec.s[2 * c + 1], dec.gs, out=up_t)
+        torch.nn.functional.gelu(gate_t, approximate="tanh").mul_(up_t)
+
+    unfused_us = timed_us(unfused, 8, warmup=2)
+    del gate_t, up_t
+
     log("multi-row qmv")
     mr = MultiRow(16, copies=16)
     mdur = eager_launch_us(mr, 64)
@@ -531,6 +573,16 @@ def main():
                     "roofline": {"bound": "mfma", "achieved": round(ptf, 2), "peak": BF16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(ptf / BF16_PEAK_TFLOPS, 4),
                                  "kernel": "gemm_mfma_v3_kernel", "kernel_duration": pdur}},
+        "mlp_gate_up_prefill": {"workload": "mlp_gate_up_m2048_k5376_f21504_bf16_gelu_tanh",
+                                "value": round(gtf, 2), "unit": "TFLOP/s", "flops": mlp.flops,
+                                "roofline": {"bound": "mfma", "achieved": round(gtf, 2), "peak": BF16_PEAK_TFLOPS,
+                                             "unit": "TFLOP/s", "frac": round(gtf / BF16_PEAK_TFLOPS, 4),
+                                             "kernel": "gemm_mfma_v3_kernel<glu>", "kernel_duration": gdur},
+                                "separate_qmm_pair_us": round(2 * pdur["mean_us"], 2),
+                                "unfused_us": round(unfused_us, 2),
+                                "note": "one fused launch; separate_qmm_pair_us = two prefill qmm launches of the "
+                                        "same planes; unfused_us = those two launches plus the activation and "
+                                        "product as torch elementwise ops (measurement only)"},
         "multirow_m16": {"workload": "multirow_qmv_m16_k4096_n14336_bf16", "value": round(mgbs, 2),
                          "unit": "GB/s", "frac_hbm": round(mgbs / HBM_PEAK_GBS, 4),
                          "kernel": "skinny_kernel<bf16,1,16>", "kernel_duration": mdur, "bytes": mr.bytes},

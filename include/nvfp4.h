@@ -53,6 +53,19 @@ typedef enum nvfp4_route {
   NVFP4_ROUTE_GEMM = 2
 } nvfp4_route_t;
 
+/* Gate activation of nvfp4_qmm_glu (mlxcel issue "perf(metal): close native
+ * NVFP4 prefill gap", "Activation-path follow-up": the GeGLU activation of
+ * the scaled MLP; the pages do not define it further).
+ *   NVFP4_ACT_GELU_TANH  z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))),
+ *                        the tanh approximation of GELU (Gemma's GeGLU);
+ *   NVFP4_ACT_GELU       z * Phi(z), GELU's exact form;
+ *   NVFP4_ACT_SILU       z * sigmoid(z) (SwiGLU, as in Llama). */
+typedef enum nvfp4_act {
+  NVFP4_ACT_GELU_TANH = 0,
+  NVFP4_ACT_GELU = 1,
+  NVFP4_ACT_SILU = 2
+} nvfp4_act_t;
+
 /* Status codes. */
 enum {
   NVFP4_OK = 0,
@@ -194,6 +207,45 @@ int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
  */
 int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
                                  nvfp4_dtype_t dtype, nvfp4_route_t route);
+
+/*
+ * nvfp4_qmm_glu -- the gated projection of an MLP against two NVFP4 planes
+ * (mlxcel issue "perf(metal): close native NVFP4 prefill gap", "Hypothesis"
+ * and "Activation-path follow-up": the scaled gate/up MLP of the Gemma and
+ * Llama 4 paths, each projection with its global-scale sidecar, followed by
+ * the GeGLU activation; "Acceptance criteria": a fused native prefill path
+ * with unchanged dequantization semantics):
+ *
+ *   out[m, f] = act(g_gate * sum_k x[m, k] W_gate[f, k]) * (g_up * sum_k x[m, k] W_up[f, k])
+ *
+ *   x        [M, K] activations of `dtype`;
+ *   w_gate, w_up     transposed planes [F, K/8] (K % 16 == 0);
+ *   s_gate, s_up     their scale planes [F, K/16];
+ *   gs_gate, gs_up   NULL or device float[1] each (g = gs / 2688);
+ *   act      the gate activation;
+ *   out      [M, F] of `dtype`, 16-byte aligned.
+ *
+ * bf16 activations with K % 64 == 0, at sizes where nvfp4_qmm takes its GEMM
+ * route, run as ONE kernel: each tile multiplies gate and up rows of the same
+ * features and applies g, the activation and the product to the float32 sums
+ * before the single rounding to bf16; no workspace is used.  Every other case
+ * runs both projections through nvfp4_qmm's kernels into `workspace` and
+ * `out` and then combines them (one extra rounding of each projection to the
+ * output dtype).  nvfp4_qmm_glu_workspace_size gives the bytes that case needs
+ * (0 for the fused case); a smaller workspace returns NVFP4_ERR_SHAPE.  The
+ * workspace must not overlap any other argument; its contents are scratch.
+ * Errors as nvfp4_qmm; an unknown act returns NVFP4_ERR_SHAPE.
+ */
+int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t F,
+                  const uint32_t* w_gate, const uint8_t* s_gate, const float* gs_gate,
+                  const uint32_t* w_up, const uint8_t* s_up, const float* gs_up,
+                  nvfp4_act_t act, void* workspace, int64_t workspace_bytes, void* out,
+                  hipStream_t stream);
+
+/* Workspace bytes nvfp4_qmm_glu needs for these sizes (host only): 0 when it
+ * runs the fused kernel, M * F * sizeof(dtype) rounded up to 256 otherwise;
+ * a negative status for invalid sizes or dtype. */
+int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtype_t dtype);
 
 /*
  * nvfp4_qmm_batched -- nvfp4_qmm over a batch of weight matrices (mlxcel PR

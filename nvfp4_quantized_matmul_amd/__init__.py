@@ -23,8 +23,8 @@ import torch
 
 __all__ = [
     "NVFP4Error", "library_path", "load_library", "transcode", "dequantize", "quantize", "qmm",
-    "qmm_batched", "gather_qmm", "select_route", "qmv_max_rows", "status_string",
-    "ROUTE_AUTO", "ROUTE_QMV", "ROUTE_GEMM",
+    "qmm_batched", "qmm_glu", "gather_qmm", "select_route", "qmv_max_rows", "status_string",
+    "ROUTE_AUTO", "ROUTE_QMV", "ROUTE_GEMM", "GLU_ACTIVATIONS",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,9 @@ _LIB_NAME = "libnvfp4.so"
 ROUTE_AUTO, ROUTE_QMV, ROUTE_GEMM = 0, 1, 2
 _ROUTES = {"auto": ROUTE_AUTO, "qmv": ROUTE_QMV, "gemm": ROUTE_GEMM}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+# Gate activations of qmm_glu, by the names the C header's nvfp4_act_t stands for.
+_ACTS = {"gelu_tanh": 0, "gelu": 1, "silu": 2}
+GLU_ACTIVATIONS = tuple(_ACTS)
 _WORD_DTYPES = (torch.int32, torch.uint32)
 
 _lib = None
@@ -70,6 +73,8 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_qmm_batched": [vp, c_int, i64, i64, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_qmm_ws": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, i64, vp, vp],
         "nvfp4_qmm_workspace_size": [i64, i64, i64, c_int, c_int, c_int],
+        "nvfp4_qmm_glu": [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, c_int, vp, i64, vp, vp],
+        "nvfp4_qmm_glu_workspace_size": [i64, i64, i64, c_int],
         "nvfp4_gather_qmm": [vp, c_int, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, i64, c_int, vp, vp],
         "nvfp4_select_route": [i64, i64, i64, c_int, c_int],
         "nvfp4_qmv_max_rows": [],
@@ -82,6 +87,7 @@ def load_library() -> ctypes.CDLL:
         fn.restype = c_int
     lib.nvfp4_qmv_max_rows.restype = i64
     lib.nvfp4_qmm_workspace_size.restype = i64
+    lib.nvfp4_qmm_glu_workspace_size.restype = i64
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -304,6 +310,50 @@ def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[tor
     _check("nvfp4_qmm", lib.nvfp4_qmm(
         _ptr(x), code, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), tr,
         _ROUTES[route], _ptr(out), _stream(dev)))
+    return out
+
+
+def qmm_glu(x: torch.Tensor, w_gate: torch.Tensor, s_gate: torch.Tensor, gs_gate: Optional[torch.Tensor],
+            w_up: torch.Tensor, s_up: torch.Tensor, gs_up: Optional[torch.Tensor], act: str = "gelu_tanh",
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gated MLP projection: out = act(x @ dequantize(w_gate).T) * (x @ dequantize(w_up).T).
+
+    x [..., K] (float32, bfloat16 or float16); w_gate and w_up transposed
+    planes [F, K/8] of one shape with their scale planes; gs_gate and gs_up
+    float32 with one element, or None; act one of GLU_ACTIVATIONS.  The output
+    has x's dtype and shape [..., F].  Where the library runs the two
+    projections separately it gets a workspace from torch's allocator.
+    """
+    check_planes(w_gate, s_gate)
+    check_planes(w_up, s_up)
+    if w_gate.dim() != 2 or tuple(w_gate.shape) != tuple(w_up.shape):
+        raise ValueError("w_gate and w_up must be 2-D planes of one shape")
+    F, K = w_gate.shape[0], w_gate.shape[1] * 8
+    if x.shape[-1] != K:
+        raise ValueError(f"x has K={x.shape[-1]}, weight planes imply K={K}")
+    for g in (gs_gate, gs_up):
+        if g is not None and (g.dtype != torch.float32 or g.numel() != 1):
+            raise ValueError("global scales must be float32 tensors with one element")
+    if act not in _ACTS:
+        raise ValueError(f"act must be one of {GLU_ACTIVATIONS}")
+    code = _dtype_code(x.dtype)
+    M = 1
+    for d in x.shape[:-1]:
+        M *= d
+    dev = _require_gpu(x, w_gate, s_gate, gs_gate, w_up, s_up, gs_up)
+    lib = load_library()
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (F,), dtype=x.dtype, device=dev)
+    elif out.dtype != x.dtype or tuple(out.shape) != tuple(x.shape[:-1]) + (F,):
+        raise ValueError("out has the wrong dtype or shape")
+    _require_gpu(out)
+    ws_bytes = int(lib.nvfp4_qmm_glu_workspace_size(M, K, F, code))
+    if ws_bytes < 0:
+        raise NVFP4Error("nvfp4_qmm_glu_workspace_size", ws_bytes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+    _check("nvfp4_qmm_glu", lib.nvfp4_qmm_glu(
+        _ptr(x), code, M, K, F, _ptr(w_gate), _ptr(s_gate), _ptr(gs_gate), _ptr(w_up), _ptr(s_up),
+        _ptr(gs_up), _ACTS[act], _ptr(ws), ws_bytes, _ptr(out), _stream(dev)))
     return out
 
 

@@ -6,6 +6,7 @@
 // review"): the scale plane is derived from the weight plane so the two
 // cannot disagree, the quantized axis must be a multiple of 16, grids are
 // bounded, and an empty output launches nothing.
+#include <climits>
 #include <cstdint>
 #include <cstring>
 
@@ -100,6 +101,15 @@ void qmm_launch(const QmmPlan& plan, const void* x, nvfp4_dtype_t dtype, int64_t
       break;
   }
 }
+
+// True when nvfp4_qmm_glu runs the fused gate/up kernel for these sizes:
+// bf16 activations, K % 64 == 0, and sizes where qmm takes the GEMM route.
+bool glu_fused(int64_t M, int64_t K, int64_t F, nvfp4_dtype_t dtype) {
+  return dtype == NVFP4_BF16 && K > 0 && K % 64 == 0 && M > 0 && F > 0 &&
+         nvfp4_select_route(M, K, F, 1, dtype) == NVFP4_ROUTE_GEMM;
+}
+
+bool valid_act(int act) { return act == NVFP4_ACT_GELU_TANH || act == NVFP4_ACT_GELU || act == NVFP4_ACT_SILU; }
 
 }  // namespace
 
@@ -239,6 +249,58 @@ int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64
       return NVFP4_ERR_SHAPE;
   }
   qmm_launch(plan, x, dtype, M, K, N, w, scales, gs, transpose, out, stream, workspace, workspace_bytes);
+  return launched();
+}
+
+int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtype_t dtype) {
+  if (M < 0 || K < 0 || F < 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  int64_t t, mf;
+  if (!mul_ok(M, K, &t) || !mul_ok(K, F, &t) || !mul_ok(M, F, &mf) || !mul_ok(mf, dtype_size(dtype), &t) ||
+      t > INT64_MAX - 256)
+    return NVFP4_ERR_SHAPE;
+  if (M == 0 || F == 0 || K == 0 || glu_fused(M, K, F, dtype)) return 0;
+  return (t + 255) / 256 * 256;
+}
+
+int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t F, const uint32_t* w_gate,
+                  const uint8_t* s_gate, const float* gs_gate, const uint32_t* w_up, const uint8_t* s_up,
+                  const float* gs_up, nvfp4_act_t act, void* workspace, int64_t workspace_bytes, void* out,
+                  hipStream_t stream) {
+  const int64_t need = nvfp4_qmm_glu_workspace_size(M, K, F, dtype);
+  if (need < 0) return (int)need;
+  if (!valid_act((int)act)) return NVFP4_ERR_SHAPE;
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return NVFP4_ERR_SHAPE;
+  // Both projections get qmm's full checks (pointers, alignment, grid).
+  QmmPlan pg, pu;
+  int st = qmm_plan(x, dtype, M, K, F, w_gate, s_gate, gs_gate, 1, NVFP4_ROUTE_AUTO, out, &pg);
+  if (st != NVFP4_OK) return st;
+  st = qmm_plan(x, dtype, M, K, F, w_up, s_up, gs_up, 1, NVFP4_ROUTE_AUTO, out, &pu);
+  if (st != NVFP4_OK) return st;
+  if (pg.kind == QmmPlan::kNothing) return NVFP4_OK;
+  if (pg.kind == QmmPlan::kZeroFill) {   // K == 0: act(0) * 0 = 0 for every activation
+    nvfp4host::launch_fill_zero(out, M * F * dtype_size(dtype), stream);
+    return launched();
+  }
+  if (need == 0) {
+    if (!aligned(s_gate, 4) || !aligned(s_up, 4)) return NVFP4_ERR_ALIGN;
+    if (nvfp4host::gemm_glu_tiles(M, F) + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    nvfp4host::launch_gemm_glu(x, M, K, F, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, (int)act, out, stream);
+    return launched();
+  }
+  if (workspace_bytes < need) return NVFP4_ERR_SHAPE;
+  if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  const int64_t ds = dtype_size(dtype);
+  const int64_t wbytes = F * (K / 2), sbytes = F * (K / 16);
+  if (overlaps(workspace, workspace_bytes, out, M * F * ds) || overlaps(workspace, workspace_bytes, x, M * K * ds) ||
+      overlaps(workspace, workspace_bytes, w_gate, wbytes) || overlaps(workspace, workspace_bytes, w_up, wbytes) ||
+      overlaps(workspace, workspace_bytes, s_gate, sbytes) || overlaps(workspace, workspace_bytes, s_up, sbytes) ||
+      (gs_gate && overlaps(workspace, workspace_bytes, gs_gate, 4)) ||
+      (gs_up && overlaps(workspace, workspace_bytes, gs_up, 4)))
+    return NVFP4_ERR_SHAPE;
+  qmm_launch(pg, x, dtype, M, K, F, w_gate, s_gate, gs_gate, 1, workspace, stream);
+  qmm_launch(pu, x, dtype, M, K, F, w_up, s_up, gs_up, 1, out, stream);
+  nvfp4host::launch_glu_combine(workspace, out, M * F, dtype, (int)act, stream);
   return launched();
 }
 

@@ -17,6 +17,7 @@
 //    with both tiles decoded to float32 in LDS.
 #include <atomic>
 
+#include "glu_act.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.hpp"
 
@@ -301,14 +302,29 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
   }
 }
 
-// kSplit: the block multiplies slabs [split * per_split, ...) of its tile
-// only and writes the unscaled float32 partial to ws[split][M][N]; a second
-// kernel adds the partials in split order, applies g and rounds.
-template <bool kSplit>
+// What one block computes.
+//   kV3Plain: out tile = round(g * x W^T) over 256 weight rows.
+//   kV3Split: the block multiplies slabs [split * per_split, ...) of its tile
+//             only and writes the unscaled float32 partial to ws[split][M][N];
+//             a second kernel adds the partials in split order, applies g and
+//             rounds.
+//   kV3Glu:   the gated MLP projection.  N is the feature count F and a tile
+//             covers 128 features: the first 32-row MFMA tile of wavefront w
+//             holds gate rows f0 + 32w .. f0 + 32w + 31 (plane w, sc, gs) and
+//             the second the up rows of the same features (wu, scu, gsu), so
+//             each lane ends with the gate and up sums of the same outputs and
+//             the epilogue forms act(g_gate * gate) * (g_up * up) in float32.
+constexpr int kV3Plain = 0, kV3Split = 1, kV3Glu = 2;
+
+template <int kMode>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     const __bf16* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
     const float* __restrict__ gs, __bf16* __restrict__ out, int64_t M, int64_t K, int64_t N,
-    int64_t tiles_m, int64_t tiles_total, int64_t per_split, float* __restrict__ ws) {
+    int64_t tiles_m, int64_t tiles_total, int64_t per_split, float* __restrict__ ws,
+    const uint32_t* __restrict__ wu, const uint8_t* __restrict__ scu, const float* __restrict__ gsu,
+    int act) {
+  constexpr bool kSplit = kMode == kV3Split;
+  constexpr bool kGlu = kMode == kV3Glu;
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
   __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2];
   __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN];
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   const int64_t first_slab = split * per_split;
   if (tile >= tiles_total || first_slab >= all_slabs) return;  // whole block, before any barrier
   const int64_t m_blk = (tile % tiles_m) * kV3BM;
-  const int64_t n_blk = (tile / tiles_m) * kV3BN;
+  const int64_t n_blk = (tile / tiles_m) * (kGlu ? kV3BN / 2 : kV3BN);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -352,11 +368,23 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   for (int i = 0; i < 2; ++i) {
     const int q = (i * 4 + wave) * 64 + lane;
     const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);   // inverse of wslot
-    int64_t n = n_blk + r;
-    if (n >= N) n = N - 1;
-    src.w[i] = w + n * kw + 4 * half;
+    if constexpr (kGlu) {
+      // Tile row r = 64 w' + 32 a + l: feature n_blk + 32 w' + l of the gate
+      // (a = 0) or up (a = 1) plane.
+      int64_t f = n_blk + (r >> 6) * 32 + (r & 31);
+      if (f >= N) f = N - 1;
+      src.w[i] = (((r >> 5) & 1) ? wu : w) + f * kw + 4 * half;
+    } else {
+      int64_t n = n_blk + r;
+      if (n >= N) n = N - 1;
+      src.w[i] = w + n * kw + 4 * half;
+    }
   }
-  {
+  if constexpr (kGlu) {
+    int64_t f = n_blk + wave * 32 + (lane & 31);
+    if (f >= N) f = N - 1;
+    src.s = ((lane >> 5) ? scu : sc) + f * ks;
+  } else {
     int64_t n = n_blk + wave * 64 + lane;
     if (n >= N) n = N - 1;
     src.s = sc + n * ks;
@@ -426,6 +454,47 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
             for (int i = 0; i < 4; ++i)
               if (n + i < N) p[i] = acc[a][b][jj * 4 + i];
           }
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (kGlu) {
+    // Fragment (0, b) holds the gate sums and (1, b) the up sums of the same
+    // (feature, row) pairs, laid out as below; one output fragment per b.
+    const float gg = global_factor(gs, 0), gu = global_factor(gsu, 0);
+    const bool vec_ok = (N % 8) == 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int64_t m = m_blk + b * 32 + l32;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        uint32_t r0[2], r1[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          float v[4];
+          const int idx[4] = {(2 * p) * 4 + 2 * d, (2 * p) * 4 + 2 * d + 1, (2 * p + 1) * 4 + 2 * d,
+                              (2 * p + 1) * 4 + 2 * d + 1};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = glu_act(acc[0][b][idx[e]] * gg, act) * (acc[1][b][idx[e]] * gu);
+          r0[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+          r1[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+        }
+        const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r1[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(r0[1], r1[1], false, false);
+        const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        const int64_t f = n_blk + wave * 32 + 16 * p + 8 * h;
+        if (m >= M) continue;
+        __bf16* q = out + m * N + f;
+        if (vec_ok && f + 7 < N) {
+          *reinterpret_cast<uint4*>(q) = v;
+        } else {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (f + i < N) q[i] = __builtin_bit_cast(__bf16, (uint16_t)(wv[i / 2] >> (16 * (i % 2))));
         }
       }
     }
@@ -655,9 +724,9 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
       const int64_t nslabs = K / kV3BK;
       const int64_t per = (nslabs + sp - 1) / sp;
       const int64_t grid = (tiles * sp + 7) / 8 * 8;
-      gemm_mfma_v3_kernel<true><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+      gemm_mfma_v3_kernel<kV3Split><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
           static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, per,
-          static_cast<float*>(ws));
+          static_cast<float*>(ws), nullptr, nullptr, nullptr, 0);
       const int64_t MN = M * N;
       int64_t rgrid = (MN / 4 + 255) / 256;
       if (rgrid > 4096) rgrid = 4096;
@@ -667,8 +736,9 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
       return;
     }
     const int64_t grid = (tiles + 7) / 8 * 8;
-    gemm_mfma_v3_kernel<false><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-        static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, 0, nullptr);
+    gemm_mfma_v3_kernel<kV3Plain><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+        static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, 0, nullptr,
+        nullptr, nullptr, nullptr, 0);
     return;
   }
   const int64_t tiles_m = (M + kBM - 1) / kBM;
@@ -677,6 +747,21 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
   const int64_t grid = (tiles + 7) / 8 * 8;
   gemm_mfma_kernel<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
       static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
+}
+
+void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint32_t* w_gate,
+                     const uint8_t* s_gate, const float* gs_gate, const uint32_t* w_up, const uint8_t* s_up,
+                     const float* gs_up, int act, void* out, hipStream_t s) {
+  const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
+  const int64_t tiles = tiles_m * ((F + kV3BN / 2 - 1) / (kV3BN / 2));
+  const int64_t grid = (tiles + 7) / 8 * 8;
+  gemm_mfma_v3_kernel<kV3Glu><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+      static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, tiles, 0,
+      nullptr, w_up, s_up, gs_up, act);
+}
+
+int64_t gemm_glu_tiles(int64_t M, int64_t F) {
+  return ((M + kV3BM - 1) / kV3BM) * ((F + kV3BN / 2 - 1) / (kV3BN / 2));
 }
 
 int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {

@@ -55,6 +55,16 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
 // Workspace the split GEMM wants for this shape on the current device (0:
 // no split).
 int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+// Gated MLP projection as one MFMA GEMM: bf16 activations, transposed gate
+// and up planes [F, K/8] with K % 64 == 0 and 4-byte aligned scale planes;
+// a tile holds 128 features of both planes.
+void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint32_t* w_gate,
+                     const uint8_t* s_gate, const float* gs_gate, const uint32_t* w_up, const uint8_t* s_up,
+                     const float* gs_up, int act, void* out, hipStream_t s);
+// Blocks launch_gemm_glu runs for these sizes (before rounding to XCDs).
+int64_t gemm_glu_tiles(int64_t M, int64_t F);
+// out[i] = act(gate[i]) * out[i] over n elements of dtype dt.
+void launch_glu_combine(const void* gate, void* out, int64_t n, nvfp4_dtype_t dt, int act, hipStream_t s);
 // Generic float32-accumulating GEMM for any dtype and either plane layout.
 void launch_gemm_generic(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
                          const uint32_t* w, const uint8_t* sc, const float* gs, int transpose,

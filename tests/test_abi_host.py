@@ -39,6 +39,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_ws",
                  "nvfp4_qmm_workspace_size", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
+                 "nvfp4_qmm_glu", "nvfp4_qmm_glu_workspace_size",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
         assert want in names
 
@@ -117,6 +118,66 @@ def test_qmm_workspace_size_and_validation(lib):
     assert qws(*args(ws=None, nb=16)) == SHAPE
     assert qws(*args(ws=MISALIGNED)) == ALIGN
     assert qws(*args(x=None)) == NULLPTR
+
+
+def glu(lib, x=FAKE, dt=BF16, M=300, K=64, F=32, wg=FAKE, sg=FAKE, gg=None, wu=FAKE, su=FAKE, gu=None, act=0,
+        ws=None, nb=0, out=FAKE):
+    return lib.nvfp4_qmm_glu(x, dt, M, K, F, wg, sg, gg, wu, su, gu, act, ws, nb, out, None)
+
+
+def test_qmm_glu_workspace_size_and_validation(lib):
+    wsz = lib.nvfp4_qmm_glu_workspace_size
+    # the fused kernel (bf16, K % 64 == 0, GEMM-route sizes) needs no workspace
+    assert wsz(2048, 5376, 21504, BF16) == 0
+    assert wsz(300, 64, 32, BF16) == 0
+    # otherwise gate goes to a workspace of M * F elements, rounded up to 256 bytes
+    assert wsz(1, 5376, 21504, BF16) == 21504 * 2                  # qmv-route sizes
+    assert wsz(300, 48, 40, BF16) == (300 * 40 * 2 + 255) // 256 * 256   # K % 64 != 0
+    assert wsz(300, 64, 32, F32) == 300 * 32 * 4
+    assert wsz(300, 64, 32, F16) == 300 * 32 * 2
+    assert wsz(0, 64, 32, F32) == 0 and wsz(3, 0, 32, F32) == 0
+    assert wsz(3, 24, 32, BF16) == SHAPE
+    assert wsz(-1, 64, 32, BF16) == SHAPE
+    assert wsz(3, 64, 32, 9) == DTYPE
+    assert wsz(1 << 40, 64, 1 << 40, BF16) == SHAPE
+    # validation before any launch
+    assert glu(lib, x=None) == NULLPTR
+    assert glu(lib, wg=None) == NULLPTR
+    assert glu(lib, su=None) == NULLPTR
+    assert glu(lib, out=None) == NULLPTR
+    assert glu(lib, K=24) == SHAPE
+    assert glu(lib, act=3) == SHAPE
+    assert glu(lib, act=-1) == SHAPE
+    assert glu(lib, dt=7) == DTYPE
+    assert glu(lib, nb=-1) == SHAPE
+    assert glu(lib, nb=64, ws=None) == SHAPE
+    assert glu(lib, wu=MISALIGNED) == ALIGN
+    assert glu(lib, gu=P(0x100002)) == ALIGN
+    assert glu(lib, sg=P(0x100002)) == ALIGN         # the fused kernel reads scale words
+    assert glu(lib, su=P(0x100002)) == ALIGN
+    # the separate-projection case needs its workspace
+    assert glu(lib, dt=F32) == SHAPE                 # no workspace given
+    assert glu(lib, dt=F32, ws=P(0x200000), nb=300 * 32 * 4 - 1) == SHAPE
+    assert glu(lib, dt=F32, ws=P(0x200004), nb=300 * 32 * 4) == ALIGN
+    assert glu(lib, dt=F32, ws=P(0x100000), nb=300 * 32 * 4) == SHAPE   # overlaps the inputs
+    # empty outputs succeed without launching
+    assert glu(lib, M=0, x=None, wg=None, sg=None, wu=None, su=None, out=None) == OK
+    assert glu(lib, F=0, x=None, wg=None, sg=None, wu=None, su=None, out=None) == OK
+
+
+def test_binding_qmm_glu_checks_before_the_gpu():
+    w = torch.zeros(32, 8, dtype=torch.int32)
+    s = torch.zeros(32, 4, dtype=torch.uint8)
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nv.qmm_glu(x, w, s, None, w[:16], s[:16], None)
+    with pytest.raises(ValueError):
+        nv.qmm_glu(x[:, :32], w, s, None, w, s, None)
+    with pytest.raises(ValueError):
+        nv.qmm_glu(x, w, s, None, w, s, None, act="relu")
+    with pytest.raises(ValueError):
+        nv.qmm_glu(x, w, s, torch.ones(2), w, s, None)
+    assert nv.GLU_ACTIVATIONS == ("gelu_tanh", "gelu", "silu")
 
 
 def qmm_b(lib, x=FAKE, dt=BF16, XB=3, B=3, M=4, K=64, N=32, w=FAKE, s=FAKE, gs=None, tr=1, route=0,

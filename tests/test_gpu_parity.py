@@ -492,6 +492,109 @@ def test_prefill_gemm_full_size_sampled():
     assert oracle.relative_error(got, ref) <= TOL[torch.bfloat16]
 
 
+# ----------------------------------------------------------------------------
+# gated MLP projection
+# ----------------------------------------------------------------------------
+
+GLU_CODES = (0x08, 0x28)   # block scales 2^-6 .. 2^-2: gate sums of unit size, where the activations bend
+
+
+def glu_planes(seed, M, K, F, gs=(True, True)):
+    g = synth.dense_case(seed, M, K, F, with_gs=gs[0], code_range=GLU_CODES)
+    u = synth.dense_case(seed + 1, M, K, F, with_gs=gs[1], code_range=GLU_CODES)
+    return g, u
+
+
+def gs_arg(c):
+    return None if c.gs is None else f32(c.gs)
+
+
+def gs_ref(c):
+    return None if c.gs is None else c.gs[0]
+
+
+def run_glu(g, u, dtype, act, guard=True):
+    x_t, x_ref = activations(g.x, dtype)
+    ref = oracle.qmm_glu(x_ref, g.w, g.scales, gs_ref(g), u.w, u.scales, gs_ref(u), act)
+    out = check = None
+    if guard:
+        out, check = guarded((g.M, g.N), dtype)
+    out = nv.qmm_glu(x_t, words(g.w), u8(g.scales), gs_arg(g), words(u.w), u8(u.scales), gs_arg(u),
+                     act=act, out=out)
+    torch.cuda.synchronize()
+    if check:
+        check()
+    return out, ref
+
+
+def glu_workspace(M, K, F, dtype):
+    code = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}[dtype]
+    return int(nv.load_library().nvfp4_qmm_glu_workspace_size(M, K, F, code))
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu", "silu"])
+@pytest.mark.parametrize("shape", [(300, 1024, 1000), (513, 320, 257), (65, 64, 128), (256, 4096, 384)])
+def test_qmm_glu_fused_kernel(shape, act):
+    """bf16 with K % 64 == 0 at GEMM sizes runs the one fused kernel (no
+    workspace): several row and feature tiles, a ragged feature count (257,
+    and 1000 = 7 full tiles + 104), one slab (K = 64), rows past a tile."""
+    M, K, F = shape
+    assert glu_workspace(M, K, F, torch.bfloat16) == 0
+    g, u = glu_planes(6100 + M + K + F, M, K, F)
+    out, ref = run_glu(g, u, torch.bfloat16, act)
+    assert rel(out, ref) <= TOL[torch.bfloat16], (shape, act)
+
+
+@pytest.mark.parametrize("gs", [(False, False), (True, False), (False, True)])
+def test_qmm_glu_fused_global_scales(gs):
+    """Each plane's global scale applies to its own projection only."""
+    g, u = glu_planes(6200, 300, 512, 272, gs=gs)
+    out, ref = run_glu(g, u, torch.bfloat16, "gelu_tanh")
+    assert rel(out, ref) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(1, 512, 300), (3, 256, 200), (40, 512, 96), (300, 48, 40), (70, 96, 64)])
+@pytest.mark.parametrize("act", ["gelu_tanh", "silu"])
+def test_qmm_glu_separate_projections(shape, dtype, act):
+    """Every case the fused kernel does not take: the projections run through
+    qmm's own routes (qmv at M = 1 and 3, the MFMA qmv at 40, the GEMMs at
+    300 with K = 48 and at 70 with K = 96) into a workspace, then combine."""
+    M, K, F = shape
+    fused = dtype == torch.bfloat16 and K % 64 == 0 and nv.select_route(M, K, F) == "gemm"
+    assert (glu_workspace(M, K, F, dtype) == 0) == fused
+    g, u = glu_planes(6300 + M + K + F, M, K, F)
+    out, ref = run_glu(g, u, dtype, act)
+    assert rel(out, ref) <= TOL[dtype], (shape, dtype, act)
+
+
+def test_qmm_glu_zero_k_and_empty():
+    g, u = glu_planes(6400, 5, 0, 32)
+    out, ref = run_glu(g, u, torch.bfloat16, "gelu")
+    assert np.all(host(out) == 0.0)
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros(32, 8, dtype=torch.int32, device=DEV)
+    s = torch.zeros(32, 4, dtype=torch.uint8, device=DEV)
+    assert nv.qmm_glu(x, w, s, None, w, s, None).shape == (0, 32)
+
+
+def test_qmm_glu_full_size_sampled():
+    """The prefill MLP's gate/up shape, M=2048, K=5376, F=21504, bf16, through
+    the fused kernel that is timed; sampled rows and features against the
+    oracle (features are independent rows of both planes)."""
+    M, K, F = 2048, 5376, 21504
+    assert glu_workspace(M, K, F, torch.bfloat16) == 0
+    g, u = glu_planes(6500, M, K, F)
+    x_t, x_ref = activations(g.x, torch.bfloat16)
+    out = nv.qmm_glu(x_t, words(g.w), u8(g.scales), f32(g.gs), words(u.w), u8(u.scales), f32(u.gs))
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [1, 255, 256, 2047]]))
+    feats = np.unique(np.concatenate([np.arange(0, F, 61), [127, 128, 21503]]))
+    ref = oracle.qmm_glu(x_ref[rows], g.w[feats], g.scales[feats], g.gs[0], u.w[feats], u.scales[feats],
+                         u.gs[0], "gelu_tanh")
+    got = host(out)[np.ix_(rows, feats)]
+    assert oracle.relative_error(got, ref) <= TOL[torch.bfloat16]
+
+
 def test_global_scale_2688_is_identity():
     case = synth.dense_case(3400, 4, 256, 96, with_gs=False)
     x_t, _ = activations(case.x, torch.float32)
