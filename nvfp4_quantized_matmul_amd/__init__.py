@@ -75,6 +75,7 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_qmm_workspace_size": [i64, i64, i64, c_int, c_int, c_int],
         "nvfp4_qmm_glu": [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, c_int, vp, i64, vp, vp],
         "nvfp4_qmm_glu_workspace_size": [i64, i64, i64, c_int],
+        "nvfp4_stream_read": [vp, i64, i64, vp, vp],
         "nvfp4_gather_qmm": [vp, c_int, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, i64, c_int, vp, vp],
         "nvfp4_select_route": [i64, i64, i64, c_int, c_int],
         "nvfp4_qmv_max_rows": [],

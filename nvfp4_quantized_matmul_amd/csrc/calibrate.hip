@@ -1,0 +1,37 @@
+// Measurement aid: a plain streaming read, used to measure the rate a
+// kernel can reach on this device for a given byte count (the context for
+// the decode kernel's HBM roofline).  It reads every 16-byte chunk once in a
+// grid-stride loop and folds the data into one word per lane; a word is
+// stored only if the fold hits a sentinel, so the loads cannot be elided
+// and nothing is written in practice.
+#include "nvfp4_internal.hpp"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ p, int64_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+}  // namespace
+
+extern "C" int nvfp4_stream_read(const void* p, int64_t bytes, int64_t blocks, uint32_t* sink,
+                                 hipStream_t stream) {
+  if (bytes < 0 || bytes % 16 != 0 || blocks < 1 || blocks > nvfp4host::kMaxGridX) return NVFP4_ERR_SHAPE;
+  if (bytes == 0) return NVFP4_OK;
+  if (!p || !sink) return NVFP4_ERR_NULLPTR;
+  if ((reinterpret_cast<uintptr_t>(p) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
+    return NVFP4_ERR_ALIGN;
+  stream_read_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(static_cast<const uint4*>(p),
+                                                                          bytes / 16, sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}

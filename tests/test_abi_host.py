@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_ws",
                  "nvfp4_qmm_workspace_size", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
-                 "nvfp4_qmm_glu", "nvfp4_qmm_glu_workspace_size",
+                 "nvfp4_qmm_glu", "nvfp4_qmm_glu_workspace_size", "nvfp4_stream_read",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
         assert want in names
 
@@ -163,6 +163,18 @@ def test_qmm_glu_workspace_size_and_validation(lib):
     # empty outputs succeed without launching
     assert glu(lib, M=0, x=None, wg=None, sg=None, wu=None, su=None, out=None) == OK
     assert glu(lib, F=0, x=None, wg=None, sg=None, wu=None, su=None, out=None) == OK
+
+
+def test_stream_read_validation(lib):
+    sr = lib.nvfp4_stream_read
+    assert sr(FAKE, 24, 64, FAKE, None) == SHAPE       # not a multiple of 16
+    assert sr(FAKE, -16, 64, FAKE, None) == SHAPE
+    assert sr(FAKE, 1024, 0, FAKE, None) == SHAPE
+    assert sr(None, 1024, 64, FAKE, None) == NULLPTR
+    assert sr(FAKE, 1024, 64, None, None) == NULLPTR
+    assert sr(P(0x100008), 1024, 64, FAKE, None) == ALIGN
+    assert sr(FAKE, 1024, 64, P(0x100002), None) == ALIGN
+    assert sr(None, 0, 64, None, None) == OK
 
 
 def test_binding_qmm_glu_checks_before_the_gpu():

@@ -862,3 +862,25 @@ def test_gather_random_sweep(i, tokens, E, N, K, top_k, sort, M, dtype):
     out, ref = run_gather(case, dtype, guard=True)
     assert oracle.relative_error(host(out), ref) <= TOL[dtype], (tokens, E, N, K, top_k, M, dtype)
     assert_zero_rows(out, case.rhs, case.lhs, E, tokens)
+
+
+# ----------------------------------------------------------------------------
+# measurement aid
+# ----------------------------------------------------------------------------
+
+def test_stream_read_reads_every_chunk_and_writes_only_on_the_sentinel():
+    lib = nv.load_library()
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    zeros = torch.zeros(1 << 20, dtype=torch.int32, device=DEV)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.nvfp4_stream_read(ctypes.c_void_p(zeros.data_ptr()), zeros.numel() * 4, 2048,
+                                 ctypes.c_void_p(sink.data_ptr()), st) == 0
+    torch.cuda.synchronize()
+    assert int(sink[0]) == 0
+    # the last 16-byte chunk folds to the sentinel: its lane stores it
+    last = torch.zeros(1 << 20, dtype=torch.int32, device=DEV)
+    last[-4] = int(np.array(0x9E3779B9, dtype=np.uint32).view(np.int32))
+    assert lib.nvfp4_stream_read(ctypes.c_void_p(last.data_ptr()), last.numel() * 4, 2048,
+                                 ctypes.c_void_p(sink.data_ptr()), st) == 0
+    torch.cuda.synchronize()
+    assert np.uint32(int(sink[0]) & 0xFFFFFFFF) == np.uint32(0x9E3779B9)
