@@ -884,3 +884,80 @@ def test_stream_read_reads_every_chunk_and_writes_only_on_the_sentinel():
                                  ctypes.c_void_p(sink.data_ptr()), st) == 0
     torch.cuda.synchronize()
     assert np.uint32(int(sink[0]) & 0xFFFFFFFF) == np.uint32(0x9E3779B9)
+
+
+# ----------------------------------------------------------------------------
+# HIP graph capture
+# ----------------------------------------------------------------------------
+
+def test_graph_capture_replays_match_eager():
+    """Every entry point's kernels captured in one HIP graph (decode qmv,
+    multi-row MFMA qmv, GEMM, split-K GEMM with its workspace, sorted and
+    unsorted gather, fused and separate-projection gated projection,
+    quantize with its zero fill and atomic maximum) and replayed three times
+    on new inputs, with eager work and synchronizations in between: each
+    replay equals the eager result bit for bit (all reductions here run in a
+    fixed order)."""
+    g = synth.rng(8100)
+    K, N = 512, 768
+    w = words(synth.packed_words(g, (N, K // 8)))
+    s = u8(synth.scale_codes(g, (N, K // 16), (0x08, 0x30)))
+    gs = f32(synth.global_scales(g, 1))
+    wu = words(synth.packed_words(g, (N, K // 8)))
+    su = u8(synth.scale_codes(g, (N, K // 16), (0x08, 0x30)))
+    Ks, Ns = 2048, 4096
+    ws_ = words(synth.packed_words(g, (Ns, Ks // 8)))
+    ss_ = u8(synth.scale_codes(g, (Ns, Ks // 16), (0x08, 0x30)))
+    assert int(nv.load_library().nvfp4_qmm_workspace_size(96, Ks, Ns, 1, 1, 0)) > 0   # split-K applies
+    ge = synth.gather_case(8101, tokens=24, E=6, N=256, K=512, top_k=2, sort=True, with_gs=True)
+    gu = synth.gather_case(8102, tokens=5, E=6, N=256, K=512, top_k=2, sort=False, with_gs=True)
+    gw, gsc, ggs = words(ge.w), u8(ge.scales), f32(ge.gs)
+    rs, ls = i32(ge.rhs), i32(ge.lhs)
+    ru, lu = i32(gu.rhs), i32(gu.lhs)
+    bufs = {
+        "x1": torch.empty(1, K, dtype=torch.bfloat16, device=DEV),
+        "x16": torch.empty(16, K, dtype=torch.bfloat16, device=DEV),
+        "x300": torch.empty(300, K, dtype=torch.bfloat16, device=DEV),
+        "x3f": torch.empty(3, K, dtype=torch.float32, device=DEV),
+        "xs": torch.empty(96, Ks, dtype=torch.bfloat16, device=DEV),
+        "xg": torch.empty(24, 1, 512, dtype=torch.bfloat16, device=DEV),
+        "xgu": torch.empty(5, 1, 512, dtype=torch.bfloat16, device=DEV),
+        "dense": torch.empty(64, 256, dtype=torch.bfloat16, device=DEV),
+    }
+
+    def fill(seed):
+        gg = synth.rng(seed)
+        for name, t in bufs.items():
+            t.copy_(torch.from_numpy(synth.activations(gg, tuple(t.shape))).to(t.dtype))
+
+    def run():
+        return [
+            nv.qmm(bufs["x1"], w, s, gs),
+            nv.qmm(bufs["x16"], w, s, gs),
+            nv.qmm(bufs["x300"], w, s, gs),
+            nv.qmm(bufs["xs"], ws_, ss_, gs),
+            nv.gather_qmm(bufs["xg"], gw, gsc, rs, ls, ggs, sorted_indices=True),
+            nv.gather_qmm(bufs["xgu"], gw, gsc, ru, lu, ggs),
+            nv.qmm_glu(bufs["x300"], w, s, gs, wu, su, None, act="gelu_tanh"),
+            nv.qmm_glu(bufs["x3f"], w, s, gs, wu, su, gs, act="silu"),
+        ] + list(nv.quantize(bufs["dense"]))
+
+    fill(1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = run()
+    for rep in range(3):
+        fill(100 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = run()
+        torch.cuda.synchronize()
+        for i, (c, e) in enumerate(zip(captured, eager)):
+            assert torch.equal(c, e), (rep, i)
