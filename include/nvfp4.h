@@ -234,7 +234,10 @@ int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
  * output dtype).  nvfp4_qmm_glu_workspace_size gives the bytes that case needs
  * (0 for the fused case); a smaller workspace returns NVFP4_ERR_SHAPE.  The
  * workspace must not overlap any other argument; its contents are scratch.
- * Errors as nvfp4_qmm; an unknown act returns NVFP4_ERR_SHAPE.
+ * Errors as nvfp4_qmm; an unknown act returns NVFP4_ERR_SHAPE; the fused
+ * kernel reads scale bytes four at a time, so there both scale planes must
+ * be 4-byte aligned (NVFP4_ERR_ALIGN otherwise).  Calls on one stream with
+ * one workspace are ordered; concurrent calls need separate workspaces.
  */
 int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t F,
                   const uint32_t* w_gate, const uint8_t* s_gate, const float* gs_gate,
