@@ -148,20 +148,25 @@ class MlpGateUp:
     gate and up planes of launch c are the weight copies 2c and 2c+1."""
     M, K, F = 2048, 5376, 21504
 
-    def __init__(self, pre: Prefill, decode: Decode):
+    def __init__(self, pre: Prefill, decode: Decode, workspace: bool = True):
         self.x = pre.x
         self.w, self.s, self.gs = decode.w, decode.s, decode.gs
         self.out = torch.empty((self.M, self.F), dtype=torch.bfloat16, device=DEV)
         self.lib = decode.lib
         self.flops = 2 * 2.0 * self.M * self.K * self.F
         self.fn = self.lib.nvfp4_qmm_glu
+        # the caller-owned workspace that lets the last partial round of tiles
+        # split along K (what the Python binding passes)
+        nbytes = int(self.lib.nvfp4_qmm_glu_workspace_size(self.M, self.K, self.F, BF16)) if workspace else 0
+        self.ws_bytes = nbytes
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV) if nbytes > 0 else None
 
     def prebuilt(self):
         st = stream_ptr()
         pairs = len(self.w) // 2
         return [(P(self.x), BF16, self.M, self.K, self.F, P(self.w[2 * c]), P(self.s[2 * c]), P(self.gs),
-                 P(self.w[2 * c + 1]), P(self.s[2 * c + 1]), P(self.gs), 0, None, 0, P(self.out), st)
-                for c in range(pairs)]
+                 P(self.w[2 * c + 1]), P(self.s[2 * c + 1]), P(self.gs), 0, P(self.ws), self.ws_bytes,
+                 P(self.out), st) for c in range(pairs)]
 
 
 class MultiRow:
@@ -572,6 +577,9 @@ def main():
     mlp = MlpGateUp(pre, dec)
     gdur = eager_launch_us(mlp, 16, warmup=8)
     gtf = mlp.flops / (gdur["mean_us"] * 1e-6) / 1e12
+    mlp_nows = MlpGateUp(pre, dec, workspace=False)
+    nows_us = eager_launch_us(mlp_nows, 16, warmup=4)["mean_us"]
+    del mlp_nows
     # the same projection unfused, for comparison: two library qmm launches
     # (gate, up) and the activation and product as torch elementwise ops
     gate_t = torch.empty_like(mlp.out)
@@ -645,11 +653,15 @@ def main():
                                 "roofline": {"bound": "mfma", "achieved": round(gtf, 2), "peak": BF16_PEAK_TFLOPS,
                                              "unit": "TFLOP/s", "frac": round(gtf / BF16_PEAK_TFLOPS, 4),
                                              "kernel": "gemm_mfma_v3_kernel<glu>", "kernel_duration": gdur},
+                                "workspace_bytes": mlp.ws_bytes,
+                                "no_workspace_us": round(nows_us, 2),
                                 "separate_qmm_pair_us": round(2 * pdur["mean_us"], 2),
                                 "unfused_us": round(unfused_us, 2),
-                                "note": "one fused launch; separate_qmm_pair_us = two prefill qmm launches of the "
-                                        "same planes; unfused_us = those two launches plus the activation and "
-                                        "product as torch elementwise ops (measurement only)"},
+                                "note": "the fused kernel with its workspace (the last partial round of tiles "
+                                        "split along K, three launches per step); no_workspace_us = the same call "
+                                        "without one (one launch); separate_qmm_pair_us = two prefill qmm "
+                                        "launches of the same planes; unfused_us = those two launches plus the "
+                                        "activation and product as torch elementwise ops (measurement only)"},
         "multirow_m16": {"workload": "multirow_qmv_m16_k4096_n14336_bf16", "value": round(mgbs, 2),
                          "unit": "GB/s", "frac_hbm": round(mgbs / HBM_PEAK_GBS, 4),
                          "kernel": "skinny_kernel<bf16,1,16>", "kernel_duration": mdur, "bytes": mr.bytes},

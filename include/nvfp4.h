@@ -228,12 +228,15 @@ int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
  * bf16 activations with K % 64 == 0, at sizes where nvfp4_qmm takes its GEMM
  * route, run as ONE kernel: each tile multiplies gate and up rows of the same
  * features and applies g, the activation and the product to the float32 sums
- * before the single rounding to bf16; no workspace is used.  Every other case
- * runs both projections through nvfp4_qmm's kernels into `workspace` and
- * `out` and then combines them (one extra rounding of each projection to the
- * output dtype).  nvfp4_qmm_glu_workspace_size gives the bytes that case needs
- * (0 for the fused case); a smaller workspace returns NVFP4_ERR_SHAPE.  The
- * workspace must not overlap any other argument; its contents are scratch.
+ * before the single rounding to bf16.  There the workspace is optional: with
+ * at least nvfp4_qmm_glu_workspace_size bytes, the last, partial round of
+ * tiles is split along K into float32 partials that a second kernel adds (in
+ * a fixed order) before the same epilogue; with less, or none, no split.
+ * Every other case runs both projections through nvfp4_qmm's kernels into
+ * `workspace` and `out` and then combines them (one extra rounding of each
+ * projection to the output dtype); a workspace smaller than the queried size
+ * returns NVFP4_ERR_SHAPE there.  The workspace must be 16-byte aligned and
+ * must not overlap any other argument; its contents are scratch.
  * Errors as nvfp4_qmm; an unknown act returns NVFP4_ERR_SHAPE; the fused
  * kernel reads scale bytes four at a time, so there both scale planes must
  * be 4-byte aligned (NVFP4_ERR_ALIGN otherwise).  Calls on one stream with
@@ -245,9 +248,10 @@ int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int6
                   nvfp4_act_t act, void* workspace, int64_t workspace_bytes, void* out,
                   hipStream_t stream);
 
-/* Workspace bytes nvfp4_qmm_glu needs for these sizes (host only): 0 when it
- * runs the fused kernel, M * F * sizeof(dtype) rounded up to 256 otherwise;
- * a negative status for invalid sizes or dtype. */
+/* Workspace bytes nvfp4_qmm_glu wants for these sizes on the current device
+ * (host only): for the fused kernel the bytes of its tail split (0 when it
+ * would not split), M * F * sizeof(dtype) rounded up to 256 otherwise; a
+ * negative status for invalid sizes or dtype. */
 int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtype_t dtype);
 
 /*

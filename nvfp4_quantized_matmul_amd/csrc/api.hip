@@ -259,7 +259,8 @@ int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtyp
   if (!mul_ok(M, K, &t) || !mul_ok(K, F, &t) || !mul_ok(M, F, &mf) || !mul_ok(mf, dtype_size(dtype), &t) ||
       t > INT64_MAX - 256)
     return NVFP4_ERR_SHAPE;
-  if (M == 0 || F == 0 || K == 0 || glu_fused(M, K, F, dtype)) return 0;
+  if (M == 0 || F == 0 || K == 0) return 0;
+  if (glu_fused(M, K, F, dtype)) return nvfp4host::gemm_glu_workspace_bytes(M, K, F);
   return (t + 255) / 256 * 256;
 }
 
@@ -282,22 +283,31 @@ int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int6
     nvfp4host::launch_fill_zero(out, M * F * dtype_size(dtype), stream);
     return launched();
   }
-  if (need == 0) {
+  const int64_t ds = dtype_size(dtype);
+  const int64_t wbytes = F * (K / 2), sbytes = F * (K / 16);
+  const bool ws_overlaps =
+      workspace && (overlaps(workspace, workspace_bytes, out, M * F * ds) ||
+                    overlaps(workspace, workspace_bytes, x, M * K * ds) ||
+                    overlaps(workspace, workspace_bytes, w_gate, wbytes) ||
+                    overlaps(workspace, workspace_bytes, w_up, wbytes) ||
+                    overlaps(workspace, workspace_bytes, s_gate, sbytes) ||
+                    overlaps(workspace, workspace_bytes, s_up, sbytes) ||
+                    (gs_gate && overlaps(workspace, workspace_bytes, gs_gate, 4)) ||
+                    (gs_up && overlaps(workspace, workspace_bytes, gs_up, 4)));
+  if (glu_fused(M, K, F, dtype)) {
+    // The fused kernel; a workspace is optional (it splits the last,
+    // partial round of tiles along K when large enough).
     if (!aligned(s_gate, 4) || !aligned(s_up, 4)) return NVFP4_ERR_ALIGN;
-    if (nvfp4host::gemm_glu_tiles(M, F) + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
-    nvfp4host::launch_gemm_glu(x, M, K, F, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, (int)act, out, stream);
+    if (workspace && !aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+    if (ws_overlaps) return NVFP4_ERR_SHAPE;
+    if (nvfp4host::gemm_glu_tiles(M, F) * 9 + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    nvfp4host::launch_gemm_glu(x, M, K, F, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, (int)act, out, stream,
+                               workspace, workspace_bytes);
     return launched();
   }
   if (workspace_bytes < need) return NVFP4_ERR_SHAPE;
   if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
-  const int64_t ds = dtype_size(dtype);
-  const int64_t wbytes = F * (K / 2), sbytes = F * (K / 16);
-  if (overlaps(workspace, workspace_bytes, out, M * F * ds) || overlaps(workspace, workspace_bytes, x, M * K * ds) ||
-      overlaps(workspace, workspace_bytes, w_gate, wbytes) || overlaps(workspace, workspace_bytes, w_up, wbytes) ||
-      overlaps(workspace, workspace_bytes, s_gate, sbytes) || overlaps(workspace, workspace_bytes, s_up, sbytes) ||
-      (gs_gate && overlaps(workspace, workspace_bytes, gs_gate, 4)) ||
-      (gs_up && overlaps(workspace, workspace_bytes, gs_up, 4)))
-    return NVFP4_ERR_SHAPE;
+  if (ws_overlaps) return NVFP4_ERR_SHAPE;
   qmm_launch(pg, x, dtype, M, K, F, w_gate, s_gate, gs_gate, 1, workspace, stream);
   qmm_launch(pu, x, dtype, M, K, F, w_up, s_up, gs_up, 1, out, stream);
   nvfp4host::launch_glu_combine(workspace, out, M * F, dtype, (int)act, stream);

@@ -314,7 +314,12 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
 //             the second the up rows of the same features (wu, scu, gsu), so
 //             each lane ends with the gate and up sums of the same outputs and
 //             the epilogue forms act(g_gate * gate) * (g_up * up) in float32.
-constexpr int kV3Plain = 0, kV3Split = 1, kV3Glu = 2;
+//   kV3GluSplit: tiles tile0 .. tile0 + tiles_total - 1 of the gated
+//             projection, each shared by `splits` blocks along K as in
+//             kV3Split; block (split, t) writes its unscaled float32 gate and
+//             up sums to ws[split][t][256 rows][256 tile rows], and
+//             glu_tail_reduce_kernel finishes them.
+constexpr int kV3Plain = 0, kV3Split = 1, kV3Glu = 2, kV3GluSplit = 3;
 
 template <int kMode>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
@@ -322,9 +327,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     const float* __restrict__ gs, __bf16* __restrict__ out, int64_t M, int64_t K, int64_t N,
     int64_t tiles_m, int64_t tiles_total, int64_t per_split, float* __restrict__ ws,
     const uint32_t* __restrict__ wu, const uint8_t* __restrict__ scu, const float* __restrict__ gsu,
-    int act) {
-  constexpr bool kSplit = kMode == kV3Split;
-  constexpr bool kGlu = kMode == kV3Glu;
+    int act, int64_t tile0) {
+  constexpr bool kSplit = kMode == kV3Split || kMode == kV3GluSplit;
+  constexpr bool kGlu = kMode == kV3Glu || kMode == kV3GluSplit;
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
   __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2];
   __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN];
@@ -339,9 +344,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   const int64_t logical = ((int64_t)blockIdx.x % 8) * per_xcd + (int64_t)blockIdx.x / 8;
   const int64_t all_slabs = K / kV3BK;
   const int64_t split = kSplit ? logical / tiles_total : 0;
-  const int64_t tile = kSplit ? logical - split * tiles_total : logical;
+  const int64_t tloc = kSplit ? logical - split * tiles_total : logical;
   const int64_t first_slab = split * per_split;
-  if (tile >= tiles_total || first_slab >= all_slabs) return;  // whole block, before any barrier
+  if (tloc >= tiles_total || first_slab >= all_slabs) return;  // whole block, before any barrier
+  const int64_t tile = tile0 + tloc;
   const int64_t m_blk = (tile % tiles_m) * kV3BM;
   const int64_t n_blk = (tile / tiles_m) * (kGlu ? kV3BN / 2 : kV3BN);
 
@@ -431,6 +437,21 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   wait_vmem(false);   // no load-to-LDS may land after the block ends
 #undef NVFP4_V3_STEP
 
+  if constexpr (kMode == kV3GluSplit) {
+    // Tile-local partial: fragment (a, b) holds C[n][m] with tile row
+    // n = 64 wave + 32a + 8jj + 4h + i and row m = 32b + l32; every row of the
+    // 256 x 256 slice is written (the reduction skips rows past M or F).
+    float* wsp = ws + ((split * tiles_total + tloc) << 16);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(wsp + (b * 32 + l32) * 256 + wave * 64 + a * 32 + jj * 8 + h * 4) =
+              make_float4(acc[a][b][jj * 4], acc[a][b][jj * 4 + 1], acc[a][b][jj * 4 + 2], acc[a][b][jj * 4 + 3]);
+    return;
+  }
   if constexpr (kSplit) {
     // Partial: fragment (a, b) holds C[n][m] with n = 8*jj + 4h + i, m =
     // l32; four consecutive n per jj go out as one 16-byte store.
@@ -572,6 +593,42 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 
 constexpr int kGT = 64;   // output tile edge
 constexpr int kGK = 16;   // k per stage (one scale block)
+
+// Finishes the K-split tail tiles of the gated projection: for each output
+// of tile tile0 + t, the gate and up sums are the partials of every split
+// added in split order; out = bf16(act(g_gate * gate) * (g_up * up)).  One
+// thread per four consecutive features (tile rows 64 w' + i and
+// 64 w' + 32 + i hold feature 32 w' + i of the gate and of the up plane).
+__global__ __launch_bounds__(256) void glu_tail_reduce_kernel(const float* __restrict__ ws, int64_t splits,
+                                                              int64_t ntiles, int64_t tile0, int64_t tiles_m,
+                                                              int64_t M, int64_t F, const float* __restrict__ gs,
+                                                              const float* __restrict__ gsu, int act,
+                                                              __bf16* __restrict__ out) {
+  const int64_t total = ntiles * 256 * 32;
+  const float gg = global_factor(gs, 0), gu = global_factor(gsu, 0);
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t t = idx / (256 * 32);
+    const int ml = (int)((idx / 32) % 256), f4 = (int)(idx % 32);
+    const int64_t tile = tile0 + t;
+    const int64_t m = (tile % tiles_m) * 256 + ml;
+    const int64_t f = (tile / tiles_m) * 128 + 4 * f4;
+    if (m >= M || f >= F) continue;
+    const int nl = 64 * (f4 >> 3) + 4 * (f4 & 7);
+    float4 ga = make_float4(0.0f, 0.0f, 0.0f, 0.0f), ua = ga;
+    for (int64_t sp = 0; sp < splits; ++sp) {
+      const float* base = ws + ((sp * ntiles + t) << 16) + ml * 256;
+      const float4 a = *reinterpret_cast<const float4*>(base + nl);
+      const float4 b = *reinterpret_cast<const float4*>(base + nl + 32);
+      ga.x += a.x; ga.y += a.y; ga.z += a.z; ga.w += a.w;
+      ua.x += b.x; ua.y += b.y; ua.z += b.z; ua.w += b.w;
+    }
+    const float gv[4] = {ga.x, ga.y, ga.z, ga.w}, uv[4] = {ua.x, ua.y, ua.z, ua.w};
+    __bf16* q = out + m * F + f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (f + i < F) q[i] = (__bf16)(glu_act(gv[i] * gg, act) * (uv[i] * gu));
+  }
+}
 
 template <typename TX, bool TRANS>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(const TX* __restrict__ x,
@@ -726,7 +783,7 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
       const int64_t grid = (tiles * sp + 7) / 8 * 8;
       gemm_mfma_v3_kernel<kV3Split><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
           static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, per,
-          static_cast<float*>(ws), nullptr, nullptr, nullptr, 0);
+          static_cast<float*>(ws), nullptr, nullptr, nullptr, 0, 0);
       const int64_t MN = M * N;
       int64_t rgrid = (MN / 4 + 255) / 256;
       if (rgrid > 4096) rgrid = 4096;
@@ -738,7 +795,7 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
     const int64_t grid = (tiles + 7) / 8 * 8;
     gemm_mfma_v3_kernel<kV3Plain><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
         static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, 0, nullptr,
-        nullptr, nullptr, nullptr, 0);
+        nullptr, nullptr, nullptr, 0, 0);
     return;
   }
   const int64_t tiles_m = (M + kBM - 1) / kBM;
@@ -749,15 +806,61 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
       static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
 }
 
+// K-split of the gated projection's last, partial round of tiles: with
+// `rem` tiles left over after whole rounds on the device's compute units,
+// each is shared by floor(cus / rem) blocks (at most 8, each at least 4 slabs
+// of K), so the last round takes a fraction of a tile's time; the float32
+// partials go through a workspace and a reduction.  0 splits: no split.
+void glu_tail_split(int64_t M, int64_t K, int64_t F, int64_t* tail_tiles, int64_t* splits) {
+  *tail_tiles = 0;
+  *splits = 0;
+  if (K % kV3BK != 0) return;
+  const int64_t tiles = gemm_glu_tiles(M, F);
+  const int64_t cus = device_cu_count();
+  const int64_t rem = tiles % cus;
+  if (rem == 0) return;
+  int64_t sp = cus / rem;
+  if (sp > 8) sp = 8;
+  const int64_t nslabs = K / kV3BK;
+  while (sp > 1 && nslabs / sp < 4) --sp;
+  if (sp < 2) return;
+  *tail_tiles = rem;
+  *splits = sp;
+}
+
+int64_t gemm_glu_workspace_bytes(int64_t M, int64_t K, int64_t F) {
+  int64_t tail, sp;
+  glu_tail_split(M, K, F, &tail, &sp);
+  return sp > 1 ? tail * sp * 65536 * 4 : 0;
+}
+
 void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint32_t* w_gate,
                      const uint8_t* s_gate, const float* gs_gate, const uint32_t* w_up, const uint8_t* s_up,
-                     const float* gs_up, int act, void* out, hipStream_t s) {
+                     const float* gs_up, int act, void* out, hipStream_t s, void* ws, int64_t ws_bytes) {
   const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
-  const int64_t tiles = tiles_m * ((F + kV3BN / 2 - 1) / (kV3BN / 2));
-  const int64_t grid = (tiles + 7) / 8 * 8;
-  gemm_mfma_v3_kernel<kV3Glu><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-      static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, tiles, 0,
-      nullptr, w_up, s_up, gs_up, act);
+  const int64_t tiles = gemm_glu_tiles(M, F);
+  int64_t tail = 0, sp = 0;
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) glu_tail_split(M, K, F, &tail, &sp);
+  if (sp < 2 || ws_bytes < tail * sp * 65536 * 4) tail = 0;
+  const int64_t dp = tiles - tail;
+  if (dp > 0) {
+    const int64_t grid = (dp + 7) / 8 * 8;
+    gemm_mfma_v3_kernel<kV3Glu><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+        static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, dp, 0,
+        nullptr, w_up, s_up, gs_up, act, 0);
+  }
+  if (tail == 0) return;
+  const int64_t nslabs = K / kV3BK;
+  const int64_t per = (nslabs + sp - 1) / sp;
+  const int64_t grid = (tail * sp + 7) / 8 * 8;
+  gemm_mfma_v3_kernel<kV3GluSplit><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+      static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, tail, per,
+      static_cast<float*>(ws), w_up, s_up, gs_up, act, dp);
+  int64_t rgrid = (tail * 256 * 32 + 255) / 256;
+  if (rgrid > 4096) rgrid = 4096;
+  glu_tail_reduce_kernel<<<dim3((unsigned)rgrid), dim3(256), 0, s>>>(static_cast<const float*>(ws), sp, tail, dp,
+                                                                    tiles_m, M, F, gs_gate, gs_up, act,
+                                                                    static_cast<__bf16*>(out));
 }
 
 int64_t gemm_glu_tiles(int64_t M, int64_t F) {

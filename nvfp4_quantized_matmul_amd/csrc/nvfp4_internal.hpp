@@ -57,10 +57,17 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
 int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 // Gated MLP projection as one MFMA GEMM: bf16 activations, transposed gate
 // and up planes [F, K/8] with K % 64 == 0 and 4-byte aligned scale planes;
-// a tile holds 128 features of both planes.
+// a tile holds 128 features of both planes.  With a 16-byte aligned
+// workspace of at least gemm_glu_workspace_bytes(M, K, F) bytes, the last,
+// partial round of tiles is split along K (two more launches: the split
+// tiles and their reduction); otherwise one launch.
 void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint32_t* w_gate,
                      const uint8_t* s_gate, const float* gs_gate, const uint32_t* w_up, const uint8_t* s_up,
-                     const float* gs_up, int act, void* out, hipStream_t s);
+                     const float* gs_up, int act, void* out, hipStream_t s, void* ws = nullptr,
+                     int64_t ws_bytes = 0);
+// Workspace the gated projection's tail split wants on the current device
+// (0: no split).
+int64_t gemm_glu_workspace_bytes(int64_t M, int64_t K, int64_t F);
 // Blocks launch_gemm_glu runs for these sizes (before rounding to XCDs).
 int64_t gemm_glu_tiles(int64_t M, int64_t F);
 // out[i] = act(gate[i]) * out[i] over n elements of dtype dt.

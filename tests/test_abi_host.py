@@ -127,9 +127,12 @@ def glu(lib, x=FAKE, dt=BF16, M=300, K=64, F=32, wg=FAKE, sg=FAKE, gg=None, wu=F
 
 def test_qmm_glu_workspace_size_and_validation(lib):
     wsz = lib.nvfp4_qmm_glu_workspace_size
-    # the fused kernel (bf16, K % 64 == 0, GEMM-route sizes) needs no workspace
-    assert wsz(2048, 5376, 21504, BF16) == 0
-    assert wsz(300, 64, 32, BF16) == 0
+    # the fused kernel (bf16, K % 64 == 0, GEMM-route sizes) takes a workspace
+    # only to split its last, partial round of tiles along K: 1344 tiles of
+    # 128 features leave 64 after five rounds on 256 compute units (the host
+    # reading without a GPU), each split 4 ways, 256 x 256 floats per piece
+    assert wsz(2048, 5376, 21504, BF16) == 64 * 4 * 256 * 256 * 4
+    assert wsz(300, 64, 32, BF16) == 0          # one slab of K: nothing to split
     # otherwise gate goes to a workspace of M * F elements, rounded up to 256 bytes
     assert wsz(1, 5376, 21504, BF16) == 21504 * 2                  # qmv-route sizes
     assert wsz(300, 48, 40, BF16) == (300 * 40 * 2 + 255) // 256 * 256   # K % 64 != 0

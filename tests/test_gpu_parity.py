@@ -532,16 +532,43 @@ def glu_workspace(M, K, F, dtype):
     return int(nv.load_library().nvfp4_qmm_glu_workspace_size(M, K, F, code))
 
 
+def glu_is_fused(M, K, F, dtype):
+    return dtype == torch.bfloat16 and K > 0 and K % 64 == 0 and nv.select_route(M, K, F) == "gemm"
+
+
+ACT_CODES = {"gelu_tanh": 0, "gelu": 1, "silu": 2}
+
+
+def run_glu_no_workspace(g, u, act):
+    """The fused kernel through the C ABI with no workspace: one launch, no
+    tail split."""
+    x_t, x_ref = activations(g.x, torch.bfloat16)
+    ref = oracle.qmm_glu(x_ref, g.w, g.scales, gs_ref(g), u.w, u.scales, gs_ref(u), act)
+    out, check = guarded((g.M, g.N), torch.bfloat16)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    keep = [x_t, words(g.w), u8(g.scales), gs_arg(g), words(u.w), u8(u.scales), gs_arg(u)]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    status = nv.load_library().nvfp4_qmm_glu(P(keep[0]), 1, g.M, g.K, g.N, P(keep[1]), P(keep[2]), P(keep[3]),
+                                             P(keep[4]), P(keep[5]), P(keep[6]), ACT_CODES[act], None, 0, P(out), st)
+    assert status == 0
+    torch.cuda.synchronize()
+    check()
+    return out, ref
+
+
 @pytest.mark.parametrize("act", ["gelu_tanh", "gelu", "silu"])
 @pytest.mark.parametrize("shape", [(300, 1024, 1000), (513, 320, 257), (65, 64, 128), (256, 4096, 384)])
-def test_qmm_glu_fused_kernel(shape, act):
-    """bf16 with K % 64 == 0 at GEMM sizes runs the one fused kernel (no
-    workspace): several row and feature tiles, a ragged feature count (257,
-    and 1000 = 7 full tiles + 104), one slab (K = 64), rows past a tile."""
+@pytest.mark.parametrize("workspace", [True, False])
+def test_qmm_glu_fused_kernel(shape, act, workspace):
+    """bf16 with K % 64 == 0 at GEMM sizes runs the fused kernel: several row
+    and feature tiles, a ragged feature count (257, and 1000 = 7 full tiles +
+    104), one slab (K = 64), rows past a tile.  With the binding's workspace
+    the tiles (fewer than the compute units here) are also split along K
+    where each piece keeps at least four slabs; without one, one launch."""
     M, K, F = shape
-    assert glu_workspace(M, K, F, torch.bfloat16) == 0
+    assert glu_is_fused(M, K, F, torch.bfloat16)
     g, u = glu_planes(6100 + M + K + F, M, K, F)
-    out, ref = run_glu(g, u, torch.bfloat16, act)
+    out, ref = run_glu(g, u, torch.bfloat16, act) if workspace else run_glu_no_workspace(g, u, act)
     assert rel(out, ref) <= TOL[torch.bfloat16], (shape, act)
 
 
@@ -561,8 +588,9 @@ def test_qmm_glu_separate_projections(shape, dtype, act):
     qmm's own routes (qmv at M = 1 and 3, the MFMA qmv at 40, the GEMMs at
     300 with K = 48 and at 70 with K = 96) into a workspace, then combine."""
     M, K, F = shape
-    fused = dtype == torch.bfloat16 and K % 64 == 0 and nv.select_route(M, K, F) == "gemm"
-    assert (glu_workspace(M, K, F, dtype) == 0) == fused
+    if not glu_is_fused(M, K, F, dtype):
+        size = M * F * (4 if dtype == torch.float32 else 2)
+        assert glu_workspace(M, K, F, dtype) == (size + 255) // 256 * 256
     g, u = glu_planes(6300 + M + K + F, M, K, F)
     out, ref = run_glu(g, u, dtype, act)
     assert rel(out, ref) <= TOL[dtype], (shape, dtype, act)
@@ -578,17 +606,49 @@ def test_qmm_glu_zero_k_and_empty():
     assert nv.qmm_glu(x, w, s, None, w, s, None).shape == (0, 32)
 
 
+def test_qmm_glu_fused_tail_split():
+    """300 tiles of 128 features leave 44 after one round on 256 compute
+    units; with the workspace they are split 5 ways along K (32 slabs) and
+    reduced: sampled features of whole-round and split tiles against the
+    oracle, and the whole output against the unsplit fused launch."""
+    M, K, F = 256, 2048, 128 * 300
+    lib = nv.load_library()
+    ws_bytes = glu_workspace(M, K, F, torch.bfloat16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"split sizes are chosen for 256 compute units, this device has {cus}")
+    assert ws_bytes == 44 * 5 * 256 * 256 * 4
+    g, u = glu_planes(6600, M, K, F)
+    x_t, x_ref = activations(g.x, torch.bfloat16)
+    wg, sg, wu_, su_ = words(g.w), u8(g.scales), words(u.w), u8(u.scales)
+    ggs, ugs = f32(g.gs), f32(u.gs)
+    out = nv.qmm_glu(x_t, wg, sg, ggs, wu_, su_, ugs, act="silu")     # the binding passes the workspace
+    plain, check = guarded((M, F), torch.bfloat16)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    assert lib.nvfp4_qmm_glu(P(x_t), 1, M, K, F, P(wg), P(sg), P(ggs), P(wu_), P(su_), P(ugs), 2, None, 0,
+                             P(plain), st) == 0
+    torch.cuda.synchronize()
+    check()
+    feats = np.unique(np.concatenate([np.arange(0, 256 * 128, 509), np.arange(256 * 128, F, 37), [F - 1]]))
+    ref = oracle.qmm_glu(x_ref, g.w[feats], g.scales[feats], g.gs[0], u.w[feats], u.scales[feats], u.gs[0], "silu")
+    assert oracle.relative_error(host(out)[:, feats], ref) <= TOL[torch.bfloat16]
+    assert oracle.relative_error(host(out), host(plain)) <= TOL[torch.bfloat16]
+
+
 def test_qmm_glu_full_size_sampled():
     """The prefill MLP's gate/up shape, M=2048, K=5376, F=21504, bf16, through
-    the fused kernel that is timed; sampled rows and features against the
+    the fused kernel that is timed, with the binding's workspace (so the 64
+    tiles past five whole rounds are split along K); sampled rows and
+    features, among them the split tiles' (features 20480 on), against the
     oracle (features are independent rows of both planes)."""
     M, K, F = 2048, 5376, 21504
-    assert glu_workspace(M, K, F, torch.bfloat16) == 0
+    assert glu_is_fused(M, K, F, torch.bfloat16)
     g, u = glu_planes(6500, M, K, F)
     x_t, x_ref = activations(g.x, torch.bfloat16)
     out = nv.qmm_glu(x_t, words(g.w), u8(g.scales), f32(g.gs), words(u.w), u8(u.scales), f32(u.gs))
     rows = np.unique(np.concatenate([np.arange(0, M, 97), [1, 255, 256, 2047]]))
-    feats = np.unique(np.concatenate([np.arange(0, F, 61), [127, 128, 21503]]))
+    feats = np.unique(np.concatenate([np.arange(0, F, 61), np.arange(20480, F, 13), [127, 128, 21503]]))
     ref = oracle.qmm_glu(x_ref[rows], g.w[feats], g.scales[feats], g.gs[0], u.w[feats], u.scales[feats],
                          u.gs[0], "gelu_tanh")
     got = host(out)[np.ix_(rows, feats)]
