@@ -391,7 +391,8 @@ def other_configs():
     """The remaining configurations, each as microseconds per call and the
     rate against its roofline: the tiny qmv (latency), multi-row qmv at every
     M in f32 and bf16, MoE unsorted decode at B = 1, 2, 4, 8, batched-weight
-    qmm, and the load-time transcode, dequantize and quantize."""
+    qmm (all back-to-back C ABI launches with prebuilt arguments), and the
+    load-time transcode, dequantize and quantize (through the binding)."""
     out = {}
     lib = nv.load_library()
     # tiny qmv: M=1, K=1024, N=512, f32, no global scale (launch-latency bound)
@@ -400,9 +401,13 @@ def other_configs():
     x = torch.from_numpy(c.x).to(DEV)
     w, s = words_dev(c.w), u8_dev(c.scales)
     y = torch.empty((1, 512), dtype=torch.float32, device=DEV)
-    us = timed_us(lambda i: nv.qmm(x, w, s, out=y), 200, warmup=20)
-    out["tiny_qmv_m1_k1024_n512_f32"] = {"us": round(us, 3), "bytes": 301056,
-                                         "note": "fits in L2; latency, not bandwidth, bounds it"}
+    targs = (P(x), 0, 1, 1024, 512, P(w), P(s), None, 1, 0, P(y), stream_ptr())
+    us = timed_us(lambda i: lib.nvfp4_qmm(*targs), 400, warmup=50)
+    binding_us = timed_us(lambda i: nv.qmm(x, w, s, out=y), 200, warmup=20)
+    out["tiny_qmv_m1_k1024_n512_f32"] = {"us": round(us, 3), "bytes": 301056, "binding_us": round(binding_us, 3),
+                                         "note": "fits in L2; launch latency, not bandwidth, bounds it. us: "
+                                                 "back-to-back C ABI launches; binding_us: the same through the "
+                                                 "Python binding (host-bound at this size)"}
     # multi-row: one plane, 16 copies (530 MB), every M and dtype
     wl = synth.WORKLOADS["multirow_qmv_k4096_n14336"]
     c = synth.dense_case(wl["seed"], 33, 4096, 14336, with_gs=True)
@@ -411,11 +416,13 @@ def other_configs():
     ss = [s0] + [s0.clone() for _ in range(15)]
     gs = torch.from_numpy(c.gs).to(DEV)
     rows = []
-    for dt, name, size in ((torch.bfloat16, "bf16", 2), (torch.float32, "f32", 4)):
+    st = stream_ptr()
+    for dt, name, size, code in ((torch.bfloat16, "bf16", 2, BF16), (torch.float32, "f32", 4, 0)):
         for M in wl["Ms"]:
             xm = torch.from_numpy(c.x[:M]).to(dt).to(DEV)
             ym = torch.empty((M, 14336), dtype=dt, device=DEV)
-            us = timed_us(lambda i: nv.qmm(xm, ws[i % 16], ss[i % 16], gs, out=ym), 64)
+            margs = [(P(xm), code, M, 4096, 14336, P(ws[k]), P(ss[k]), P(gs), 1, 0, P(ym), st) for k in range(16)]
+            us = timed_us(lambda i: lib.nvfp4_qmm(*margs[i % 16]), 64)
             nbytes = c.w.nbytes + c.scales.nbytes + 4 + M * 4096 * size + M * 14336 * size
             rows.append({"M": M, "dtype": name, "us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
                          "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
@@ -429,7 +436,8 @@ def other_configs():
     for M in (3, 64):
         xb = torch.from_numpy(np.ascontiguousarray(bc.x[:, :M])).to(torch.bfloat16).to(DEV)
         yb = torch.empty((2, M, 14336), dtype=torch.bfloat16, device=DEV)
-        us = timed_us(lambda i: nv.qmm_batched(xb, bw, bs, bg, out=yb), 32)
+        bargs = (P(xb), BF16, 2, 2, M, 4096, 14336, P(bw), P(bs), P(bg), 1, 0, P(yb), stream_ptr())
+        us = timed_us(lambda i: lib.nvfp4_qmm_batched(*bargs), 32)
         nbytes = bc.w.nbytes + bc.scales.nbytes + 8 + xb.numel() * 2 + yb.numel() * 2
         brow.append({"B": 2, "M": M, "dtype": "bf16", "us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
                      "note": "planes fit the MALL (cache-warm)"})
