@@ -1021,3 +1021,35 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for i, (c, e) in enumerate(zip(captured, eager)):
             assert torch.equal(c, e), (rep, i)
+
+
+# ----------------------------------------------------------------------------
+# planes beyond 2 GiB
+# ----------------------------------------------------------------------------
+
+def test_plane_beyond_2gib():
+    """A 2,147,614,720-byte word plane (N = 262160, K = 16384): the decode,
+    multi-row and grouped kernels address planes with 32-bit buffer offsets
+    and hand such a plane to the generic qmv kernel, whose offsets are 64-bit;
+    the GEMM route uses 64-bit pointers.  Sampled weight rows (features are
+    independent rows) against the oracle at M = 1, 16 (qmv route) and 300
+    (GEMM route), outputs inside guard bands."""
+    N, K = 262160, 16384
+    assert N * K // 2 > 2 ** 31
+    g = synth.rng(8200)
+    w_np = synth.packed_words(g, (N, K // 8))
+    s_np = synth.scale_codes(g, (N, K // 16), (0x08, 0x30))
+    gs_np = synth.global_scales(g, 1)
+    x_np = synth.activations(g, (300, K))
+    w_t, s_t, gs_t = words(w_np), u8(s_np), f32(gs_np)
+    rows = np.unique(np.concatenate([np.arange(0, N, 4099), [1, 63, 64, 131071, 131072, N - 17, N - 1]]))
+    for M in (1, 16, 300):
+        x_t, x_ref = activations(x_np[:M], torch.bfloat16)
+        out, check = guarded((M, N), torch.bfloat16)
+        nv.qmm(x_t, w_t, s_t, gs_t, out=out)
+        torch.cuda.synchronize()
+        check()
+        ref = oracle.qmm(x_ref, w_np[rows], s_np[rows], gs_np[0])
+        assert oracle.relative_error(host(out)[:, rows], ref) <= TOL[torch.bfloat16], M
+        del out
+    torch.cuda.empty_cache()
