@@ -261,6 +261,7 @@ int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtyp
     return NVFP4_ERR_SHAPE;
   if (M == 0 || F == 0 || K == 0) return 0;
   if (glu_fused(M, K, F, dtype)) return nvfp4host::gemm_glu_workspace_bytes(M, K, F);
+  if (M == 1 && nvfp4host::decode_glu_applies(K, F)) return 0;   // the decode kernel's gated form
   return (t + 255) / 256 * 256;
 }
 
@@ -303,6 +304,14 @@ int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int6
     if (nvfp4host::gemm_glu_tiles(M, F) * 9 + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
     nvfp4host::launch_gemm_glu(x, M, K, F, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, (int)act, out, stream,
                                workspace, workspace_bytes);
+    return launched();
+  }
+  if (M == 1 && nvfp4host::decode_glu_applies(K, F)) {
+    // one launch of the decode kernel, a feature's gate and up rows per
+    // wavefront; no workspace
+    if (!nvfp4host::launch_decode_glu(x, dtype, K, F, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, (int)act, out,
+                                      stream))
+      return NVFP4_ERR_UNSUPPORTED;
     return launched();
   }
   if (workspace_bytes < need) return NVFP4_ERR_SHAPE;

@@ -2,6 +2,7 @@
 // (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM", "Summary":
 // the qmv kernel the pages run for decode; g = global_scale / (448 * 6)
 // applied once per output).
+#include "glu_act.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.hpp"
 
@@ -117,15 +118,23 @@ __device__ __forceinline__ rsrc_t byte_buffer(const void* p, int64_t bytes) {
 // An offset no plane reaches (planes stay below 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <typename TX, int CPL, int R>
+// GLU: the gated projection of an MLP at M = 1 (mlxcel issue "perf(metal):
+// close native NVFP4 prefill gap", "Activation-path follow-up").  The
+// wavefront's two rows are feature f of the gate plane (w, sc, gs) and of the
+// up plane (wu, scu, gsu), and lane 0 stores act(g * gate) * (g_u * up).
+template <typename TX, int CPL, int R, bool GLU = false>
 __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x,
                                                         const uint32_t* w,
                                                         const uint8_t* sc,
                                                         const float* __restrict__ gs,
-                                                        TX* __restrict__ out, int64_t K, int64_t N) {
+                                                        TX* __restrict__ out, int64_t K, int64_t N,
+                                                        const uint32_t* wu = nullptr,
+                                                        const uint8_t* scu = nullptr,
+                                                        const float* __restrict__ gsu = nullptr, int act = 0) {
+  static_assert(!GLU || R == 2, "the gated form streams one gate row and one up row");
   extern __shared__ uint4 xl[];
   const int lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
+  const int64_t n0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * (GLU ? 1 : R);
   const int64_t kw = K / 8, ks = K / 16, nchunks = kw / 4;
   const int nch = (int)nchunks;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -141,26 +150,31 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
   //    result has to be merged with a default value.
   const rsrc_t wb = byte_buffer(w, N * kw * 4);
   const rsrc_t sb = byte_buffer(sc, N * ks);
+  const rsrc_t wb2 = GLU ? byte_buffer(wu, N * kw * 4) : wb;
+  const rsrc_t sb2 = GLU ? byte_buffer(scu, N * ks) : sb;
   uint4 wv[R][CPL];
   uint32_t sv[R][CPL];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t n = n0 + r;
+    const int64_t n = GLU ? n0 : n0 + r;
+    const rsrc_t& wr = (GLU && r == 1) ? wb2 : wb;
+    const rsrc_t& sr = (GLU && r == 1) ? sb2 : sb;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
       const bool ok = n < N && c < nch;
       const uint32_t wo = ok ? (uint32_t)(n * kw * 4 + c * 16) : kOutOfRange;
       const uint32_t so = ok ? (uint32_t)(n * ks + c * 2) : kOutOfRange;
-      wv[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wb, wo, 0, 0));
-      sv[r][i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sb, so, 0, 0);
+      wv[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo, 0, 0));
+      sv[r][i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
     }
   }
   // 2. Wait only for the activation pieces (issued before the 2 R CPL loads
   //    above; loads complete in order), then the block barrier makes every
   //    wave's pieces visible.  The weights are consumed as they arrive.
-  static_assert(2 * R * CPL < 16, "vmcnt immediate holds 4 bits here");
-  __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (2 * R * CPL));
+  constexpr int kLoads = 2 * R * CPL;   // vmcnt: 6 bits, low 4 at [3:0], high 2 at [15:14]
+  static_assert(kLoads < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (kLoads & 0xF) | ((kLoads >> 4) << 14));
   __builtin_amdgcn_s_barrier();
   // 3. Decode and reduce.
   float acc[R];
@@ -176,10 +190,15 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
     }
   }
   const float g = global_factor(gs, 0);
+  if constexpr (GLU) {
+    const float gate = wave_sum_dpp(acc[0]), up = wave_sum_dpp(acc[1]);
+    if (lane == 0 && n0 < N) store_out(out + n0, glu_act(gate * g, act) * (up * global_factor(gsu, 0)));
+  } else {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float v = wave_sum_dpp(acc[r]);
-    if (lane == 0 && n0 + r < N) store_out(out + n0 + r, v * g);
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum_dpp(acc[r]);
+      if (lane == 0 && n0 + r < N) store_out(out + n0 + r, v * g);
+    }
   }
 }
 
@@ -191,6 +210,30 @@ void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uin
   const int64_t blocks = (N + kWaves * kQmv1Rows - 1) / (kWaves * kQmv1Rows);
   const size_t lds = staged_x_bytes<TX>(K);
   qmv1_kernel<TX, CPL, kQmv1Rows><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(x, w, sc, gs, out, K, N);
+}
+
+template <typename TX, int CPL>
+void qmv1_glu_launch(const TX* x, int64_t K, int64_t F, const uint32_t* w, const uint8_t* sc, const float* gs,
+                     const uint32_t* wu, const uint8_t* scu, const float* gsu, int act, TX* out, hipStream_t s) {
+  const int64_t blocks = (F + kWaves - 1) / kWaves;
+  const size_t lds = staged_x_bytes<TX>(K);
+  qmv1_kernel<TX, CPL, 2, true><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(x, w, sc, gs, out, K, F, wu, scu,
+                                                                                   gsu, act);
+}
+
+// True when the decode kernel's gated form handles this K (and launches it):
+// as for try_qmv1, with both planes below 2^31 bytes.
+template <typename TX>
+bool try_qmv1_glu(const TX* x, int64_t K, int64_t F, const uint32_t* w, const uint8_t* sc, const float* gs,
+                  const uint32_t* wu, const uint8_t* scu, const float* gsu, int act, TX* out, hipStream_t s) {
+  if (K % 32 != 0 || F * (K / 2) >= ((int64_t)1 << 31)) return false;
+  switch ((K / 32 + 63) / 64) {
+    case 1: qmv1_glu_launch<TX, 1>(x, K, F, w, sc, gs, wu, scu, gsu, act, out, s); return true;
+    case 2: qmv1_glu_launch<TX, 2>(x, K, F, w, sc, gs, wu, scu, gsu, act, out, s); return true;
+    case 3: qmv1_glu_launch<TX, 3>(x, K, F, w, sc, gs, wu, scu, gsu, act, out, s); return true;
+    case 4: qmv1_glu_launch<TX, 4>(x, K, F, w, sc, gs, wu, scu, gsu, act, out, s); return true;
+    default: return false;
+  }
 }
 
 // True when the M = 1 decode kernel handles this K (and launches it):
@@ -224,6 +267,27 @@ bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const 
       return try_qmv1<float>(static_cast<const float*>(x), K, N, w, sc, gs, static_cast<float*>(out), s);
     case NVFP4_F16:
       return try_qmv1<_Float16>(static_cast<const _Float16*>(x), K, N, w, sc, gs, static_cast<_Float16*>(out), s);
+  }
+  return false;
+}
+
+bool decode_glu_applies(int64_t K, int64_t F) {
+  return K > 0 && K % 32 == 0 && (K / 32 + 63) / 64 <= 4 && F * (K / 2) < ((int64_t)1 << 31);
+}
+
+bool launch_decode_glu(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t F, const uint32_t* w,
+                       const uint8_t* sc, const float* gs, const uint32_t* wu, const uint8_t* scu,
+                       const float* gsu, int act, void* out, hipStream_t s) {
+  switch (dt) {
+    case NVFP4_BF16:
+      return try_qmv1_glu<__bf16>(static_cast<const __bf16*>(x), K, F, w, sc, gs, wu, scu, gsu, act,
+                                  static_cast<__bf16*>(out), s);
+    case NVFP4_F32:
+      return try_qmv1_glu<float>(static_cast<const float*>(x), K, F, w, sc, gs, wu, scu, gsu, act,
+                                 static_cast<float*>(out), s);
+    case NVFP4_F16:
+      return try_qmv1_glu<_Float16>(static_cast<const _Float16*>(x), K, F, w, sc, gs, wu, scu, gsu, act,
+                                    static_cast<_Float16*>(out), s);
   }
   return false;
 }

@@ -27,6 +27,13 @@ void launch_quantize(const void* w, nvfp4_dtype_t dt, int64_t batch, int64_t row
                      const float* gs_in, uint32_t* w_out, uint8_t* sc_out, float* gs_out, hipStream_t s);
 // Decode kernel (M = 1): returns false, launching nothing, when K is not
 // a multiple of 32, K > 8192 or the weight plane reaches 2^31 bytes.
+// Gated projection at M = 1 in one launch of the decode kernel (two rows
+// per wavefront: a feature's gate row and up row).  decode_glu_applies says
+// whether launch_decode_glu takes these sizes (it returns false otherwise).
+bool decode_glu_applies(int64_t K, int64_t F);
+bool launch_decode_glu(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t F, const uint32_t* w,
+                       const uint8_t* sc, const float* gs, const uint32_t* wu, const uint8_t* scu,
+                       const float* gsu, int act, void* out, hipStream_t s);
 bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const uint32_t* w,
                    const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // Dense qmv: out[M,N] = x[M,K] @ W[N,K]^T (transposed plane).

@@ -134,7 +134,10 @@ def test_qmm_glu_workspace_size_and_validation(lib):
     assert wsz(2048, 5376, 21504, BF16) == 64 * 4 * 256 * 256 * 4
     assert wsz(300, 64, 32, BF16) == 0          # one slab of K: nothing to split
     # otherwise gate goes to a workspace of M * F elements, rounded up to 256 bytes
-    assert wsz(1, 5376, 21504, BF16) == 21504 * 2                  # qmv-route sizes
+    assert wsz(1, 5376, 21504, BF16) == 0                          # M = 1: the decode kernel's gated form
+    assert wsz(1, 5376, 21504, F32) == 0
+    assert wsz(1, 8208, 64, BF16) == 64 * 2 + 128                  # K beyond the decode kernel (> 8192)
+    assert wsz(3, 5376, 21504, BF16) == 3 * 21504 * 2              # other qmv-route sizes
     assert wsz(300, 48, 40, BF16) == (300 * 40 * 2 + 255) // 256 * 256   # K % 64 != 0
     assert wsz(300, 64, 32, F32) == 300 * 32 * 4
     assert wsz(300, 64, 32, F16) == 300 * 32 * 2

@@ -584,16 +584,41 @@ def test_qmm_glu_fused_global_scales(gs):
 @pytest.mark.parametrize("shape", [(1, 512, 300), (3, 256, 200), (40, 512, 96), (300, 48, 40), (70, 96, 64)])
 @pytest.mark.parametrize("act", ["gelu_tanh", "silu"])
 def test_qmm_glu_separate_projections(shape, dtype, act):
-    """Every case the fused kernel does not take: the projections run through
-    qmm's own routes (qmv at M = 1 and 3, the MFMA qmv at 40, the GEMMs at
-    300 with K = 48 and at 70 with K = 96) into a workspace, then combine."""
+    """Every case the fused GEMM does not take: M = 1 is the decode kernel's
+    gated form (one launch); otherwise the projections run through qmm's own
+    routes (qmv at M = 3, the MFMA qmv at 40, the GEMMs at 300 with K = 48 and
+    at 70 with K = 96) into a workspace, then combine."""
     M, K, F = shape
-    if not glu_is_fused(M, K, F, dtype):
+    if M == 1 and K % 32 == 0:
+        assert glu_workspace(M, K, F, dtype) == 0      # the decode kernel's gated form
+    elif not glu_is_fused(M, K, F, dtype):
         size = M * F * (4 if dtype == torch.float32 else 2)
         assert glu_workspace(M, K, F, dtype) == (size + 255) // 256 * 256
     g, u = glu_planes(6300 + M + K + F, M, K, F)
     out, ref = run_glu(g, u, dtype, act)
     assert rel(out, ref) <= TOL[dtype], (shape, dtype, act)
+
+
+@pytest.mark.parametrize("K", [256, 4096, 5376, 8192])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu", "silu"])
+def test_qmm_glu_decode_kernel(K, dtype, act):
+    """M = 1 runs the decode kernel's gated form in one launch (no
+    workspace): one to four chunks per lane (K = 8192 keeps 16 loads in
+    flight per wavefront), a ragged feature count, each plane its own global
+    scale."""
+    assert glu_workspace(1, K, 333, dtype) == 0
+    g, u = glu_planes(6700 + K, 1, K, 333)
+    out, ref = run_glu(g, u, dtype, act)
+    assert rel(out, ref) <= TOL[dtype], (K, dtype, act)
+
+
+def test_qmm_glu_decode_mlp_shape():
+    """The decode MLP's gate/up shape, M = 1, K = 5376, F = 21504, bf16, in
+    full against the oracle."""
+    g, u = glu_planes(6800, 1, 5376, 21504)
+    out, ref = run_glu(g, u, torch.bfloat16, "gelu_tanh")
+    assert rel(out, ref) <= TOL[torch.bfloat16]
 
 
 def test_qmm_glu_zero_k_and_empty():
