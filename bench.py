@@ -450,6 +450,32 @@ def other_configs():
                          "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                          "route": nv.select_route(M, 4096, 14336, dtype=dt)})
     out["multirow_qmv_k4096_n14336"] = rows
+    # the gated projection at M = 16 on the same planes (gate and up = copies
+    # 2c and 2c + 1): one launch of the multi-row kernel's gated form, beside
+    # two multi-row launches and the unfused pipeline
+    x16 = torch.from_numpy(c.x[:16]).to(torch.bfloat16).to(DEV)
+    y16 = torch.empty((16, 14336), dtype=torch.bfloat16, device=DEV)
+    gargs = [(P(x16), BF16, 16, 4096, 14336, P(ws[2 * k]), P(ss[2 * k]), P(gs), P(ws[2 * k + 1]), P(ss[2 * k + 1]),
+              P(gs), 0, None, 0, P(y16), st) for k in range(8)]
+    glu_us = timed_us(lambda i: lib.nvfp4_qmm_glu(*gargs[i % 8]), 64)
+    pair_args = [(P(x16), BF16, 16, 4096, 14336, P(ws[k]), P(ss[k]), P(gs), 1, 0, P(y16), st) for k in range(16)]
+    pair_us = 2 * timed_us(lambda i: lib.nvfp4_qmm(*pair_args[i % 16]), 64)
+    g16, u16 = torch.empty_like(y16), torch.empty_like(y16)
+
+    def unfused16(i):
+        k = i % 8
+        nv.qmm(x16, ws[2 * k], ss[2 * k], gs, out=g16)
+        nv.qmm(x16, ws[2 * k + 1], ss[2 * k + 1], gs, out=u16)
+        torch.nn.functional.gelu(g16, approximate="tanh").mul_(u16)
+
+    unf_us = timed_us(unfused16, 32, warmup=4)
+    gbytes = 2 * (c.w.nbytes + c.scales.nbytes + 4) + 16 * 4096 * 2 + 16 * 14336 * 2
+    out["mlp_gate_up_multirow_m16_k4096_f14336_bf16"] = {
+        "us": round(glu_us, 3), "GB_s": round(gbytes / glu_us / 1e3, 1),
+        "frac_hbm": round(gbytes / glu_us / 1e3 / HBM_PEAK_GBS, 4), "bytes": gbytes,
+        "separate_pair_us": round(pair_us, 3), "unfused_us": round(unf_us, 3),
+        "note": "one launch of the multi-row kernel's gated form (tanh GELU); separate_pair_us = two multi-row "
+                "qmm launches; unfused_us = those plus torch's activation and product through the binding"}
     del ws, ss
     # batched weights: two matrices of the multi-row shape at M = 3 (qmv) and 64
     bc = synth.batched_case(3600, B=2, M=64, K=4096, N=14336)

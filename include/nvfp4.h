@@ -235,7 +235,11 @@ int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
  * M = 1 with K % 32 == 0, K <= 8192 and planes below 2^31 bytes (any
  * activation type) is one launch of the decode kernel: each wavefront
  * streams one feature's gate row and up row and applies g, the activation
- * and the product to the two float32 sums; no workspace.  Every other case
+ * and the product to the two float32 sums; no workspace.  2 <= M <= 64 with
+ * K % 256 == 0 (planes below 2^31 bytes) is one launch of the multi-row MFMA
+ * kernel, each block multiplying 32 features' gate and up rows; it needs
+ * 16-byte aligned x, planes and scale planes (NVFP4_ERR_ALIGN otherwise) and
+ * no workspace.  Every other case
  * runs both projections through nvfp4_qmm's kernels into `workspace` and
  * `out` and then combines them (one extra rounding of each projection to the
  * output dtype); a workspace smaller than the queried size returns
@@ -254,9 +258,9 @@ int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int6
 
 /* Workspace bytes nvfp4_qmm_glu wants for these sizes on the current device
  * (host only): for the fused kernel the bytes of its tail split (0 when it
- * would not split), 0 for the one-launch M = 1 form, M * F * sizeof(dtype)
- * rounded up to 256 otherwise; a negative status for invalid sizes or
- * dtype. */
+ * would not split), 0 for the one-launch M = 1 and multi-row forms,
+ * M * F * sizeof(dtype) rounded up to 256 otherwise; a negative status for
+ * invalid sizes or dtype. */
 int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtype_t dtype);
 
 /*

@@ -262,6 +262,7 @@ int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtyp
   if (M == 0 || F == 0 || K == 0) return 0;
   if (glu_fused(M, K, F, dtype)) return nvfp4host::gemm_glu_workspace_bytes(M, K, F);
   if (M == 1 && nvfp4host::decode_glu_applies(K, F)) return 0;   // the decode kernel's gated form
+  if (nvfp4host::skinny_glu_applies(M, K, F)) return 0;           // the multi-row kernel's gated form
   return (t + 255) / 256 * 256;
 }
 
@@ -310,6 +311,17 @@ int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int6
     // one launch of the decode kernel, a feature's gate and up rows per
     // wavefront; no workspace
     if (!nvfp4host::launch_decode_glu(x, dtype, K, F, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, (int)act, out,
+                                      stream))
+      return NVFP4_ERR_UNSUPPORTED;
+    return launched();
+  }
+  if (nvfp4host::skinny_glu_applies(M, K, F)) {
+    // one launch of the multi-row MFMA kernel, 32 features' gate and up rows
+    // per block; its 16-byte loads need 16-byte aligned operands
+    if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(s_gate, 16) || !aligned(w_up, 16) ||
+        !aligned(s_up, 16))
+      return NVFP4_ERR_ALIGN;
+    if (!nvfp4host::launch_skinny_glu(x, dtype, M, K, F, w_gate, s_gate, gs_gate, w_up, s_up, gs_up, (int)act, out,
                                       stream))
       return NVFP4_ERR_UNSUPPORTED;
     return launched();

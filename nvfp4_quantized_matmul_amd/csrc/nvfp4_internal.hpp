@@ -34,6 +34,14 @@ bool decode_glu_applies(int64_t K, int64_t F);
 bool launch_decode_glu(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t F, const uint32_t* w,
                        const uint8_t* sc, const float* gs, const uint32_t* wu, const uint8_t* scu,
                        const float* gsu, int act, void* out, hipStream_t s);
+// Gated projection for 2 <= M <= 64 through the multi-row MFMA kernel (a
+// block holds 32 features' gate and up rows).  skinny_glu_applies checks the
+// sizes; launch_skinny_glu also needs 16-byte aligned x, planes and scales
+// and returns false otherwise.
+bool skinny_glu_applies(int64_t M, int64_t K, int64_t F);
+bool launch_skinny_glu(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t F, const uint32_t* w,
+                       const uint8_t* sc, const float* gs, const uint32_t* wu, const uint8_t* scu,
+                       const float* gsu, int act, void* out, hipStream_t s);
 bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const uint32_t* w,
                    const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // Dense qmv: out[M,N] = x[M,K] @ W[N,K]^T (transposed plane).

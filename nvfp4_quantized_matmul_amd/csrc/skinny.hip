@@ -48,6 +48,7 @@
 // past the end of a plane reads as zeros, so rows past N or M need no
 // clamping (their results are never stored), and a valid row's pair-group
 // offset never leaves that row.
+#include "glu_act.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_internal.hpp"
 
@@ -135,18 +136,22 @@ struct PairGroup {
 template <int MF>
 struct Sources {
   rsrc_t w, s, x;         // weight plane, scale plane, activations
+  rsrc_t w2, s2;          // gated form: the up plane and its scales (tiles 2 and 3)
   uint32_t wo[kTiles];    // byte offset of this lane's weight row in tile t, + 16q
   uint32_t so[kTiles];    // byte offset of its scale row
   uint32_t xo[MF];        // byte offset of this lane's activation row in fragment f, + 8q elements
 };
 
 // Offsets of weight rows n0 + 16t + r (lane r = lane % 16, q = lane / 16).
-template <int MF>
+// GLU: tiles 0, 1 are gate rows n0 .. n0 + 31 and tiles 2, 3 the up rows of
+// the same features.
+template <int MF, bool GLU = false>
 __device__ __forceinline__ void set_rows(Sources<MF>& src, int64_t n0, int r16, int q, int64_t K) {
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
-    src.wo[t] = (uint32_t)((n0 + 16 * t + r16) * (K / 2) + 16 * q);
-    src.so[t] = (uint32_t)((n0 + 16 * t + r16) * (K / 16));
+    const int64_t row = n0 + 16 * (GLU ? (t & 1) : t) + r16;
+    src.wo[t] = (uint32_t)(row * (K / 2) + 16 * q);
+    src.so[t] = (uint32_t)(row * (K / 16));
   }
 }
 
@@ -154,7 +159,7 @@ __device__ __forceinline__ void set_rows(Sources<MF>& src, int64_t n0, int r16, 
 // activations, then scales and words tile by tile; chunk 1: activations,
 // words), so the in-order load counter lets chunk 0 be multiplied while
 // chunk 1 is still arriving.
-template <typename TX, int MF>
+template <typename TX, int MF, bool GLU = false>
 __device__ __forceinline__ void load_pg(PairGroup<MF, TX>& p, const Sources<MF>& src, uint32_t pg) {
   constexpr uint32_t E = sizeof(TX);
 #pragma unroll
@@ -168,8 +173,10 @@ __device__ __forceinline__ void load_pg(PairGroup<MF, TX>& p, const Sources<MF>&
           p.x[f][4 * c + i][h] = load16(src.x, src.xo[f], (pg * 256u + c * 128u + i * 32u) * E + h * 16u);
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      if (c == 0) p.s[t] = load16(src.s, src.so[t], pg * 16u);           // 16 scale bytes per pair-group
-      p.w[t][c] = load16(src.w, src.wo[t], pg * 128u + c * 64u);        // 32 words per pair-group
+      const rsrc_t& wr = (GLU && t >= 2) ? src.w2 : src.w;
+      const rsrc_t& sr = (GLU && t >= 2) ? src.s2 : src.s;
+      if (c == 0) p.s[t] = load16(sr, src.so[t], pg * 16u);             // 16 scale bytes per pair-group
+      p.w[t][c] = load16(wr, src.wo[t], pg * 128u + c * 64u);           // 32 words per pair-group
     }
   }
 }
@@ -232,7 +239,7 @@ __device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const Pai
 }
 
 // This wavefront's pair-groups wid, wid + nw, ... into acc.
-template <typename TX, int MF>
+template <typename TX, int MF, bool GLU = false>
 __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const Sources<MF>& src, int wid,
                                                int nw, int64_t npg, int half) {
 #pragma unroll
@@ -243,7 +250,7 @@ __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const
       for (int i = 0; i < 4; ++i) acc[t][f][i] = 0.0f;
   PairGroup<MF, TX> p;
   for (int64_t pg = wid; pg < npg; pg += nw) {
-    load_pg(p, src, (uint32_t)pg);
+    load_pg<TX, MF, GLU>(p, src, (uint32_t)pg);
     // keep every load ahead of the multiply: the scheduler would otherwise
     // sink each load to its use and expose its latency one by one
     __builtin_amdgcn_sched_barrier(0);
@@ -269,31 +276,42 @@ __device__ __forceinline__ void store4(TO* out, int64_t orow, int64_t n, int64_t
   }
 }
 
-template <typename TX, int MF, int MAXW>
+// GLU: the gated MLP projection (mlxcel issue "perf(metal): close native
+// NVFP4 prefill gap", "Activation-path follow-up"): a block covers 32
+// features, tiles 0 and 1 their gate rows (w, sc, gs) and tiles 2 and 3 their
+// up rows (wu, scu, gsu), and out = act(g * gate) * (g_u * up).
+template <typename TX, int MF, int MAXW, bool GLU = false>
 __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict__ x,
                                                           const uint32_t* __restrict__ w,
                                                           const uint8_t* __restrict__ sc,
                                                           const float* __restrict__ gs,
                                                           TX* __restrict__ out, int64_t M,
-                                                          int64_t K, int64_t N) {
+                                                          int64_t K, int64_t N,
+                                                          const uint32_t* __restrict__ wu = nullptr,
+                                                          const uint8_t* __restrict__ scu = nullptr,
+                                                          const float* __restrict__ gsu = nullptr, int act = 0) {
   __shared__ f32x4_t red[MAXW][kTiles * MF][64];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nw = (int)(blockDim.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t n0 = (int64_t)blockIdx.x * (GLU ? kRows / 2 : kRows);
 
   Sources<MF> src;
   src.w = plane(w, N * (K / 2));
   src.s = plane(sc, N * (K / 16));
   src.x = plane(x, M * K * (int64_t)sizeof(TX));
-  set_rows(src, n0, r16, q, K);
+  if constexpr (GLU) {
+    src.w2 = plane(wu, N * (K / 2));
+    src.s2 = plane(scu, N * (K / 16));
+  }
+  set_rows<MF, GLU>(src, n0, r16, q, K);
 #pragma unroll
   for (int f = 0; f < MF; ++f) src.xo[f] = (uint32_t)(((16 * f + r16) * K + 8 * q) * (int64_t)sizeof(TX));
 
   f32x4_t acc[kTiles][MF];
-  run_pairgroups<TX>(acc, src, wid, nw, K / kPG, q >> 1);
+  run_pairgroups<TX, MF, GLU>(acc, src, wid, nw, K / kPG, q >> 1);
 
   // Partial sums of the wavefronts, added in wavefront order.
 #pragma unroll
@@ -303,6 +321,28 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   __syncthreads();
 
   const float g = global_factor(gs, 0);
+  if constexpr (GLU) {
+    const float gu = global_factor(gsu, 0);
+    for (int idx = threadIdx.x; idx < 2 * MF * 64; idx += blockDim.x) {
+      const int tf = idx >> 6, l = idx & 63;   // tile t = tf / MF in {0, 1}, fragment f
+      f32x4_t gate = red[0][tf][l], up = red[0][tf + 2 * MF][l];
+      for (int k = 1; k < nw; ++k) {
+        const f32x4_t pg = red[k][tf][l], pu = red[k][tf + 2 * MF][l];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gate[i] += pg[i];
+          up[i] += pu[i];
+        }
+      }
+      f32x4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = glu_act(gate[i] * g, act) * (up[i] * gu);
+      const int t = tf / MF, f = tf % MF;
+      const int64_t m = 16 * f + (l & 15);
+      if (m < M) store4(out, m, n0 + 16 * t + 4 * (l >> 4), N, v, 1.0f);
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < kTiles * MF * 64; idx += blockDim.x) {
     const int tf = idx >> 6, l = idx & 63;
     const int t = tf / MF, f = tf % MF;
@@ -325,6 +365,17 @@ void launch_mf(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, 
   const int64_t npg = K / kPG;
   const int waves = (int)(npg < MAXW ? npg : MAXW);
   skinny_kernel<TX, MF, MAXW><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, N);
+}
+
+template <typename TX, int MF, int MAXW>
+void launch_mf_glu(const TX* x, int64_t M, int64_t K, int64_t F, const uint32_t* w, const uint8_t* sc,
+                   const float* gs, const uint32_t* wu, const uint8_t* scu, const float* gsu, int act, TX* out,
+                   hipStream_t s) {
+  const int64_t blocks = (F + kRows / 2 - 1) / (kRows / 2);
+  const int64_t npg = K / kPG;
+  const int waves = (int)(npg < MAXW ? npg : MAXW);
+  skinny_kernel<TX, MF, MAXW, true><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, F,
+                                                                                       wu, scu, gsu, act);
 }
 
 // 16-bit activations: up to four 16-row fragments in one launch.
@@ -488,6 +539,56 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
         case 2: launch_mf<float, 2, 4>(xf, M, K, N, w, sc, gs, of, s); break;
         case 3: launch_mf<float, 3, 4>(xf, M, K, N, w, sc, gs, of, s); break;
         default: launch_mf<float, 4, 4>(xf, M, K, N, w, sc, gs, of, s); break;
+      }
+      break;
+    }
+  }
+  return true;
+}
+
+bool skinny_glu_applies(int64_t M, int64_t K, int64_t F) {
+  return M >= 2 && M <= 64 && K > 0 && K % kPG == 0 && (F + kRows) * (K / 2) < kMaxPlaneBytes &&
+         64 * K * 4 < kMaxPlaneBytes;
+}
+
+bool launch_skinny_glu(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t F, const uint32_t* w,
+                       const uint8_t* sc, const float* gs, const uint32_t* wu, const uint8_t* scu,
+                       const float* gsu, int act, void* out, hipStream_t s) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
+                         reinterpret_cast<uintptr_t>(sc) | reinterpret_cast<uintptr_t>(wu) |
+                         reinterpret_cast<uintptr_t>(scu)) & 15) == 0;
+  if (!skinny_glu_applies(M, K, F) || !aligned) return false;
+  switch (dt) {
+    case NVFP4_BF16: {
+      const __bf16* xb = static_cast<const __bf16*>(x);
+      __bf16* ob = static_cast<__bf16*>(out);
+      switch ((M + 15) / 16) {
+        case 1: launch_mf_glu<__bf16, 1, 16>(xb, M, K, F, w, sc, gs, wu, scu, gsu, act, ob, s); break;
+        case 2: launch_mf_glu<__bf16, 2, 8>(xb, M, K, F, w, sc, gs, wu, scu, gsu, act, ob, s); break;
+        case 3: launch_mf_glu<__bf16, 3, 4>(xb, M, K, F, w, sc, gs, wu, scu, gsu, act, ob, s); break;
+        default: launch_mf_glu<__bf16, 4, 4>(xb, M, K, F, w, sc, gs, wu, scu, gsu, act, ob, s); break;
+      }
+      break;
+    }
+    case NVFP4_F16: {
+      const _Float16* xh = static_cast<const _Float16*>(x);
+      _Float16* oh = static_cast<_Float16*>(out);
+      switch ((M + 15) / 16) {
+        case 1: launch_mf_glu<_Float16, 1, 16>(xh, M, K, F, w, sc, gs, wu, scu, gsu, act, oh, s); break;
+        case 2: launch_mf_glu<_Float16, 2, 8>(xh, M, K, F, w, sc, gs, wu, scu, gsu, act, oh, s); break;
+        case 3: launch_mf_glu<_Float16, 3, 4>(xh, M, K, F, w, sc, gs, wu, scu, gsu, act, oh, s); break;
+        default: launch_mf_glu<_Float16, 4, 4>(xh, M, K, F, w, sc, gs, wu, scu, gsu, act, oh, s); break;
+      }
+      break;
+    }
+    case NVFP4_F32: {
+      const float* xf = static_cast<const float*>(x);
+      float* of = static_cast<float*>(out);
+      switch ((M + 15) / 16) {
+        case 1: launch_mf_glu<float, 1, 8>(xf, M, K, F, w, sc, gs, wu, scu, gsu, act, of, s); break;
+        case 2: launch_mf_glu<float, 2, 4>(xf, M, K, F, w, sc, gs, wu, scu, gsu, act, of, s); break;
+        case 3: launch_mf_glu<float, 3, 4>(xf, M, K, F, w, sc, gs, wu, scu, gsu, act, of, s); break;
+        default: launch_mf_glu<float, 4, 4>(xf, M, K, F, w, sc, gs, wu, scu, gsu, act, of, s); break;
       }
       break;
     }

@@ -137,7 +137,10 @@ def test_qmm_glu_workspace_size_and_validation(lib):
     assert wsz(1, 5376, 21504, BF16) == 0                          # M = 1: the decode kernel's gated form
     assert wsz(1, 5376, 21504, F32) == 0
     assert wsz(1, 8208, 64, BF16) == 64 * 2 + 128                  # K beyond the decode kernel (> 8192)
-    assert wsz(3, 5376, 21504, BF16) == 3 * 21504 * 2              # other qmv-route sizes
+    assert wsz(3, 5392, 21504, BF16) == 3 * 21504 * 2              # K % 256 != 0: separate projections
+    assert wsz(3, 4096, 14336, BF16) == 0                           # the multi-row kernel's gated form
+    assert wsz(64, 4096, 14336, F32) == 0
+    assert wsz(65, 4096, 14336, F32) == 65 * 14336 * 4             # beyond the multi-row widths
     assert wsz(300, 48, 40, BF16) == (300 * 40 * 2 + 255) // 256 * 256   # K % 64 != 0
     assert wsz(300, 64, 32, F32) == 300 * 32 * 4
     assert wsz(300, 64, 32, F16) == 300 * 32 * 2
@@ -161,6 +164,9 @@ def test_qmm_glu_workspace_size_and_validation(lib):
     assert glu(lib, gu=P(0x100002)) == ALIGN
     assert glu(lib, sg=P(0x100002)) == ALIGN         # the fused kernel reads scale words
     assert glu(lib, su=P(0x100002)) == ALIGN
+    # the multi-row gated form (2 <= M <= 64, K % 256 == 0) reads 16-byte scale chunks
+    assert glu(lib, M=16, K=256, sg=P(0x100004)) == ALIGN
+    assert glu(lib, M=16, K=256, x=P(0x100010), wu=P(0x100008)) == ALIGN
     # the separate-projection case needs its workspace
     assert glu(lib, dt=F32) == SHAPE                 # no workspace given
     assert glu(lib, dt=F32, ws=P(0x200000), nb=300 * 32 * 4 - 1) == SHAPE

@@ -536,6 +536,19 @@ def glu_is_fused(M, K, F, dtype):
     return dtype == torch.bfloat16 and K > 0 and K % 64 == 0 and nv.select_route(M, K, F) == "gemm"
 
 
+def glu_route(M, K, F, dtype):
+    """Which form nvfp4_qmm_glu takes: the fused GEMM, the decode kernel's
+    (M = 1), the multi-row kernel's (2 <= M <= 64, K % 256 == 0), or the two
+    projections and a combine."""
+    if glu_is_fused(M, K, F, dtype):
+        return "gemm"
+    if M == 1 and K % 32 == 0:
+        return "decode"
+    if 2 <= M <= 64 and K % 256 == 0:
+        return "rows"
+    return "separate"
+
+
 ACT_CODES = {"gelu_tanh": 0, "gelu": 1, "silu": 2}
 
 
@@ -585,13 +598,15 @@ def test_qmm_glu_fused_global_scales(gs):
 @pytest.mark.parametrize("act", ["gelu_tanh", "silu"])
 def test_qmm_glu_separate_projections(shape, dtype, act):
     """Every case the fused GEMM does not take: M = 1 is the decode kernel's
-    gated form (one launch); otherwise the projections run through qmm's own
-    routes (qmv at M = 3, the MFMA qmv at 40, the GEMMs at 300 with K = 48 and
-    at 70 with K = 96) into a workspace, then combine."""
+    gated form and M = 3 and 40 (K % 256 == 0) the multi-row kernel's (one
+    launch each); the GEMM-size shapes with K = 48 (300 rows) and K = 96 (70
+    rows) run both projections through qmm's routes into a workspace, then
+    combine."""
     M, K, F = shape
-    if M == 1 and K % 32 == 0:
-        assert glu_workspace(M, K, F, dtype) == 0      # the decode kernel's gated form
-    elif not glu_is_fused(M, K, F, dtype):
+    route = glu_route(M, K, F, dtype)
+    if route in ("decode", "rows"):
+        assert glu_workspace(M, K, F, dtype) == 0
+    elif route == "separate":
         size = M * F * (4 if dtype == torch.float32 else 2)
         assert glu_workspace(M, K, F, dtype) == (size + 255) // 256 * 256
     g, u = glu_planes(6300 + M + K + F, M, K, F)
@@ -611,6 +626,20 @@ def test_qmm_glu_decode_kernel(K, dtype, act):
     g, u = glu_planes(6700 + K, 1, K, 333)
     out, ref = run_glu(g, u, dtype, act)
     assert rel(out, ref) <= TOL[dtype], (K, dtype, act)
+
+
+@pytest.mark.parametrize("M", [2, 16, 17, 33, 64])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+def test_qmm_glu_multirow_kernel(M, dtype):
+    """2 <= M <= 64 with K % 256 == 0 runs the multi-row kernel's gated form
+    in one launch (no workspace): one to four 16-row fragments, one and
+    sixteen pair-groups, a ragged feature count (the last 32-feature block
+    partial), each plane its own global scale."""
+    for K, F, act in ((256, 100, "silu"), (4096, 333, "gelu_tanh")):
+        assert glu_route(M, K, F, dtype) == "rows" and glu_workspace(M, K, F, dtype) == 0
+        g, u = glu_planes(6900 + M + K, M, K, F)
+        out, ref = run_glu(g, u, dtype, act)
+        assert rel(out, ref) <= TOL[dtype], (M, K, dtype)
 
 
 def test_qmm_glu_decode_mlp_shape():
