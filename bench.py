@@ -303,6 +303,43 @@ def settle_clocks(work, ms: float = 100.0):
         torch.cuda.synchronize()
 
 
+def device_state(work, seconds: float = 2.5):
+    """Clocks, power and hotspot temperature while `work` runs back to back
+    (untimed): one `amd-smi metric --clock --power --temperature --json` sample taken in the middle of
+    about `seconds` of launches.  None when the tool is not available."""
+    import shutil
+    import subprocess
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    args = work.prebuilt()
+    fn, n = work.fn, len(args)
+    proc = None
+    t0 = time.perf_counter()
+    i = 0
+    try:
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(16):
+                check(fn(*args[i % n]), "device state")
+                i += 1
+            torch.cuda.synchronize()
+            if proc is None and time.perf_counter() - t0 > 0.5:
+                proc = subprocess.Popen([tool, "metric", "--clock", "--power", "--temperature", "--json"], stdout=subprocess.PIPE,
+                                        stderr=subprocess.DEVNULL, text=True)
+        text = proc.communicate(timeout=30)[0] if proc else ""
+        gpu = json.loads(text[text.find("{"):])["gpu_data"][0]
+        clk = gpu["clock"]
+        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
+        return {"gfx_mhz_mean": round(sum(gfx) / len(gfx), 1), "gfx_mhz_min": min(gfx), "gfx_mhz_max": max(gfx),
+                "mem_mhz": clk["mem_0"]["clk"]["value"], "socket_power_w": gpu["power"]["socket_power"]["value"],
+                "hotspot_c": (gpu.get("temperature") or {}).get("hotspot", {}).get("value"),
+                "sampled_during": f"{i} back-to-back launches over {time.perf_counter() - t0:.1f} s"}
+    except Exception as exc:  # the measurement is context only
+        if proc is not None and proc.poll() is None:
+            proc.kill()
+        return {"error": f"{type(exc).__name__}: {exc}"[:200]}
+
+
 def timed_eager(work, steps: int, warmup: int):
     """Warm up, then time `steps` back-to-back launches (prebuilt ctypes
     arguments, so the host stays ahead of the GPU) between HIP events on the
@@ -616,25 +653,30 @@ def main():
 
     log("prefill")
     pre = Prefill(dec)
-    # ~10 ms of warm-up: the clocks take a few milliseconds of sustained
-    # MFMA load to settle, and a short warm-up times the ramp
-    pdur = eager_launch_us(pre, 16, warmup=20)
+    # the clocks take a few hundred milliseconds of sustained MFMA load to
+    # settle (tens of milliseconds still time the ramp): ~300 ms untimed first
+    settle_clocks(pre, 300.0)
+    pdur = eager_launch_us(pre, 16, warmup=4)
     ptf = pre.flops / (pdur["mean_us"] * 1e-6) / 1e12
 
     # context, measurement only: the vendor bf16 GEMM (torch linear) on the
     # same shape with a dense bf16 weight matrix, the rate a tuned library
     # reaches here without any dequantization
     wd = torch.randn(pre.N, pre.K, device=DEV).to(torch.bfloat16)
-    timed_us(lambda i: torch.nn.functional.linear(pre.x, wd), 20, warmup=10)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:            # the same settling as the prefill above
+        timed_us(lambda i: torch.nn.functional.linear(pre.x, wd), 16, warmup=0)
     dense_us = timed_us(lambda i: torch.nn.functional.linear(pre.x, wd), 16, warmup=0)
     del wd
 
     log("mlp gate/up")
     mlp = MlpGateUp(pre, dec)
-    gdur = eager_launch_us(mlp, 16, warmup=8)
+    settle_clocks(mlp, 300.0)
+    gdur = eager_launch_us(mlp, 16, warmup=2)
     gtf = mlp.flops / (gdur["mean_us"] * 1e-6) / 1e12
     mlp_nows = MlpGateUp(pre, dec, workspace=False)
-    nows_us = eager_launch_us(mlp_nows, 16, warmup=4)["mean_us"]
+    settle_clocks(mlp_nows, 100.0)
+    nows_us = eager_launch_us(mlp_nows, 16, warmup=2)["mean_us"]
     del mlp_nows
     # the same projection unfused, for comparison: two library qmm launches
     # (gate, up) and the activation and product as torch elementwise ops
@@ -669,6 +711,9 @@ def main():
     mr = MultiRow(16, copies=16)
     mdur = eager_launch_us(mr, 64)
     mgbs = mr.bytes / (mdur["mean_us"] * 1e-6) / 1e9
+
+    log("device state (amd-smi during sustained decode, prefill and gated prefill)")
+    state = {"decode": device_state(dec), "prefill": device_state(pre), "mlp_gate_up_prefill": device_state(mlp)}
 
     log("moe gather")
     gs_sorted = Gather(128, True, copies=3)
@@ -709,6 +754,7 @@ def main():
                      "kernel_duration": dur},
         "cpu_baseline": cpu,
         "stream_ceiling": ceiling,
+        "device_state": state,
         "graph_ms_per_step": round(graph_ms, 6),
         "prefill": {"workload": "prefill_gemm_m2048_k5376_n21504_bf16", "value": round(ptf, 2),
                     "unit": "TFLOP/s", "flops": pre.flops,
