@@ -313,7 +313,8 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
 //             holds gate rows f0 + 32w .. f0 + 32w + 31 (plane w, sc, gs) and
 //             the second the up rows of the same features (wu, scu, gsu), so
 //             each lane ends with the gate and up sums of the same outputs and
-//             the epilogue forms act(g_gate * gate) * (g_up * up) in float32.
+//             the epilogue forms act(g_gate * gate) * (g_up * up) in float32,
+//             act being the template argument kAct.
 //   kV3GluSplit: tiles tile0 .. tile0 + tiles_total - 1 of the gated
 //             projection, each shared by `splits` blocks along K as in
 //             kV3Split; block (split, t) writes its unscaled float32 gate and
@@ -321,13 +322,13 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
 //             glu_tail_reduce_kernel finishes them.
 constexpr int kV3Plain = 0, kV3Split = 1, kV3Glu = 2, kV3GluSplit = 3;
 
-template <int kMode>
+template <int kMode, int kAct = 0>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     const __bf16* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
     const float* __restrict__ gs, __bf16* __restrict__ out, int64_t M, int64_t K, int64_t N,
     int64_t tiles_m, int64_t tiles_total, int64_t per_split, float* __restrict__ ws,
     const uint32_t* __restrict__ wu, const uint8_t* __restrict__ scu, const float* __restrict__ gsu,
-    int act, int64_t tile0) {
+    int64_t tile0) {
   constexpr bool kSplit = kMode == kV3Split || kMode == kV3GluSplit;
   constexpr bool kGlu = kMode == kV3Glu || kMode == kV3GluSplit;
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
           const int idx[4] = {(2 * p) * 4 + 2 * d, (2 * p) * 4 + 2 * d + 1, (2 * p + 1) * 4 + 2 * d,
                               (2 * p + 1) * 4 + 2 * d + 1};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = glu_act(acc[0][b][idx[e]] * gg, act) * (acc[1][b][idx[e]] * gu);
+          for (int e = 0; e < 4; ++e) v[e] = glu_act_t<kAct>(acc[0][b][idx[e]] * gg) * (acc[1][b][idx[e]] * gu);
           r0[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
           r1[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
@@ -783,7 +784,7 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
       const int64_t grid = (tiles * sp + 7) / 8 * 8;
       gemm_mfma_v3_kernel<kV3Split><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
           static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, per,
-          static_cast<float*>(ws), nullptr, nullptr, nullptr, 0, 0);
+          static_cast<float*>(ws), nullptr, nullptr, nullptr, 0);
       const int64_t MN = M * N;
       int64_t rgrid = (MN / 4 + 255) / 256;
       if (rgrid > 4096) rgrid = 4096;
@@ -795,7 +796,7 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
     const int64_t grid = (tiles + 7) / 8 * 8;
     gemm_mfma_v3_kernel<kV3Plain><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
         static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, 0, nullptr,
-        nullptr, nullptr, nullptr, 0, 0);
+        nullptr, nullptr, nullptr, 0);
     return;
   }
   const int64_t tiles_m = (M + kBM - 1) / kBM;
@@ -845,9 +846,12 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
   const int64_t dp = tiles - tail;
   if (dp > 0) {
     const int64_t grid = (dp + 7) / 8 * 8;
-    gemm_mfma_v3_kernel<kV3Glu><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-        static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, dp, 0,
-        nullptr, w_up, s_up, gs_up, act, 0);
+    auto glu = gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_SILU>;
+    if (act == NVFP4_ACT_GELU_TANH) glu = gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU_TANH>;
+    if (act == NVFP4_ACT_GELU) glu = gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU>;
+    glu<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate,
+                                                          static_cast<__bf16*>(out), M, K, F, tiles_m, dp, 0, nullptr,
+                                                          w_up, s_up, gs_up, 0);
   }
   if (tail == 0) return;
   const int64_t nslabs = K / kV3BK;
@@ -855,7 +859,7 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
   const int64_t grid = (tail * sp + 7) / 8 * 8;
   gemm_mfma_v3_kernel<kV3GluSplit><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
       static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, tail, per,
-      static_cast<float*>(ws), w_up, s_up, gs_up, act, dp);
+      static_cast<float*>(ws), w_up, s_up, gs_up, dp);
   int64_t rgrid = (tail * 256 * 32 + 255) / 256;
   if (rgrid > 4096) rgrid = 4096;
   glu_tail_reduce_kernel<<<dim3((unsigned)rgrid), dim3(256), 0, s>>>(static_cast<const float*>(ws), sp, tail, dp,

@@ -32,6 +32,15 @@ __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * erfcf(-z 
 // SiLU: z * sigmoid(z).
 __device__ __forceinline__ float silu(float z) { return z * sigmoid(z); }
 
+// The activation fixed at compile time, for kernels that apply it to many
+// elements per lane: no per-element test of the activation type.
+template <int kAct>
+__device__ __forceinline__ float glu_act_t(float z) {
+  if constexpr (kAct == NVFP4_ACT_GELU_TANH) return gelu_tanh(z);
+  else if constexpr (kAct == NVFP4_ACT_GELU) return gelu_erf(z);
+  else return silu(z);
+}
+
 __device__ __forceinline__ float glu_act(float z, int act) {
   if (act == NVFP4_ACT_GELU_TANH) return gelu_tanh(z);
   if (act == NVFP4_ACT_GELU) return gelu_erf(z);
