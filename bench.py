@@ -800,7 +800,7 @@ def main():
                                    "value": round(ugbs, 2), "unit": "GB/s",
                                    "frac_hbm": round(ugbs / HBM_PEAK_GBS, 4),
                                    "distinct_experts": gs_dec.distinct,
-                                   "kernel": "gather_kernel<bf16,4,4,1>", "kernel_duration": udur,
+                                   "kernel": "qmv1_gather_kernel<bf16,1>", "kernel_duration": udur,
                                    "bytes": gs_dec.bytes},
         "other_configs": others,
         "kernel_source_sha": kernel_source_sha(),

@@ -202,6 +202,88 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
   }
 }
 
+// Gather form of the one-row kernel, for GatherQMM with one activation row
+// per pair (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM",
+// "Summary" and "Changes during review": pair r multiplies activation row
+// lhs[r] by expert rhs[r]'s planes, scaled by that expert's global factor;
+// an out-of-range expert or activation row gives exact zeros).  Block (b, r)
+// computes outputs 4b .. 4b+3 of pair r exactly as the one-row kernel does
+// for that expert's plane, so a gathered row equals the plain decode of the
+// same expert bit for bit.
+template <typename TX, int CPL>
+__global__ __launch_bounds__(kThreads) void qmv1_gather_kernel(const TX* __restrict__ x, int64_t X, int64_t K,
+                                                               const int32_t* __restrict__ lhs,
+                                                               const int32_t* __restrict__ rhs, const uint32_t* w,
+                                                               const uint8_t* sc, const float* __restrict__ gs,
+                                                               int64_t E, int64_t N, TX* __restrict__ out) {
+  extern __shared__ uint4 xl[];
+  const int64_t r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t e = rhs[r];
+  const int64_t src = lhs ? (int64_t)lhs[r] : r;
+  TX* o = out + r * N;
+  if (e < 0 || e >= E || src < 0 || src >= X) {   // uniform over the block, before any barrier
+    if (lane == 0 && n < N) store_out(o + n, 0.0f);
+    return;
+  }
+  const int64_t kw = K / 8, ks = K / 16;
+  const int nch = (int)(kw / 4);
+  stage_x_lds(xl, x + src * K, K, lane, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  const rsrc_t wb = byte_buffer(w + e * N * kw, N * kw * 4);
+  const rsrc_t sb = byte_buffer(sc + e * N * ks, N * ks);
+  uint4 wv[CPL];
+  uint32_t sv[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    const bool ok = n < N && c < nch;
+    const uint32_t wo = ok ? (uint32_t)(n * kw * 4 + c * 16) : kOutOfRange;
+    const uint32_t so = ok ? (uint32_t)(n * ks + c * 2) : kOutOfRange;
+    wv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wb, wo, 0, 0));
+    sv[i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sb, so, 0, 0);
+  }
+  constexpr int kLoads = 2 * CPL;
+  __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (kLoads & 0xF) | ((kLoads >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) acc += chunk_dot_lds(wv[i], sv[i], xl, c, (typename LdsElem<TX>::type*)nullptr);
+  }
+  const float v = wave_sum_dpp(acc);
+  if (lane == 0 && n < N) store_out(o + n, v * global_factor(gs, e));
+}
+
+template <typename TX, int CPL>
+void qmv1_gather_launch(const TX* x, int64_t X, int64_t K, const int32_t* lhs, const int32_t* rhs, int64_t R,
+                        const uint32_t* w, const uint8_t* sc, const float* gs, int64_t E, int64_t N, TX* out,
+                        hipStream_t s) {
+  const int64_t blocks = (N + kWaves - 1) / kWaves;
+  qmv1_gather_kernel<TX, CPL><<<dim3((unsigned)blocks, (unsigned)R), dim3(kThreads), staged_x_bytes<TX>(K), s>>>(
+      x, X, K, lhs, rhs, w, sc, gs, E, N, out);
+}
+
+// True when the gather form handles this case (and launches it): as for
+// try_qmv1 with each expert's plane below 2^31 bytes, and at most one grid
+// row per pair.
+template <typename TX>
+bool try_qmv1_gather(const TX* x, int64_t X, int64_t K, const int32_t* lhs, const int32_t* rhs, int64_t R,
+                     const uint32_t* w, const uint8_t* sc, const float* gs, int64_t E, int64_t N, TX* out,
+                     hipStream_t s) {
+  if (K % 32 != 0 || N * (K / 2) >= ((int64_t)1 << 31) || R > nvfp4host::kMaxGridY) return false;
+  switch ((K / 32 + 63) / 64) {
+    case 1: qmv1_gather_launch<TX, 1>(x, X, K, lhs, rhs, R, w, sc, gs, E, N, out, s); return true;
+    case 2: qmv1_gather_launch<TX, 2>(x, X, K, lhs, rhs, R, w, sc, gs, E, N, out, s); return true;
+    case 3: qmv1_gather_launch<TX, 3>(x, X, K, lhs, rhs, R, w, sc, gs, E, N, out, s); return true;
+    case 4: qmv1_gather_launch<TX, 4>(x, X, K, lhs, rhs, R, w, sc, gs, E, N, out, s); return true;
+    default: return false;
+  }
+}
+
 constexpr int kQmv1Rows = 1;
 
 template <typename TX, int CPL>
@@ -267,6 +349,23 @@ bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const 
       return try_qmv1<float>(static_cast<const float*>(x), K, N, w, sc, gs, static_cast<float*>(out), s);
     case NVFP4_F16:
       return try_qmv1<_Float16>(static_cast<const _Float16*>(x), K, N, w, sc, gs, static_cast<_Float16*>(out), s);
+  }
+  return false;
+}
+
+bool launch_decode_gather(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t K, const int32_t* lhs,
+                          const int32_t* rhs, int64_t R, const uint32_t* w, const uint8_t* sc, const float* gs,
+                          int64_t E, int64_t N, void* out, hipStream_t s) {
+  switch (dt) {
+    case NVFP4_BF16:
+      return try_qmv1_gather<__bf16>(static_cast<const __bf16*>(x), X, K, lhs, rhs, R, w, sc, gs, E, N,
+                                     static_cast<__bf16*>(out), s);
+    case NVFP4_F32:
+      return try_qmv1_gather<float>(static_cast<const float*>(x), X, K, lhs, rhs, R, w, sc, gs, E, N,
+                                    static_cast<float*>(out), s);
+    case NVFP4_F16:
+      return try_qmv1_gather<_Float16>(static_cast<const _Float16*>(x), X, K, lhs, rhs, R, w, sc, gs, E, N,
+                                       static_cast<_Float16*>(out), s);
   }
   return false;
 }

@@ -42,6 +42,12 @@ bool skinny_glu_applies(int64_t M, int64_t K, int64_t F);
 bool launch_skinny_glu(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t F, const uint32_t* w,
                        const uint8_t* sc, const float* gs, const uint32_t* wu, const uint8_t* scu,
                        const float* gsu, int act, void* out, hipStream_t s);
+// GatherQMM with one activation row per pair through the decode kernel's
+// gather form; false when that form does not apply (nothing launched).
+bool launch_decode_gather(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t K, const int32_t* lhs,
+                          const int32_t* rhs, int64_t R, const uint32_t* w, const uint8_t* sc, const float* gs,
+                          int64_t E, int64_t N, void* out, hipStream_t s);
+
 bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const uint32_t* w,
                    const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // Dense qmv: out[M,N] = x[M,K] @ W[N,K]^T (transposed plane).

@@ -261,6 +261,10 @@ void gather_dispatch(const TX* x, int64_t X, int64_t M, int64_t K, const int32_t
                      const float* gs, int64_t E, int64_t N, int sorted, TX* out, hipStream_t s) {
   constexpr int ROWS = 4;
   const int64_t gx = (N + kWaves * ROWS - 1) / (kWaves * ROWS);
+  // One activation row per pair: the decode kernel's gather form, whatever
+  // the sorted hint says (so the hint cannot change the result).
+  if (M == 1 && nvfp4host::launch_decode_gather(x, nvfp4_dtype_of<TX>(), X, K, lhs, rhs, R, w, sc, gs, E, N, out, s))
+    return;
   const int64_t group = sorted ? 8 : 1;
   int64_t gy = (R + group - 1) / group;
   if (gy > nvfp4host::kMaxGridY) gy = nvfp4host::kMaxGridY;

@@ -793,6 +793,37 @@ def test_gather_lhs_out_of_range_and_identity_lhs():
     assert oracle.relative_error(host(out), ref) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("K,N", [(2048, 1536), (96, 301), (5376, 64)])
+def test_gather_one_row_pairs_equal_plain_decode(dtype, K, N):
+    """Gather with one activation row per pair (below two rows per expert)
+    runs the decode kernel's gather form: every valid pair's row equals the
+    plain M = 1 qmm of its activation row against its expert's plane, bit for
+    bit, pairs with an out-of-range expert or row give +0.0, and the sorted
+    hint does not change a bit.  Against the oracle too."""
+    # 12 pairs over 8 experts: below two rows per expert, so not the grouped path
+    case = synth.gather_case(5400 + K + N, tokens=6, E=8, N=N, K=K, top_k=2, sort=False, M=1,
+                             with_gs=True, out_of_range=(8, -1))
+    case.lhs = case.lhs.copy()
+    case.lhs[3] = 6            # x has 6 rows: out of range
+    out, ref = run_gather(case, dtype, guard=True)
+    assert oracle.relative_error(host(out), ref) <= TOL[dtype]
+    assert_zero_rows(out, case.rhs, case.lhs, 8, 6)
+    x_t, _ = activations(case.x, dtype)
+    view = torch.int32 if dtype == torch.float32 else torch.int16
+    checked = 0
+    for r in range(case.rhs.shape[0]):
+        e, src = int(case.rhs[r]), int(case.lhs[r])
+        if not (0 <= e < 8 and 0 <= src < 6):
+            continue
+        plain = nv.qmm(x_t[src], words(case.w[e]), u8(case.scales[e]), f32(case.gs[e:e + 1]))
+        assert torch.equal(out[r].view(view), plain.view(view)), r
+        checked += 1
+    assert checked >= 6
+    hinted, _ = run_gather(case, dtype, sorted_flag=True)
+    assert torch.equal(hinted.view(view), out.view(view))
+
+
 def test_gather_sorted_hint_on_unsorted_indices():
     case = synth.gather_case(5300, tokens=9, E=4, N=64, K=128, top_k=3, sort=False, M=1)
     a, ref = run_gather(case, torch.bfloat16, sorted_flag=True)
