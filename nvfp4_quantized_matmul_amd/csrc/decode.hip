@@ -118,6 +118,15 @@ __device__ __forceinline__ rsrc_t byte_buffer(const void* p, int64_t bytes) {
 // An offset no plane reaches (planes stay below 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// Cache policy of the weight and scale plane loads.  The one-row kernel
+// reads each plane byte once per call, so its loads are non-temporal (the
+// `nt` bit): measured 2% faster on the decode workload and 9% on the gated
+// decode form (`sc1` was slower).  In the gather form, pairs that share an
+// expert re-read its plane, which the default policy leaves in the caches:
+// `nt` there measured 3-9% slower.
+constexpr int kPlaneLoad = 2;
+constexpr int kGatherPlaneLoad = 0;
+
 // GLU: the gated projection of an MLP at M = 1 (mlxcel issue "perf(metal):
 // close native NVFP4 prefill gap", "Activation-path follow-up").  The
 // wavefront's two rows are feature f of the gate plane (w, sc, gs) and of the
@@ -165,8 +174,8 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
       const bool ok = n < N && c < nch;
       const uint32_t wo = ok ? (uint32_t)(n * kw * 4 + c * 16) : kOutOfRange;
       const uint32_t so = ok ? (uint32_t)(n * ks + c * 2) : kOutOfRange;
-      wv[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo, 0, 0));
-      sv[r][i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, 0);
+      wv[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo, 0, kPlaneLoad));
+      sv[r][i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sr, so, 0, kPlaneLoad);
     }
   }
   // 2. Wait only for the activation pieces (issued before the 2 R CPL loads
@@ -242,8 +251,8 @@ __global__ __launch_bounds__(kThreads) void qmv1_gather_kernel(const TX* __restr
     const bool ok = n < N && c < nch;
     const uint32_t wo = ok ? (uint32_t)(n * kw * 4 + c * 16) : kOutOfRange;
     const uint32_t so = ok ? (uint32_t)(n * ks + c * 2) : kOutOfRange;
-    wv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wb, wo, 0, 0));
-    sv[i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sb, so, 0, 0);
+    wv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wb, wo, 0, kGatherPlaneLoad));
+    sv[i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(sb, so, 0, kGatherPlaneLoad);
   }
   constexpr int kLoads = 2 * CPL;
   __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (kLoads & 0xF) | ((kLoads >> 4) << 14));
