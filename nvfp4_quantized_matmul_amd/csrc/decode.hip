@@ -10,8 +10,13 @@ using namespace nvfp4dev;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+// Wavefronts per block: eight for the one-row and gather forms, four for the
+// gated form (two rows per wavefront).  Same-process A/B on the decode,
+// gated decode and MoE decode shapes: eight measured 1-3% faster than four
+// for the one-row and gather forms and about 1% slower for the gated form;
+// two and sixteen were slower for all three.
+template <bool GLU> constexpr int qmv1_waves() { return GLU ? 4 : 8; }
+constexpr int kGatherWaves = 8;
 
 // ----------------------------------------------------------------------------
 // Decode kernel for M = 1.
@@ -22,7 +27,8 @@ constexpr int kWaves = kThreads / 64;
 // block; it then waits for the activation pieces only and decodes each chunk
 // as it lands.  Lane l owns chunk positions l, l+64, ... (CPL of them) of
 // each row, so a wave load is 1 KiB of one row.  Waves are short-lived and
-// the grid has N / (4R) blocks; with ~50 VGPRs eight waves fit per SIMD, so
+// the grid has N / (8R) blocks of eight wavefronts (the gated form: four);
+// with ~50 VGPRs eight waves fit per SIMD, so
 // several blocks' loads overlap each other's decode.  Measured against a
 // plain streaming read of the same bytes, this beats a persistent
 // row-streaming kernel whose prefetch depth could not cover HBM latency,
@@ -83,12 +89,13 @@ __device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const
 // padding that is never read.
 #define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <typename TX>
+// W = wavefronts per block: wavefront `wave` copies pieces wave, wave + W, ...
+template <int W, typename TX>
 __device__ __forceinline__ int stage_x_lds(uint4* xl, const TX* x, int64_t K, int lane, int wave) {
   const int64_t n16 = K * (int64_t)sizeof(TX) / 16;
   const int64_t pieces = (n16 + 63) / 64;
   int issued = 0;
-  for (int64_t p = wave; p < pieces; p += kWaves) {
+  for (int64_t p = wave; p < pieces; p += W) {
     int64_t q = p * 64 + lane;
     q = q < n16 ? q : n16 - 1;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(x) + q, NVFP4_LDS(xl + p * 64), 16, 0, 0);
@@ -132,7 +139,7 @@ constexpr int kGatherPlaneLoad = 0;
 // wavefront's two rows are feature f of the gate plane (w, sc, gs) and of the
 // up plane (wu, scu, gsu), and lane 0 stores act(g * gate) * (g_u * up).
 template <typename TX, int CPL, int R, bool GLU = false>
-__global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x,
+__global__ __launch_bounds__(64 * qmv1_waves<GLU>()) void qmv1_kernel(const TX* __restrict__ x,
                                                         const uint32_t* w,
                                                         const uint8_t* sc,
                                                         const float* __restrict__ gs,
@@ -143,14 +150,15 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
   static_assert(!GLU || R == 2, "the gated form streams one gate row and one up row");
   extern __shared__ uint4 xl[];
   const int lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * (GLU ? 1 : R);
+  constexpr int kW = qmv1_waves<GLU>();
+  const int64_t n0 = ((int64_t)blockIdx.x * kW + (threadIdx.x >> 6)) * (GLU ? 1 : R);
   const int64_t kw = K / 8, ks = K / 16, nchunks = kw / 4;
   const int nch = (int)nchunks;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   // 0. The activation row goes straight to LDS (no registers, so nothing
   //    below has to wait for it to land before issuing).  These are this
   //    wave's first vector-memory operations.
-  stage_x_lds(xl, x, K, lane, wave);
+  stage_x_lds<kW>(xl, x, K, lane, wave);
   __builtin_amdgcn_sched_barrier(0);
   // 1. All weight and scale loads of this wave's rows, back to back, as
   //    buffer loads: chunks past the row end and rows past N get an
@@ -216,11 +224,11 @@ __global__ __launch_bounds__(kThreads) void qmv1_kernel(const TX* __restrict__ x
 // "Summary" and "Changes during review": pair r multiplies activation row
 // lhs[r] by expert rhs[r]'s planes, scaled by that expert's global factor;
 // an out-of-range expert or activation row gives exact zeros).  Block (b, r)
-// computes outputs 4b .. 4b+3 of pair r exactly as the one-row kernel does
+// computes outputs 8b .. 8b+7 of pair r exactly as the one-row kernel does
 // for that expert's plane, so a gathered row equals the plain decode of the
 // same expert bit for bit.
 template <typename TX, int CPL>
-__global__ __launch_bounds__(kThreads) void qmv1_gather_kernel(const TX* __restrict__ x, int64_t X, int64_t K,
+__global__ __launch_bounds__(64 * kGatherWaves) void qmv1_gather_kernel(const TX* __restrict__ x, int64_t X, int64_t K,
                                                                const int32_t* __restrict__ lhs,
                                                                const int32_t* __restrict__ rhs, const uint32_t* w,
                                                                const uint8_t* sc, const float* __restrict__ gs,
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void qmv1_gather_kernel(const TX* __restr
   const int64_t r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t n = (int64_t)blockIdx.x * kGatherWaves + wave;
   const int64_t e = rhs[r];
   const int64_t src = lhs ? (int64_t)lhs[r] : r;
   TX* o = out + r * N;
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void qmv1_gather_kernel(const TX* __restr
   }
   const int64_t kw = K / 8, ks = K / 16;
   const int nch = (int)(kw / 4);
-  stage_x_lds(xl, x + src * K, K, lane, wave);
+  stage_x_lds<kGatherWaves>(xl, x + src * K, K, lane, wave);
   __builtin_amdgcn_sched_barrier(0);
   const rsrc_t wb = byte_buffer(w + e * N * kw, N * kw * 4);
   const rsrc_t sb = byte_buffer(sc + e * N * ks, N * ks);
@@ -271,8 +279,8 @@ template <typename TX, int CPL>
 void qmv1_gather_launch(const TX* x, int64_t X, int64_t K, const int32_t* lhs, const int32_t* rhs, int64_t R,
                         const uint32_t* w, const uint8_t* sc, const float* gs, int64_t E, int64_t N, TX* out,
                         hipStream_t s) {
-  const int64_t blocks = (N + kWaves - 1) / kWaves;
-  qmv1_gather_kernel<TX, CPL><<<dim3((unsigned)blocks, (unsigned)R), dim3(kThreads), staged_x_bytes<TX>(K), s>>>(
+  const int64_t blocks = (N + kGatherWaves - 1) / kGatherWaves;
+  qmv1_gather_kernel<TX, CPL><<<dim3((unsigned)blocks, (unsigned)R), dim3(64 * kGatherWaves), staged_x_bytes<TX>(K), s>>>(
       x, X, K, lhs, rhs, w, sc, gs, E, N, out);
 }
 
@@ -298,17 +306,19 @@ constexpr int kQmv1Rows = 1;
 template <typename TX, int CPL>
 void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
                  const float* gs, TX* out, hipStream_t s) {
-  const int64_t blocks = (N + kWaves * kQmv1Rows - 1) / (kWaves * kQmv1Rows);
+  constexpr int kW = qmv1_waves<false>();
+  const int64_t blocks = (N + kW * kQmv1Rows - 1) / (kW * kQmv1Rows);
   const size_t lds = staged_x_bytes<TX>(K);
-  qmv1_kernel<TX, CPL, kQmv1Rows><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(x, w, sc, gs, out, K, N);
+  qmv1_kernel<TX, CPL, kQmv1Rows><<<dim3((unsigned)blocks), dim3(64 * kW), lds, s>>>(x, w, sc, gs, out, K, N);
 }
 
 template <typename TX, int CPL>
 void qmv1_glu_launch(const TX* x, int64_t K, int64_t F, const uint32_t* w, const uint8_t* sc, const float* gs,
                      const uint32_t* wu, const uint8_t* scu, const float* gsu, int act, TX* out, hipStream_t s) {
-  const int64_t blocks = (F + kWaves - 1) / kWaves;
+  constexpr int kW = qmv1_waves<true>();
+  const int64_t blocks = (F + kW - 1) / kW;
   const size_t lds = staged_x_bytes<TX>(K);
-  qmv1_kernel<TX, CPL, 2, true><<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(x, w, sc, gs, out, K, F, wu, scu,
+  qmv1_kernel<TX, CPL, 2, true><<<dim3((unsigned)blocks), dim3(64 * kW), lds, s>>>(x, w, sc, gs, out, K, F, wu, scu,
                                                                                    gsu, act);
 }
 
