@@ -99,6 +99,33 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
   }
 }
 
+// The same expansion with no index division: one block row per matrix, and
+// over a matrix's words taken as one flat array, word i uses scale byte i / 2
+// (every row holds an even number of words).  Lane l of a wavefront writes
+// the 8 outputs of word base + l, so each store instruction covers one
+// contiguous run; the per-element arithmetic is that of dequant_kernel.
+template <typename TO>
+__global__ __launch_bounds__(kThreads) void dequant_flat_kernel(const uint32_t* __restrict__ w,
+                                                                const uint8_t* __restrict__ sc,
+                                                                const float* __restrict__ gs, int64_t wpm,
+                                                                TO* __restrict__ out) {
+  const int64_t mat = blockIdx.y;
+  const uint32_t* wm = w + mat * wpm;
+  const uint8_t* sm = sc + mat * (wpm >> 1);
+  TO* om = out + mat * wpm * 8;
+  const float g = gs ? gs[mat] / kGlobalDivisor : 1.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < wpm; i += stride) {
+    float v[8];
+    decode_word_f32(wm[i], e4m3<0>(sm[i >> 1]), v);
+    if (gs) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] *= g;
+    }
+    store8<TO>(om + i * 8, v);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Quantize: dense matrices -> packed words, E4M3 block scales, global scale
 // (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM", "Summary":
@@ -316,8 +343,22 @@ void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, in
   const int64_t kw = cols / 8;
   const int64_t nwords = batch * rows * kw;
   if (nwords == 0) return;
-  const int64_t grid = grid_for(nwords, kThreads, 1 << 20);
   const int64_t wpm = rows * kw;
+  if (batch <= kMaxGridY) {
+    const dim3 gridf((unsigned)grid_for(wpm, kThreads, 1 << 16), (unsigned)batch);
+    switch (dt) {
+      case NVFP4_F32:
+        dequant_flat_kernel<float><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, static_cast<float*>(out));
+        return;
+      case NVFP4_BF16:
+        dequant_flat_kernel<__bf16><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, static_cast<__bf16*>(out));
+        return;
+      case NVFP4_F16:
+        dequant_flat_kernel<_Float16><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, static_cast<_Float16*>(out));
+        return;
+    }
+  }
+  const int64_t grid = grid_for(nwords, kThreads, 1 << 20);
   switch (dt) {
     case NVFP4_F32:
       dequant_kernel<float><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, sc, gs, nwords, kw, wpm,
