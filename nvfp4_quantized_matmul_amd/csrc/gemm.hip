@@ -745,6 +745,9 @@ int64_t device_cu_count() {
 
 namespace nvfp4host {
 
+// Slabs per piece when `nslabs` slabs are shared by `sp` blocks.
+static int64_t v3_piece(int64_t nslabs, int64_t sp) { return (nslabs + sp - 1) / sp; }
+
 // Splits of K for the MFMA GEMM: with few tiles most compute units would
 // idle, so the slabs of each tile are shared among `splits` blocks and their
 // float32 partials added afterwards.  Model: rounds of blocks times the
@@ -759,7 +762,8 @@ int64_t gemm_splits(int64_t M, int64_t K, int64_t N) {
   int64_t best = 1;
   double best_t = 0.0;
   for (int64_t sp = 1; sp <= 8 && sp <= nslabs / 4; ++sp) {
-    const int64_t per = (nslabs + sp - 1) / sp;
+    const int64_t per = v3_piece(nslabs, sp);
+    if ((sp - 1) * per >= nslabs) continue;   // the last split would be empty
     const double rounds = (double)((tiles * sp + cus - 1) / cus);
     double t = rounds * (per * slab_us + block_us);
     if (sp > 1) t += (double)(sp * 4 + 2) * (double)M * (double)N / bytes_per_us;
@@ -779,8 +783,7 @@ void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint
     const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
     const int64_t sp = ws ? gemm_splits(M, K, N) : 1;
     if (sp > 1 && ws_bytes >= sp * M * N * 4 && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
-      const int64_t nslabs = K / kV3BK;
-      const int64_t per = (nslabs + sp - 1) / sp;
+      const int64_t per = v3_piece(K / kV3BK, sp);
       const int64_t grid = (tiles * sp + 7) / 8 * 8;
       gemm_mfma_v3_kernel<kV3Split><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
           static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, per,
@@ -824,6 +827,10 @@ void glu_tail_split(int64_t M, int64_t K, int64_t F, int64_t* tail_tiles, int64_
   if (sp > 8) sp = 8;
   const int64_t nslabs = K / kV3BK;
   while (sp > 1 && nslabs / sp < 4) --sp;
+  // Pieces of ceil(nslabs / sp) slabs; recount the splits from the piece
+  // length so that none is empty (42 slabs over 8 splits would give pieces
+  // of 6 and an eighth split starting past the end).
+  if (sp > 1) sp = (nslabs + v3_piece(nslabs, sp) - 1) / v3_piece(nslabs, sp);
   if (sp < 2) return;
   *tail_tiles = rem;
   *splits = sp;
@@ -854,8 +861,7 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
                                                           w_up, s_up, gs_up, 0);
   }
   if (tail == 0) return;
-  const int64_t nslabs = K / kV3BK;
-  const int64_t per = (nslabs + sp - 1) / sp;
+  const int64_t per = v3_piece(K / kV3BK, sp);
   const int64_t grid = (tail * sp + 7) / 8 * 8;
   gemm_mfma_v3_kernel<kV3GluSplit><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
       static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, tail, per,

@@ -177,6 +177,43 @@ def test_qmm_glu_workspace_size_and_validation(lib):
     assert glu(lib, F=0, x=None, wg=None, sg=None, wu=None, su=None, out=None) == OK
 
 
+def test_split_counts_leave_no_split_empty(lib):
+    """Both K splits of the bf16 GEMM (the split-K launch for few tiles and
+    the gated projection's tail split) give each split ceil(slabs / splits)
+    slabs; the split count must be recounted from that piece length so the
+    last split still starts inside K (42 slabs over 8 splits would leave the
+    eighth empty and its partial unwritten).  The host reading here assumes
+    256 compute units, as without a GPU."""
+    qws = lib.nvfp4_qmm_workspace_size
+    qws.restype = ctypes.c_int64
+    gws = lib.nvfp4_qmm_glu_workspace_size
+    seen_glu = set()
+    for K in range(64, 8192 + 1, 64):
+        nslabs = K // 64
+        # gated projection: one tile of 256 rows x 128 features, split up to 8 ways
+        b = int(gws(256, K, 128, BF16))
+        if b:
+            assert b % (256 * 256 * 4) == 0
+            sp = b // (256 * 256 * 4)
+            per = -(-nslabs // sp)
+            assert 2 <= sp <= 8 and (sp - 1) * per < nslabs, (K, sp, per)
+            seen_glu.add(sp)
+        # split-K qmm: M = 128 rows, a few tiles
+        for N in (256, 4096):
+            b = int(qws(128, K, N, 1, BF16, 0))
+            if b:
+                assert b % (128 * N * 4) == 0
+                sp = b // (128 * N * 4)
+                per = -(-nslabs // sp)
+                assert 2 <= sp <= 8 and (sp - 1) * per < nslabs, (K, N, sp, per)
+    # K = 2688 (42 slabs) and K = 2112 (33 slabs) split 7 ways, not 8;
+    # K = 1600 (25 slabs) 5 ways, not 6
+    assert gws(256, 2688, 128, BF16) == 7 * 256 * 256 * 4
+    assert gws(256, 2112, 128, BF16) == 7 * 256 * 256 * 4
+    assert gws(256, 1600, 128, BF16) == 5 * 256 * 256 * 4
+    assert 8 in seen_glu
+
+
 def test_stream_read_validation(lib):
     sr = lib.nvfp4_stream_read
     assert sr(FAKE, 24, 64, FAKE, None) == SHAPE       # not a multiple of 16

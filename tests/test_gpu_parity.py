@@ -690,6 +690,37 @@ def test_qmm_glu_fused_tail_split():
     assert oracle.relative_error(host(out), host(plain)) <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("K,splits", [(2688, 7), (2112, 7), (1600, 5)])
+def test_qmm_glu_tail_split_piece_lengths(K, splits):
+    """One tile of 256 rows x 128 features shared by up to 8 blocks along K:
+    at K = 2688 (42 slabs) pieces of 6 slabs need 7 splits, at 2112 (33
+    slabs) pieces of 5 need 7, at 1600 (25 slabs, at most 6 splits of four or
+    more) pieces of 5 need 5.  Every
+    split must start inside K, or its partial would never be written and the
+    reduction would add whatever the workspace held.  The binding's
+    workspace is filled with NaN first, so an unwritten partial would show."""
+    M, F = 256, 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"split sizes are chosen for 256 compute units, this device has {cus}")
+    ws_bytes = glu_workspace(M, K, F, torch.bfloat16)
+    assert ws_bytes == splits * 256 * 256 * 4, ws_bytes
+    g, u = glu_planes(6650 + K, M, K, F)
+    x_t, x_ref = activations(g.x, torch.bfloat16)
+    ref = oracle.qmm_glu(x_ref, g.w, g.scales, g.gs[0], u.w, u.scales, u.gs[0], "gelu_tanh")
+    ws = torch.full((ws_bytes // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    out, check = guarded((M, F), torch.bfloat16)
+    keep = [x_t, words(g.w), u8(g.scales), f32(g.gs), words(u.w), u8(u.scales), f32(u.gs)]
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert nv.load_library().nvfp4_qmm_glu(P(keep[0]), 1, M, K, F, *[P(t) for t in keep[1:]], 0, P(ws), ws_bytes,
+                                           P(out), st) == 0
+    torch.cuda.synchronize()
+    check()
+    assert np.all(np.isfinite(host(out)))
+    assert rel(out, ref) <= TOL[torch.bfloat16], K
+
+
 def test_qmm_glu_full_size_sampled():
     """The prefill MLP's gate/up shape, M=2048, K=5376, F=21504, bf16, through
     the fused kernel that is timed, with the binding's workspace (so the 64
