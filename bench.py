@@ -118,10 +118,13 @@ class Decode:
 
 
 class Prefill:
-    """qmm M=2048, K=5376, N=21504, bf16, gs after the matmul."""
+    """qmm M=2048, K=5376, N=21504, bf16, gs after the matmul.  With
+    `workspace` (what the Python binding passes) the call is nvfp4_qmm_ws
+    with the workspace nvfp4_qmm_workspace_size asks for; without, the
+    one-launch nvfp4_qmm."""
     M, K, N = 2048, 5376, 21504
 
-    def __init__(self, decode: Decode):
+    def __init__(self, decode: Decode, workspace: bool = True):
         wl = synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]
         g = synth.rng(wl["seed"])
         self.x = torch.from_numpy(synth.activations(g, (self.M, self.K))).to(torch.bfloat16).to(DEV)
@@ -129,17 +132,22 @@ class Prefill:
         self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=DEV)
         self.lib = decode.lib
         self.flops = 2.0 * self.M * self.N * self.K
-        self.fn = self.lib.nvfp4_qmm
+        nbytes = int(self.lib.nvfp4_qmm_workspace_size(self.M, self.K, self.N, 1, BF16, 0)) if workspace else 0
+        self.ws_bytes = nbytes
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV) if nbytes > 0 else None
+        self.fn = self.lib.nvfp4_qmm_ws if self.ws is not None else self.lib.nvfp4_qmm
 
     def prebuilt(self):
         st = stream_ptr()
+        if self.ws is not None:
+            return [(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
+                     P(self.ws), self.ws_bytes, P(self.out), st) for c in range(len(self.w))]
         return [(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
                  P(self.out), st) for c in range(len(self.w))]
 
     def launch(self, i):
-        c = i % len(self.w)
-        check(self.lib.nvfp4_qmm(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]),
-                                 P(self.gs), 1, 0, P(self.out), stream_ptr()), "prefill qmm")
+        args = self.prebuilt()[i % len(self.w)]
+        check(self.fn(*args[:-1], stream_ptr()), "prefill qmm")
 
 
 class MlpGateUp:
@@ -389,7 +397,7 @@ def traffic_for(kernel_key: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("decode_source_sha") != kernel_source_sha(DECODE_SOURCES):
+    if vals.get("decode_source_sha", vals.get("source_sha")) != kernel_source_sha(DECODE_SOURCES):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -585,25 +593,46 @@ def cpu_baseline(decode_bytes: float):
 
 COPY_BYTES = 256 << 20
 
+# Workloads for hardware-counter runs: the kernel each one times and the
+# sources that define it (the digest recorded beside its counter summary).
+COUNTER_WORKLOADS = {
+    "decode": ("decode.hip", "nvfp4_device.hpp"),
+    "prefill": ("gemm.hip", "nvfp4_device.hpp"),
+    "multirow16": ("skinny.hip", "nvfp4_device.hpp"),
+    "moe_sorted": ("skinny.hip", "nvfp4_device.hpp"),
+}
 
-def counters_decode(steps: int):
-    """Workload for the FETCH_SIZE / WRITE_SIZE passes: one plain device copy
-    of COPY_BYTES (reads and writes exactly that many bytes, so its counter
-    values give the scale of the counters), then `steps` decode launches
-    rotating over the 8 weight copies, each on a synchronized stream so that
-    every dispatch is counted on its own."""
+
+def counters_run(name: str, steps: int):
+    """Workload for rocprofv3 PMC passes: one plain device copy of COPY_BYTES
+    (it reads and writes exactly that many bytes, so its counter values give
+    the scale of the counters), then `steps` launches of the named workload,
+    each on a synchronized stream so that every dispatch is counted on its
+    own.  Prints the launch count, the algorithmic bytes and flops per
+    launch, and the digest of the kernel's sources."""
     src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device=DEV).fill_(7)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    dec = Decode(copies=8)
+    del src, dst
+    if name == "decode":
+        work = Decode(copies=8)
+    elif name == "prefill":
+        work = Prefill(Decode(copies=8))
+    elif name == "multirow16":
+        work = MultiRow(16, copies=16)
+    else:
+        work = Gather(128, True, copies=3)
+    args = work.prebuilt()
     torch.cuda.synchronize()
     for i in range(steps):
-        dec.launch(i)
+        check(work.fn(*args[i % len(args)]), name)
         torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": COPY_BYTES, "decode_launches": steps, "decode_bytes": dec.bytes,
-                      "decode_source_sha": kernel_source_sha(DECODE_SOURCES)}), flush=True)
+    print(json.dumps({"workload": name, "copy_bytes": COPY_BYTES, "launches": steps,
+                      "bytes_per_launch": getattr(work, "bytes", None),
+                      "flops_per_launch": getattr(work, "flops", None),
+                      "source_sha": kernel_source_sha(COUNTER_WORKLOADS[name])}), flush=True)
 
 
 # ----------------------------------------------------------------------------
@@ -616,10 +645,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
-    ap.add_argument("--counters-decode", action="store_true",
+    ap.add_argument("--counters", choices=sorted(COUNTER_WORKLOADS),
                     help="for hardware-counter runs: a 256 MiB device copy (the calibration of "
-                         "FETCH_SIZE/WRITE_SIZE against known bytes), then `steps` decode launches; "
-                         "prints the launch count and bytes instead of the JSON line")
+                         "FETCH_SIZE/WRITE_SIZE against known bytes), then `steps` launches of the named "
+                         "workload; prints the launch count and bytes instead of the JSON line")
+    ap.add_argument("--counters-decode", action="store_true", help="the same as --counters decode")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the NVFP4 matmul path here is single-GPU "
@@ -630,8 +660,8 @@ def main():
         sys.exit(2)
     steps, warmup = max(1, args.steps), max(0, args.warmup)
     nv.load_library()
-    if args.counters_decode:
-        counters_decode(steps)
+    if args.counters or args.counters_decode:
+        counters_run(args.counters or "decode", steps)
         return
 
     log("decode: building inputs")
