@@ -77,9 +77,11 @@ enum {
   NVFP4_ERR_ROUTE = -5,       /* forced QMV route on a non-transposed weight */
   NVFP4_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
   NVFP4_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
-  NVFP4_ERR_ALIGN = -8        /* a pointer is not aligned as required: activations,
+  NVFP4_ERR_ALIGN = -8,       /* a pointer is not aligned as required: activations,
                                  weights and outputs to 16 bytes, scales to 2 bytes,
                                  float global scales and indices to 4 bytes */
+  NVFP4_ERR_SCRATCH = -9      /* nvfp4_qmm_noalloc: the call needs more than
+                                 NVFP4_STATIC_SCRATCH_BYTES of scratch */
 };
 
 /*
@@ -207,6 +209,36 @@ int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
  */
 int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
                                  nvfp4_dtype_t dtype, nvfp4_route_t route);
+
+/* Size of the library's static device scratch used by nvfp4_qmm_noalloc
+ * (64 MiB; one copy per GPU the library runs on, held until the process
+ * ends). */
+#define NVFP4_STATIC_SCRATCH_BYTES (64LL << 20)
+
+/*
+ * nvfp4_qmm_noalloc -- nvfp4_qmm for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as nvfp4_qmm, and
+ * the same K split as nvfp4_qmm_ws would make with a workspace of
+ * nvfp4_qmm_workspace_size() bytes; its float32 partials live in a static
+ * device array of NVFP4_STATIC_SCRATCH_BYTES owned by the library instead of
+ * a caller workspace, so results equal nvfp4_qmm_ws's bit for bit.  Nothing
+ * is allocated (no hipMalloc/hipFree or allocating library call).  A call
+ * whose split needs more than NVFP4_STATIC_SCRATCH_BYTES returns
+ * NVFP4_ERR_SCRATCH and launches nothing; the device address of the array is
+ * looked up once per device (NVFP4_ERR_HIP if the runtime cannot give it).
+ * All calls on one GPU share that GPU's array and every split writes its
+ * whole slice before it is read, so nothing carries over from an earlier
+ * call; calls that overlap on one GPU (different streams, or another
+ * thread) race on the array and must be serialized by the caller.
+ */
+int nvfp4_qmm_noalloc(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
+                      int64_t N, const uint32_t* w, const uint8_t* scales,
+                      const float* gs, int transpose, nvfp4_route_t route,
+                      void* out, hipStream_t stream);
+
+/* NVFP4_STATIC_SCRATCH_BYTES, as compiled into the library (host only). */
+int64_t nvfp4_static_scratch_bytes(void);
 
 /*
  * nvfp4_qmm_glu -- the gated projection of an MLP against two NVFP4 planes

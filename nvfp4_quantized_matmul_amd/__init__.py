@@ -72,6 +72,8 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_qmm": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_qmm_batched": [vp, c_int, i64, i64, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_qmm_ws": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, i64, vp, vp],
+        "nvfp4_qmm_noalloc": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
+        "nvfp4_static_scratch_bytes": [],
         "nvfp4_qmm_workspace_size": [i64, i64, i64, c_int, c_int, c_int],
         "nvfp4_qmm_glu": [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, c_int, vp, i64, vp, vp],
         "nvfp4_qmm_glu_workspace_size": [i64, i64, i64, c_int],
@@ -89,6 +91,7 @@ def load_library() -> ctypes.CDLL:
     lib.nvfp4_qmv_max_rows.restype = i64
     lib.nvfp4_qmm_workspace_size.restype = i64
     lib.nvfp4_qmm_glu_workspace_size.restype = i64
+    lib.nvfp4_static_scratch_bytes.restype = i64
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib

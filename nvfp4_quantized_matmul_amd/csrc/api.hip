@@ -9,6 +9,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "nvfp4_internal.hpp"
 
@@ -130,6 +131,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_UNSUPPORTED: return "request not implemented";
     case NVFP4_ERR_HIP: return "HIP runtime error at launch";
     case NVFP4_ERR_ALIGN: return "pointer not aligned as required";
+    case NVFP4_ERR_SCRATCH: return "the call needs more scratch than the library's static array holds";
     default: return "unknown status";
   }
 }
@@ -251,6 +253,63 @@ int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64
   qmm_launch(plan, x, dtype, M, K, N, w, scales, gs, transpose, out, stream, workspace, workspace_bytes);
   return launched();
 }
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of nvfp4_qmm_noalloc: a file-scope device array, one copy per GPU,
+// held until the process ends.  Host code never passes the array's name to
+// a kernel (on the host it only stands for the symbol); it uses the device
+// address that hipGetSymbolAddress returns for the current device.
+constexpr int64_t kStaticScratchBytes = NVFP4_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current; nullptr when the runtime cannot give it.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();   // leave no sticky error for the caller's next call
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_qmm_noalloc(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                      const uint8_t* scales, const float* gs, int transpose, nvfp4_route_t route, void* out,
+                      hipStream_t stream) {
+  QmmPlan plan;
+  const int st = qmm_plan(x, dtype, M, K, N, w, scales, gs, transpose, route, out, &plan);
+  if (st != NVFP4_OK) return st;
+  if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
+  const int64_t need = nvfp4_qmm_workspace_size(M, K, N, transpose, dtype, route);
+  if (need < 0) return (int)need;
+  if (need > kStaticScratchBytes) return NVFP4_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && plan.kind == QmmPlan::kGemmMfma) {
+    ws = scratch_address();
+    if (!ws) return NVFP4_ERR_HIP;
+  }
+  qmm_launch(plan, x, dtype, M, K, N, w, scales, gs, transpose, out, stream, ws, ws ? need : 0);
+  return launched();
+}
+
+int64_t nvfp4_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtype_t dtype) {
   if (M < 0 || K < 0 || F < 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;

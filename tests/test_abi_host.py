@@ -17,7 +17,7 @@ import nvfp4_quantized_matmul_amd as nv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 
-OK, NULLPTR, SHAPE, DTYPE, GRID, ROUTE, UNSUP, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULLPTR, SHAPE, DTYPE, GRID, ROUTE, UNSUP, HIP, ALIGN, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 F32, BF16, F16 = 0, 1, 2
 P = ctypes.c_void_p
 FAKE = P(0x100000)       # never dereferenced: every call below fails validation first
@@ -38,6 +38,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_ws",
+                 "nvfp4_qmm_noalloc", "nvfp4_static_scratch_bytes",
                  "nvfp4_qmm_workspace_size", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
                  "nvfp4_qmm_glu", "nvfp4_qmm_glu_workspace_size", "nvfp4_stream_read",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.nvfp4_version() >> 16 == 1
-    for code in (OK, NULLPTR, SHAPE, DTYPE, GRID, ROUTE, UNSUP, HIP, ALIGN):
+    for code in (OK, NULLPTR, SHAPE, DTYPE, GRID, ROUTE, UNSUP, HIP, ALIGN, SCRATCH):
         s = nv.status_string(code)
         assert s and s != "unknown status"
     assert nv.status_string(12345) == "unknown status"
@@ -118,6 +119,26 @@ def test_qmm_workspace_size_and_validation(lib):
     assert qws(*args(ws=None, nb=16)) == SHAPE
     assert qws(*args(ws=MISALIGNED)) == ALIGN
     assert qws(*args(x=None)) == NULLPTR
+
+
+def test_qmm_noalloc_validation(lib):
+    """The no-allocation qmm checks like nvfp4_qmm and refuses, before any
+    launch, a split whose partials exceed the static scratch."""
+    na = lib.nvfp4_qmm_noalloc
+    args = lambda **k: (k.get("x", FAKE), k.get("dt", BF16), k.get("M", 128), k.get("K", 5376),
+                        k.get("N", 21504), FAKE, FAKE, None, 1, 0, k.get("out", FAKE), None)
+    assert lib.nvfp4_static_scratch_bytes() == 64 << 20
+    assert na(*args(x=None)) == NULLPTR
+    assert na(*args(out=MISALIGNED)) == ALIGN
+    assert na(*args(K=24)) == SHAPE
+    assert na(*args(dt=7)) == DTYPE
+    assert na(*args(M=0, x=None, out=None)) == OK
+    # M = 256, K = 8192 on a 36864-row plane splits K three ways into
+    # 3 * 256 * 36864 floats (113 MB): more than the 64 MiB scratch
+    ws = lib.nvfp4_qmm_workspace_size
+    ws.restype = ctypes.c_int64
+    assert ws(256, 8192, 36864, 1, BF16, 0) == 3 * 256 * 36864 * 4
+    assert na(*args(M=256, K=8192, N=36864)) == SCRATCH
 
 
 def glu(lib, x=FAKE, dt=BF16, M=300, K=64, F=32, wg=FAKE, sg=FAKE, gg=None, wu=FAKE, su=FAKE, gu=None, act=0,
