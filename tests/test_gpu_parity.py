@@ -66,6 +66,37 @@ def test_transcode_bit_exact(batch, rows, cols, with_ws2):
         assert gs is None
 
 
+def test_direct_transcode_against_dense_requantization():
+    """P1's acceptance fixture through the library: two ModelOpt triplets
+    transcoded and dequantized (the direct path) against the dense path
+    (float16 reconstruction by the library's dequantize, then its quantize
+    and dequantize).  Every stage equals the oracle's bit for bit, and the
+    dense result stays within the FP8 scale-rounding bound of the direct
+    one."""
+    from test_oracle_pins import dense_requantization, fp8_rounding_bound
+    g = synth.rng(7150)
+    weight, scale, ws2 = synth.modelopt_triplet(g, 2, 48, 256)
+    tw, ts, tg = nv.transcode(torch.from_numpy(weight).to(DEV), torch.from_numpy(scale).to(DEV),
+                              torch.from_numpy(ws2).to(DEV))
+    direct = nv.dequantize(tw, ts, tg)
+    w16 = nv.dequantize(tw, ts, tg, dtype=torch.float16)
+    qw, qs, qg = nv.quantize(w16)
+    dense = nv.dequantize(qw, qs, qg)
+    torch.cuda.synchronize()
+    for b in range(2):
+        w, s, gs = oracle.transcode(weight[b], scale[b], ws2[b:b + 1])
+        want_direct = oracle.dequantize(w, s, gs[0])
+        r16, rqw, rqs, rqg, want_dense = dense_requantization(w, s, gs[0])
+        assert np.array_equal(direct[b].cpu().numpy().view(np.uint32), want_direct.view(np.uint32))
+        assert np.array_equal(w16[b].cpu().numpy().view(np.uint16), r16.view(np.uint16))
+        assert np.array_equal(qw[b].cpu().numpy().view(np.uint32), rqw)
+        assert np.array_equal(qs[b].cpu().numpy(), rqs)
+        assert qg[b].cpu().numpy().view(np.uint32) == rqg.view(np.uint32)[0]
+        assert np.array_equal(dense[b].cpu().numpy().view(np.uint32), want_dense.view(np.uint32))
+        err = np.abs(host(dense[b]) - want_direct.astype(np.float64))
+        assert np.all(err <= fp8_rounding_bound(r16, rqg[0]))
+
+
 def test_transcode_in_place_and_guard_bands():
     g = synth.rng(120)
     wu8, ws, ws2 = synth.modelopt_triplet(g, 2, 33, 64)
@@ -1045,7 +1076,11 @@ def test_gather_random_sweep(i, tokens, E, N, K, top_k, sort, M, dtype):
 # ----------------------------------------------------------------------------
 
 def test_stream_read_reads_every_chunk_and_writes_only_on_the_sentinel():
-    lib = nv.load_library()
+    """The benchmark's streaming-read aid (its own library, not libnvfp4)."""
+    import os
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(nv.library_path()), "libnvfp4_measure.so"))
+    lib.nvfp4_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_void_p]
     sink = torch.zeros(4, dtype=torch.int32, device=DEV)
     zeros = torch.zeros(1 << 20, dtype=torch.int32, device=DEV)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)

@@ -481,6 +481,83 @@ def test_transcode_without_second_scale():
 
 
 # ----------------------------------------------------------------------------
+# Direct transcode against the dense-f16 requantization path (P1 "Acceptance
+# criteria", third bullet, and "Implementation plan" step 4)
+# ----------------------------------------------------------------------------
+
+def dense_requantization(w, scales, gs):
+    """P1's conservative load path, restated with the oracle: reconstruct the
+    dense weights in float16 (round to nearest even of the direct path's
+    dequantized float32 values), quantize them again (the global scale is
+    the matrix maximum) and dequantize the result."""
+    w16 = orc.dequantize(w, scales, gs).astype(np.float16)
+    qw, qs, qg = orc.quantize(w16.astype(np.float32))
+    return w16, qw, qs, qg, orc.dequantize(qw, qs, qg[0])
+
+
+def fp8_rounding_bound(w16, gs_new):
+    """Largest |dense - direct| the requantization can cause, per element
+    (the reading documented with the fixture): for a 16-block whose largest
+    |value| is a, the requantized E4M3 block scale is within 1/16 of
+    a * 448 / gs (or 2^-10 absolute where that is subnormal), so its step
+    d = e4m3 * gs / 2688 is at most (17/16) a / 6 + 2^-10 g; each element
+    moves by at most one such step (half the widest E2M1 gap, 4 to 6), or by
+    a / 16 + 6 * 2^-10 g where it saturates, plus the float16 rounding of the
+    reconstruction (2^-11 relative, 2^-25 absolute below 2^-14).  With
+    g = gs / 2688: (17/96) a + 2^-7 g + 2^-10 a + 2^-24."""
+    a = np.abs(w16.astype(np.float64)).reshape(w16.shape[:-1] + (-1, 16)).max(axis=-1)
+    g = float(gs_new) / 2688.0
+    per_block = (17.0 / 96.0) * a + 2.0 ** -7 * g + 2.0 ** -10 * a + 2.0 ** -24
+    return np.repeat(per_block, 16, axis=-1)
+
+
+def test_direct_transcode_equals_dense_path_when_scales_round_trip():
+    """Every 16-block holds a +-6 nibble, the largest block code is 448 and the
+    second-level scale is a power of two: then the float16 reconstruction is
+    exact, its maximum is 6 * 448 * ws2, every requantized block scale lands
+    on the source code and every element on the source nibble, so the dense
+    path gives the direct planes and sidecar bit for bit (signed zeros
+    included)."""
+    g = synth.rng(7100)
+    weight, scale, _ = synth.modelopt_triplet(g, 1, 24, 256)
+    weight, scale = weight[0].copy(), scale[0].copy()
+    nib = np.stack([weight & 0xF, weight >> 4], axis=-1).reshape(24, 256)
+    blocks = nib.reshape(24, 16, 16)
+    pos = g.integers(0, 16, size=(24, 16))
+    sign = g.integers(0, 2, size=(24, 16)) * 8
+    np.put_along_axis(blocks, pos[..., None], (7 | sign)[..., None], axis=-1)
+    nib = blocks.reshape(24, 128, 2)
+    weight = (nib[..., 0] | (nib[..., 1] << 4)).astype(np.uint8)
+    scale[5, 3] = 0x7E
+    ws2 = np.array([2.0 ** -10], dtype=np.float32)
+    w, s, gs = orc.transcode(weight, scale, ws2)
+    direct = orc.dequantize(w, s, gs[0])
+    w16, qw, qs, qg, dense = dense_requantization(w, s, gs[0])
+    assert np.array_equal(w16.astype(np.float32).view(np.uint32), direct.view(np.uint32))
+    assert np.array_equal(qs, s) and np.array_equal(qw, w)
+    assert qg.view(np.uint32)[0] == gs.view(np.uint32)[0]
+    assert np.array_equal(dense.view(np.uint32), direct.view(np.uint32))
+
+
+def test_direct_transcode_against_dense_path_within_fp8_rounding():
+    """Random triplets (uniform nibbles, normal block codes, log-uniform
+    second-level scale): the dense path differs from the direct transcode by
+    no more than the FP8 scale-rounding bound, element by element, and the
+    bound is not vacuous (a few blocks' scales do change)."""
+    for seed in (7110, 7111, 7112):
+        g = synth.rng(seed)
+        weight, scale, ws2 = synth.modelopt_triplet(g, 1, 32, 256)
+        w, s, gs = orc.transcode(weight[0], scale[0], ws2)
+        direct = orc.dequantize(w, s, gs[0]).astype(np.float64)
+        w16, qw, qs, qg, dense = dense_requantization(w, s, gs[0])
+        err = np.abs(dense.astype(np.float64) - direct)
+        assert np.all(err <= fp8_rounding_bound(w16, qg[0])), seed
+        assert np.any(err > 0), seed
+        # a plain error check that a dropped global scale would fail
+        assert orc.relative_error(dense, direct) <= 0.2
+
+
+# ----------------------------------------------------------------------------
 # Gated MLP projection
 # ----------------------------------------------------------------------------
 
