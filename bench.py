@@ -421,11 +421,21 @@ def timed_us(fn, n: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def measure_library():
+    """The benchmark's measurement aid (libnvfp4_measure.so, built beside the
+    library but not part of it): nvfp4_stream_read."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "nvfp4_quantized_matmul_amd", "libnvfp4_measure.so"))
+    lib.nvfp4_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.nvfp4_stream_read.restype = ctypes.c_int
+    return lib
+
+
 def stream_ceiling(nbytes: int, decode_us: float, copies: int = 8, n: int = 100):
     """The best plain streaming read of the decode workload's byte count on
     this device (nvfp4_stream_read over `copies` rotating buffers, a sweep of
     grid sizes), as context for the decode kernel's HBM fraction."""
-    lib = nv.load_library()
+    lib = measure_library()
     nbytes = nbytes // 16 * 16
     bufs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device=DEV)
             for _ in range(copies)]

@@ -349,17 +349,6 @@ int nvfp4_gather_qmm(const void* x, nvfp4_dtype_t dtype, int64_t X, int64_t M,
                      void* out, hipStream_t stream);
 
 /*
- * nvfp4_stream_read -- measurement aid, not part of the method: reads the
- * `bytes` (a multiple of 16) at device pointer p once, with 16-byte loads in a
- * grid-stride loop over `blocks` workgroups of 256 threads, and writes to
- * sink[0] only if the XOR of all the data equals a fixed sentinel (so the
- * loads are kept).  A benchmark times it over the decode workload's byte
- * count to state the streaming rate the device reaches, beside the published
- * HBM peak.  p 16-byte aligned, sink 4-byte aligned; blocks >= 1.
- */
-int nvfp4_stream_read(const void* p, int64_t bytes, int64_t blocks, uint32_t* sink, hipStream_t stream);
-
-/*
  * nvfp4_select_route -- the route nvfp4_qmm takes for NVFP4_ROUTE_AUTO
  * (host only, no GPU needed).  Returns NVFP4_ROUTE_QMV or NVFP4_ROUTE_GEMM,
  * or a negative status for an invalid request.

@@ -77,7 +77,6 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_qmm_workspace_size": [i64, i64, i64, c_int, c_int, c_int],
         "nvfp4_qmm_glu": [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, c_int, vp, i64, vp, vp],
         "nvfp4_qmm_glu_workspace_size": [i64, i64, i64, c_int],
-        "nvfp4_stream_read": [vp, i64, i64, vp, vp],
         "nvfp4_gather_qmm": [vp, c_int, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, i64, c_int, vp, vp],
         "nvfp4_select_route": [i64, i64, i64, c_int, c_int],
         "nvfp4_qmv_max_rows": [],
@@ -150,6 +149,23 @@ def _require_gpu(*tensors: Optional[torch.Tensor]) -> torch.device:
         elif t.device != dev:
             raise ValueError("all tensors must be on the same device")
     return dev
+
+
+# nvfp4_qmm_workspace_size answers, per device and call shape: a per-token
+# decode call then costs a dictionary lookup instead of a library round trip.
+_QMM_WS_CACHE: dict = {}
+
+
+def _qmm_workspace_bytes(lib, dev: torch.device, M: int, K: int, N: int, tr: int, code: int, route: int) -> int:
+    key = (dev.index, M, K, N, tr, code, route)
+    ws_bytes = _QMM_WS_CACHE.get(key)
+    if ws_bytes is None:
+        ws_bytes = int(lib.nvfp4_qmm_workspace_size(M, K, N, tr, code, route))
+        if ws_bytes < 0:
+            raise NVFP4Error("nvfp4_qmm_workspace_size", ws_bytes)
+        if len(_QMM_WS_CACHE) < 4096:
+            _QMM_WS_CACHE[key] = ws_bytes
+    return ws_bytes
 
 
 def check_planes(w: torch.Tensor, scales: torch.Tensor) -> None:
@@ -300,9 +316,7 @@ def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[tor
         raise ValueError("out has the wrong dtype or shape")
     _require_gpu(out)
     tr = int(bool(transpose))
-    ws_bytes = int(lib.nvfp4_qmm_workspace_size(M, K, N, tr, code, _ROUTES[route]))
-    if ws_bytes < 0:
-        raise NVFP4Error("nvfp4_qmm_workspace_size", ws_bytes)
+    ws_bytes = _qmm_workspace_bytes(lib, dev, M, K, N, tr, code, _ROUTES[route])
     if ws_bytes > 0:
         # split GEMM for few output tiles: the partials live in a workspace
         # from torch's allocator (the library itself never allocates)

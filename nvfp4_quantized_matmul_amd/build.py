@@ -1,8 +1,9 @@
-"""Build libnvfp4.so (HIP kernels + C ABI) for gfx950, in-tree.
+"""Build libnvfp4.so (HIP kernels + C ABI) for gfx950, in-tree, and the
+benchmark's measurement aid libnvfp4_measure.so (not part of the library).
 
 Usage: ``python -m nvfp4_quantized_matmul_amd.build`` (or call :func:`build`).
 Every call recompiles; object files go to ``_build/`` at the repository root
-and the shared library is written next to this file.
+and the shared libraries are written next to this file.
 """
 
 from __future__ import annotations
@@ -20,6 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+MEASURE_DIR = os.path.join(PKG_DIR, "measure")
+MEASURE_LIB_PATH = os.path.join(PKG_DIR, "libnvfp4_measure.so")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are disabled for every device compile.
@@ -37,35 +40,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libnvfp4")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(directory: str = CSRC):
+    return sorted(os.path.join(directory, f) for f in os.listdir(directory) if f.endswith(".hip"))
 
 
 def _compile(src: str, cc: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    obj = os.path.join(BUILD_DIR, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
+    cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", os.path.dirname(src), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libnvfp4.so; returns its path."""
-    cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8")), 16))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, cc), srcs))
-    tmp = LIB_PATH + ".tmp"
+def _link(cc: str, objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libnvfp4.so (and the benchmark's
+    libnvfp4_measure.so); returns the library's path."""
+    cc = hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs, msrcs = sources(), sources(MEASURE_DIR)
+    jobs = max(1, min(len(srcs) + len(msrcs), int(os.environ.get("MAX_JOBS", "8")), 16))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, cc), srcs + msrcs))
+    _link(cc, objs[:len(srcs)], LIB_PATH)
+    _link(cc, objs[len(srcs):], MEASURE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources")
+        print(f"built {LIB_PATH} from {len(srcs)} sources and {MEASURE_LIB_PATH} from {len(msrcs)}")
     return LIB_PATH
 
 

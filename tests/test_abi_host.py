@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
     for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_ws",
                  "nvfp4_qmm_noalloc", "nvfp4_static_scratch_bytes",
                  "nvfp4_qmm_workspace_size", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
-                 "nvfp4_qmm_glu", "nvfp4_qmm_glu_workspace_size", "nvfp4_stream_read",
+                 "nvfp4_qmm_glu", "nvfp4_qmm_glu_workspace_size",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
         assert want in names
 
@@ -235,8 +235,21 @@ def test_split_counts_leave_no_split_empty(lib):
     assert 8 in seen_glu
 
 
-def test_stream_read_validation(lib):
-    sr = lib.nvfp4_stream_read
+def measure_library():
+    """The benchmark's streaming-read aid, a library of its own."""
+    m = ctypes.CDLL(os.path.join(ROOT, "nvfp4_quantized_matmul_amd", "libnvfp4_measure.so"))
+    m.nvfp4_stream_read.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P]
+    m.nvfp4_stream_read.restype = ctypes.c_int
+    return m
+
+
+def test_measurement_aid_is_not_in_the_library(lib):
+    assert not hasattr(lib, "nvfp4_stream_read")
+    assert "nvfp4_stream_read" not in declared_functions()
+
+
+def test_stream_read_validation():
+    sr = measure_library().nvfp4_stream_read
     assert sr(FAKE, 24, 64, FAKE, None) == SHAPE       # not a multiple of 16
     assert sr(FAKE, -16, 64, FAKE, None) == SHAPE
     assert sr(FAKE, 1024, 0, FAKE, None) == SHAPE
