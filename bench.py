@@ -132,6 +132,8 @@ class Prefill:
         self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=DEV)
         self.lib = decode.lib
         self.flops = 2.0 * self.M * self.N * self.K
+        self.bytes = (decode.w[0].numel() * 4 + decode.s[0].numel() + 4 + self.x.numel() * 2
+                      + self.out.numel() * 2)
         nbytes = int(self.lib.nvfp4_qmm_workspace_size(self.M, self.K, self.N, 1, BF16, 0)) if workspace else 0
         self.ws_bytes = nbytes
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV) if nbytes > 0 else None
