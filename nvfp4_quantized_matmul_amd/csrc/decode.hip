@@ -35,12 +35,35 @@ constexpr int kGatherWaves = 8;
 // and two or more rows per wavefront.
 // ----------------------------------------------------------------------------
 
+// LDS placement of the staged activation row.  A weight chunk (32
+// elements) meets PPC 16-byte activation pieces (4 for 2-byte types, 8 for
+// float32), and lane l reads the pieces of chunk l, so the 16 lanes served
+// together read 16 consecutive chunks.  Stored in order, every fourth (2-byte
+// types) or second (float32) chunk would start in the same bank; instead the
+// pieces of chunk c are rotated by its position within the 256-byte bank
+// row, piece q at slot c * PPC + (q + c / CPR) mod PPC with CPR = 256 / (16
+// PPC) chunks per row, which spreads the 16 lanes over all 64 banks.
+template <int PPC>
+__device__ __forceinline__ int x_slot(int c, int q) {
+  constexpr int kCpr = 16 / PPC;
+  return c * PPC + ((q + c / kCpr) & (PPC - 1));
+}
+
+// The global piece stored at LDS slot s (the inverse of x_slot).
+template <int PPC>
+__device__ __forceinline__ int64_t x_piece(int64_t s) {
+  constexpr int kCpr = 16 / PPC;
+  const int64_t c = s / PPC;
+  const int64_t rot = (c / kCpr) & (PPC - 1);
+  return c * PPC + ((s - c * PPC - rot) & (PPC - 1));
+}
+
 // One 16-byte chunk (two scale blocks) against 32 activations.
 __device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const uint4* xl, int c, __bf16*) {
   uint32_t xp[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint4 v = xl[c * 4 + q];
+    const uint4 v = xl[x_slot<4>(c, q)];
     xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
   }
   float p0 = dot_word_bf16(w.x, xp + 0, 0.0f);
@@ -55,7 +78,7 @@ __device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const
   float xv[32];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const uint4 v = xl[c * 8 + q];
+    const uint4 v = xl[x_slot<8>(c, q)];
     xv[4 * q] = __builtin_bit_cast(float, v.x); xv[4 * q + 1] = __builtin_bit_cast(float, v.y);
     xv[4 * q + 2] = __builtin_bit_cast(float, v.z); xv[4 * q + 3] = __builtin_bit_cast(float, v.w);
   }
@@ -71,7 +94,7 @@ __device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const
   float xv[32];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint4 v = xl[c * 4 + q];
+    const uint4 v = xl[x_slot<4>(c, q)];
     const _Float16* h = reinterpret_cast<const _Float16*>(&v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) xv[8 * q + j] = (float)h[j];
@@ -84,9 +107,10 @@ __device__ __forceinline__ float chunk_dot_lds(const uint4& w, uint32_t s, const
 }
 
 // The activation row is copied to LDS by the load-to-LDS path (no
-// registers involved), 1 KiB per wavefront instruction.  The last piece may
-// run past the row: those lanes re-read the row's last 16 bytes into LDS
-// padding that is never read.
+// registers involved), 1 KiB per wavefront instruction; lane l of piece p
+// fills slot 64 p + l with the global piece x_piece(64 p + l).  The last
+// piece may run past the row: those lanes re-read the row's last 16 bytes
+// into LDS padding that is never read.
 #define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // W = wavefronts per block: wavefront `wave` copies pieces wave, wave + W, ...
@@ -95,8 +119,9 @@ __device__ __forceinline__ int stage_x_lds(uint4* xl, const TX* x, int64_t K, in
   const int64_t n16 = K * (int64_t)sizeof(TX) / 16;
   const int64_t pieces = (n16 + 63) / 64;
   int issued = 0;
+  constexpr int kPpc = 32 * (int)sizeof(TX) / 16;   // pieces per 32-element chunk
   for (int64_t p = wave; p < pieces; p += W) {
-    int64_t q = p * 64 + lane;
+    int64_t q = x_piece<kPpc>(p * 64 + lane);
     q = q < n16 ? q : n16 - 1;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(x) + q, NVFP4_LDS(xl + p * 64), 16, 0, 0);
     ++issued;
