@@ -179,7 +179,10 @@ int nvfp4_quantize(const void* w, nvfp4_dtype_t dtype, int64_t batch,
  *           QMV on transpose = 0 is NVFP4_ERR_ROUTE
  *   out     [M, N] of dtype, accumulated in float32
  *
- * K = 0 gives an all-zero output.
+ * On the GEMM route with transpose = 1 and K % 64 == 0, bf16 and f16
+ * activations run on the matrix cores with exact bf16/f16 weight operands;
+ * float32 activations do so only through nvfp4_qmm_ws (below), and every
+ * other case runs a float32 FMA kernel.  K = 0 gives an all-zero output.
  */
 int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
               int64_t N, const uint32_t* w, const uint8_t* scales,
@@ -188,13 +191,20 @@ int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
 
 /*
  * nvfp4_qmm_ws -- nvfp4_qmm with a caller-owned workspace (device, 16-byte
- * aligned, not overlapping x or out).  When the GEMM route has few output
- * tiles for the device (small M, e.g. a prefill chunk of a few hundred rows),
- * the contraction over K is split among several blocks per tile, their
- * float32 partials are kept in the workspace and added in a fixed order by a
- * second kernel, which applies g and rounds; this needs at least
- * nvfp4_qmm_workspace_size() bytes.  With less (or NULL, 0) it is nvfp4_qmm.
- * Results equal nvfp4_qmm's up to float32 summation order.
+ * aligned, not overlapping x or out), used in two cases of the GEMM route
+ * with transpose = 1, each needing at least nvfp4_qmm_workspace_size() bytes:
+ *  * bf16/f16 with few output tiles for the device (small M, e.g. a prefill
+ *    chunk of a few hundred rows): the contraction over K is split among
+ *    several blocks per tile, their float32 partials are kept in the
+ *    workspace and added in a fixed order by a second kernel, which applies
+ *    g and rounds;
+ *  * float32 with K % 64 == 0: each activation is split exactly into three
+ *    bf16 parts (hi + mid + lo == x) written to the workspace as [M, 3K],
+ *    and the bf16 matrix-core GEMM contracts them against the weight taken
+ *    three times, so every product is exact and only the float32
+ *    accumulation order differs from a plain float32 dot product.
+ * With less (or NULL, 0) it is nvfp4_qmm.  Results equal nvfp4_qmm's up to
+ * float32 summation order.
  */
 int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
                  int64_t N, const uint32_t* w, const uint8_t* scales,
@@ -204,8 +214,9 @@ int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
 
 /*
  * nvfp4_qmm_workspace_size -- bytes of workspace nvfp4_qmm_ws uses for this
- * call on the current device (0: it would not split), or a negative status
- * for an invalid request.  Host only.
+ * call on the current device (0: it uses none), or a negative status for an
+ * invalid request: splits * M * N * 4 for a K split, M * 3K * 2 rounded up to
+ * 256 for float32 activations.  Host only.
  */
 int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
                                  nvfp4_dtype_t dtype, nvfp4_route_t route);
@@ -222,10 +233,12 @@ int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
  * the same K split as nvfp4_qmm_ws would make with a workspace of
  * nvfp4_qmm_workspace_size() bytes; its float32 partials live in a static
  * device array of NVFP4_STATIC_SCRATCH_BYTES owned by the library instead of
- * a caller workspace, so results equal nvfp4_qmm_ws's bit for bit.  Nothing
- * is allocated (no hipMalloc/hipFree or allocating library call).  A call
- * whose split needs more than NVFP4_STATIC_SCRATCH_BYTES returns
- * NVFP4_ERR_SCRATCH and launches nothing; the device address of the array is
+ * a caller workspace, so results equal nvfp4_qmm_ws's bit for bit (the same
+ * holds for the three-part copy of float32 activations).  Nothing is
+ * allocated (no hipMalloc/hipFree or allocating library call).  A call whose
+ * K split needs more than NVFP4_STATIC_SCRATCH_BYTES returns
+ * NVFP4_ERR_SCRATCH and launches nothing; float32 activations whose copy does
+ * not fit run nvfp4_qmm's float32 FMA kernel instead.  The device address of the array is
  * looked up once per device (NVFP4_ERR_HIP if the runtime cannot give it).
  * All calls on one GPU share that GPU's array and every split writes its
  * whole slice before it is read, so nothing carries over from an earlier

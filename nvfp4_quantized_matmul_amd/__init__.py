@@ -284,8 +284,9 @@ def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[tor
         ) -> torch.Tensor:
     """out = x @ dequantize(w).T (transpose) or x @ dequantize(w).
 
-    When the GEMM route would leave most compute units idle (few output tiles)
-    the call goes through nvfp4_qmm_ws with a workspace from torch's allocator.
+    When the GEMM route wants a workspace (a K split for few output tiles, or
+    the three-part bf16 copy of float32 activations) the call goes through
+    nvfp4_qmm_ws with a workspace from torch's allocator.
 
     x [..., K] (float32, bfloat16 or float16); w [N, K/8] (transpose) or
     [K, N/8]; scales as for check_planes; gs float32 with one element or None.
@@ -318,8 +319,8 @@ def qmm(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor, gs: Optional[tor
     tr = int(bool(transpose))
     ws_bytes = _qmm_workspace_bytes(lib, dev, M, K, N, tr, code, _ROUTES[route])
     if ws_bytes > 0:
-        # split GEMM for few output tiles: the partials live in a workspace
-        # from torch's allocator (the library itself never allocates)
+        # K-split partials or the float32 split copy live in a workspace from
+        # torch's allocator (the library itself never allocates)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         _check("nvfp4_qmm_ws", lib.nvfp4_qmm_ws(
             _ptr(x), code, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), tr, _ROUTES[route],

@@ -75,9 +75,10 @@ int qmm_plan(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N
   if (r == NVFP4_ROUTE_QMV) {
     if ((N + 15) / 16 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
     plan->kind = QmmPlan::kQmv;
-  } else if (dtype == NVFP4_BF16 && transpose && K % 32 == 0) {
+  } else if (transpose) {
+    // the MFMA GEMM where one of its forms applies, else the generic kernel
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles + 8 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
+    if (tiles + 8 > nvfp4host::kMaxGridX || (N + 63) / 64 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
     plan->kind = QmmPlan::kGemmMfma;
   } else {
     if ((N + 63) / 64 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
@@ -95,7 +96,8 @@ void qmm_launch(const QmmPlan& plan, const void* x, nvfp4_dtype_t dtype, int64_t
     case QmmPlan::kZeroFill: nvfp4host::launch_fill_zero(out, M * N * dtype_size(dtype), stream); break;
     case QmmPlan::kQmv: nvfp4host::launch_qmv(x, dtype, M, K, N, w, scales, gs, out, stream); break;
     case QmmPlan::kGemmMfma:
-      nvfp4host::launch_gemm_mfma(x, M, K, N, w, scales, gs, out, stream, ws, ws_bytes);
+      if (!nvfp4host::launch_gemm_mfma(x, dtype, M, K, N, w, scales, gs, out, stream, ws, ws_bytes))
+        nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
       break;
     case QmmPlan::kGemmGeneric:
       nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
@@ -230,8 +232,8 @@ int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
   int64_t t;
   if (!mul_ok(M, K, &t) || !mul_ok(M, N, &t) || !mul_ok(K, N, &t)) return NVFP4_ERR_SHAPE;
   const int r = route == NVFP4_ROUTE_AUTO ? auto_route : (int)route;
-  if (r != NVFP4_ROUTE_GEMM || dtype != NVFP4_BF16 || !transpose || K % 32 != 0 || M == 0 || N == 0) return 0;
-  return nvfp4host::gemm_workspace_bytes(M, K, N);
+  if (r != NVFP4_ROUTE_GEMM || !transpose || M == 0 || N == 0 || K == 0) return 0;
+  return nvfp4host::gemm_workspace_bytes(M, K, N, dtype);
 }
 
 int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N, const uint32_t* w,
@@ -297,9 +299,14 @@ int nvfp4_qmm_noalloc(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, 
   const int st = qmm_plan(x, dtype, M, K, N, w, scales, gs, transpose, route, out, &plan);
   if (st != NVFP4_OK) return st;
   if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
-  const int64_t need = nvfp4_qmm_workspace_size(M, K, N, transpose, dtype, route);
+  int64_t need = nvfp4_qmm_workspace_size(M, K, N, transpose, dtype, route);
   if (need < 0) return (int)need;
-  if (need > kStaticScratchBytes) return NVFP4_ERR_SCRATCH;
+  if (need > kStaticScratchBytes) {
+    // float32 activations whose three-part copy does not fit take the generic
+    // kernel, which needs no scratch; a K split that does not fit is refused
+    if (dtype != NVFP4_F32) return NVFP4_ERR_SCRATCH;
+    need = 0;
+  }
   void* ws = nullptr;
   if (need > 0 && plan.kind == QmmPlan::kGemmMfma) {
     ws = scratch_address();

@@ -246,25 +246,49 @@ __device__ __forceinline__ void wait_vmem(bool keep_one_slab) {
 }
 
 struct V3Src {
-  const __bf16* x[8];        // activation chunk per x load, slab 0
+  const uint16_t* x[8];      // activation chunk per x load, slab 0 (2-byte elements)
   const uint32_t* w[2];      // packed-word chunk per weight load, slab 0
   const uint8_t* s;          // scale bytes, slab 0
 };
 
-__device__ __forceinline__ void v3_issue(const V3Stage& st, const V3Src& src, int64_t slab, int wave) {
+// Queues slab `slab` of the activations and slab `wslab` of the weights and
+// scales (the same slab, except for the float32 form, whose activation rows
+// are three bf16 parts laid end to end against one weight row).
+__device__ __forceinline__ void v3_issue(const V3Stage& st, const V3Src& src, int64_t slab, int64_t wslab,
+                                         int wave) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_global_load_lds(src.x[i] + slab * kV3BK, NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    __builtin_amdgcn_global_load_lds(src.w[i] + slab * 8, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(src.s + slab * 4, NVFP4_LDS(&st.s[wave * 64]), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(src.w[i] + wslab * 8, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src.s + wslab * 4, NVFP4_LDS(&st.s[wave * 64]), 4, 0, 0);
 }
+
+// 2-byte activation types of the MFMA GEMM: bf16 runs the bf16 MFMA on exact
+// bf16 weight products, f16 the f16 MFMA on exact f16 products.
+template <typename TA> struct V3Ops;
+template <> struct V3Ops<__bf16> {
+  typedef bf16x8_t vec;
+  static __device__ __forceinline__ vec decode(uint32_t w, float s) { return decode_word_bf16(w, s); }
+  static __device__ __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct V3Ops<_Float16> {
+  typedef f16x8_t vec;
+  static __device__ __forceinline__ vec decode(uint32_t w, float s) { return decode_word_f16(w, s); }
+  static __device__ __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 // Four 32x32x16 steps over one slab: lane half h supplies word 4h+j (k in
 // [8(4h+j), 8(4h+j)+8)) and the activation fragment reads the same chunk.
+template <typename TA>
 __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave,
                                            int l32, int h) {
+  typedef typename V3Ops<TA>::vec vec;
   uint4 wr[2];
   float slo[2], shi[2];
 #pragma unroll
@@ -284,20 +308,136 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
     // sink each read back to its multiplies, so the order is pinned.
     // (Reading the next step's fragments during this step's multiplies
     // measured slower: the extra 32 registers cost more than they hide.)
-    bf16x8_t B[8];
+    vec B[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(bf16x8_t, st.x[xslot(b * 32 + l32, 4 * h + j)]);
-    bf16x8_t A[2];
+    for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]);
+    vec A[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
-      A[a] = decode_word_bf16(word, j < 2 ? slo[a] : shi[a]);
+      A[a] = V3Ops<TA>::decode(word, j < 2 ? slo[a] : shi[a]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0], B[b], acc[0][b], 0, 0, 0);
-      acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1], B[b], acc[1][b], 0, 0, 0);
+      acc[0][b] = V3Ops<TA>::mfma(A[0], B[b], acc[0][b]);
+      acc[1][b] = V3Ops<TA>::mfma(A[1], B[b], acc[1][b]);
+    }
+  }
+}
+
+// Zeroes the accumulators, then streams `nslabs` slabs through the three
+// LDS stages and multiplies them.  One step: wait for slab s, release the
+// stage read two steps ago, queue slab s + 2 into it (the last slab again
+// near the end, so the issue is unconditional and the compiler keeps exact
+// track of what is in flight), multiply slab s.  The load counter is
+// drained before returning, so no load-to-LDS lands after the caller moves
+// on.  Weight rows hold wslabs slabs; activation slab s meets weight slab
+// s mod wslabs (the same slab unless the activation rows are longer).
+template <typename TA>
+__device__ __forceinline__ void v3_mainloop(f32x16_t (&acc)[2][8], const V3Stage& st0, const V3Stage& st1,
+                                            const V3Stage& st2, const V3Src& src, int64_t nslabs, int64_t wslabs,
+                                            int wave, int l32, int h) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  const int64_t s1 = nslabs > 1 ? 1 : 0;
+  v3_issue(st0, src, 0, 0, wave);
+  v3_issue(st1, src, s1, s1 < wslabs ? s1 : s1 - wslabs, wave);
+
+#define NVFP4_V3_STEP(S, CUR, FREE)                                              \
+  do {                                                                           \
+    wait_vmem(true);                                                             \
+    __builtin_amdgcn_s_barrier();                                                \
+    const int64_t nx = ((S) + 2 < nslabs) ? (S) + 2 : nslabs - 1;                \
+    v3_issue(FREE, src, nx, nx < wslabs ? nx : nx % wslabs, wave);               \
+    v3_compute<TA>(acc, CUR, wave, l32, h);                                      \
+  } while (0)
+
+  int64_t s = 0;
+  for (; s + 3 <= nslabs; s += 3) {
+    NVFP4_V3_STEP(s, st0, st2);
+    NVFP4_V3_STEP(s + 1, st1, st0);
+    NVFP4_V3_STEP(s + 2, st2, st1);
+  }
+  if (s < nslabs) NVFP4_V3_STEP(s, st0, st2);
+  if (s + 1 < nslabs) NVFP4_V3_STEP(s + 1, st1, st0);
+  wait_vmem(false);   // no load-to-LDS may land after this point
+#undef NVFP4_V3_STEP
+}
+
+// Epilogue of a plain tile: fragment (a, b) holds C[n][m] with n = 8*jj +
+// 4h + i, m = l32.  A swap between the lane halves gives lane h the eight
+// consecutive n 16p + 8h .. 16p + 8h + 7 of jj pair p, stored as one 16-byte
+// write.
+template <typename TO>
+__device__ __forceinline__ void v3_store_tile(const f32x16_t (&acc)[2][8], TO* __restrict__ out, int64_t M,
+                                              int64_t N, int64_t m_blk, int64_t n_blk, float g, int wave,
+                                              int l32, int h) {
+  if constexpr (sizeof(TO) == 4) {
+    // float32 output: lane h holds n = 8 jj + 4h .. 8 jj + 4h + 3 of each
+    // jj, one 16-byte store each.
+    const bool vec4 = (N % 4) == 0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int64_t m = m_blk + b * 32 + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int64_t n = n_blk + wave * 64 + a * 32 + jj * 8 + h * 4;
+          const float v[4] = {acc[a][b][jj * 4] * g, acc[a][b][jj * 4 + 1] * g, acc[a][b][jj * 4 + 2] * g,
+                              acc[a][b][jj * 4 + 3] * g};
+          TO* q = out + m * N + n;
+          if (vec4 && n + 3 < N) {
+            *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (n + i < N) q[i] = v[i];
+          }
+        }
+      }
+  } else {
+    const bool vec_ok = (N % 8) == 0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int64_t m = m_blk + b * 32 + l32;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          uint32_t r0[2], r1[2];
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const TO lo0 = (TO)(acc[a][b][(2 * p) * 4 + 2 * d] * g);
+            const TO hi0 = (TO)(acc[a][b][(2 * p) * 4 + 2 * d + 1] * g);
+            const TO lo1 = (TO)(acc[a][b][(2 * p + 1) * 4 + 2 * d] * g);
+            const TO hi1 = (TO)(acc[a][b][(2 * p + 1) * 4 + 2 * d + 1] * g);
+            r0[d] = (uint32_t)__builtin_bit_cast(uint16_t, lo0) | ((uint32_t)__builtin_bit_cast(uint16_t, hi0) << 16);
+            r1[d] = (uint32_t)__builtin_bit_cast(uint16_t, lo1) | ((uint32_t)__builtin_bit_cast(uint16_t, hi1) << 16);
+          }
+          const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r1[0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(r0[1], r1[1], false, false);
+          const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          const int64_t n = n_blk + wave * 64 + a * 32 + 16 * p + 8 * h;
+          if (m >= M) continue;
+          TO* q = out + m * N + n;
+          if (vec_ok && n + 7 < N) {
+            *reinterpret_cast<uint4*>(q) = v;
+          } else {
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (n + i < N) q[i] = __builtin_bit_cast(TO, (uint16_t)(wv[i / 2] >> (16 * (i % 2))));
+          }
+        }
+      }
     }
   }
 }
@@ -322,13 +462,21 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
 //             glu_tail_reduce_kernel finishes them.
 constexpr int kV3Plain = 0, kV3Split = 1, kV3Glu = 2, kV3GluSplit = 3;
 
-template <int kMode, int kAct = 0>
+//
+// TA is the 2-byte activation type (bf16 or f16, the MFMA operand type) and
+// TO the output type.  K is the activation row length and wslabs the number
+// of 64-element slabs of a weight row; activation slab s meets weight slab
+// s mod wslabs.  They are equal (K = 64 wslabs) except in the float32 form,
+// whose activation rows are three bf16 parts laid end to end (K = 192
+// wslabs): one plane multiplies each part and the three sums accumulate
+// together.
+template <int kMode, int kAct = 0, typename TA = __bf16, typename TO = __bf16>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
-    const __bf16* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
-    const float* __restrict__ gs, __bf16* __restrict__ out, int64_t M, int64_t K, int64_t N,
+    const TA* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
+    const float* __restrict__ gs, TO* __restrict__ out, int64_t M, int64_t K, int64_t N,
     int64_t tiles_m, int64_t tiles_total, int64_t per_split, float* __restrict__ ws,
     const uint32_t* __restrict__ wu, const uint8_t* __restrict__ scu, const float* __restrict__ gsu,
-    int64_t tile0) {
+    int64_t tile0, int64_t wslabs) {
   constexpr bool kSplit = kMode == kV3Split || kMode == kV3GluSplit;
   constexpr bool kGlu = kMode == kV3Glu || kMode == kV3GluSplit;
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
@@ -356,7 +504,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const int64_t kw = K / 8, ks = K / 16;
+  const int64_t kw = wslabs * (kV3BK / 8), ks = wslabs * (kV3BK / 16);   // weight and scale row lengths
   const int64_t nslabs = kSplit ? (all_slabs - first_slab < per_split ? all_slabs - first_slab : per_split)
                                 : all_slabs;
 
@@ -369,7 +517,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     const int r = slot >> 3, c = (slot & 7) ^ swz(r);
     int64_t m = m_blk + r;
     if (m >= M) m = M - 1;
-    src.x[i] = x + m * K + c * 8;
+    src.x[i] = reinterpret_cast<const uint16_t*>(x) + m * K + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -405,38 +553,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   }
 
   f32x16_t acc[2][8];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-  v3_issue(st0, src, 0, wave);
-  v3_issue(st1, src, nslabs > 1 ? 1 : 0, wave);
-
-  // One step: wait for slab s, release the stage read two steps ago, queue
-  // slab s + 2 into it (the last slab again near the end, so the issue is
-  // unconditional and the compiler keeps exact track of what is in
-  // flight), multiply slab s.
-#define NVFP4_V3_STEP(S, CUR, FREE)                                              \
-  do {                                                                           \
-    wait_vmem(true);                                                             \
-    __builtin_amdgcn_s_barrier();                                                \
-    v3_issue(FREE, src, ((S) + 2 < nslabs) ? (S) + 2 : nslabs - 1, wave);        \
-    v3_compute(acc, CUR, wave, l32, h);                                          \
-  } while (0)
-
-  int64_t s = 0;
-  for (; s + 3 <= nslabs; s += 3) {
-    NVFP4_V3_STEP(s, st0, st2);
-    NVFP4_V3_STEP(s + 1, st1, st0);
-    NVFP4_V3_STEP(s + 2, st2, st1);
-  }
-  if (s < nslabs) NVFP4_V3_STEP(s, st0, st2);
-  if (s + 1 < nslabs) NVFP4_V3_STEP(s + 1, st1, st0);
-  wait_vmem(false);   // no load-to-LDS may land after the block ends
-#undef NVFP4_V3_STEP
+  v3_mainloop<TA>(acc, st0, st1, st2, src, nslabs, wslabs, wave, l32, h);
 
   if constexpr (kMode == kV3GluSplit) {
     // Tile-local partial: fragment (a, b) holds C[n][m] with tile row
@@ -522,51 +639,15 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     }
     return;
   }
-  // Epilogue: fragment (a, b) holds C[n][m] with n = 8*jj + 4h + i, m = l32.
-  // A swap between the lane halves gives lane h the eight consecutive n
-  // 16p + 8h .. 16p + 8h + 7 of jj pair p, stored as one 16-byte write.
-  const float g = global_factor(gs, 0);
-  const bool vec_ok = (N % 8) == 0;
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int64_t m = m_blk + b * 32 + l32;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        uint32_t r0[2], r1[2];
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const __bf16 lo0 = (__bf16)(acc[a][b][(2 * p) * 4 + 2 * d] * g);
-          const __bf16 hi0 = (__bf16)(acc[a][b][(2 * p) * 4 + 2 * d + 1] * g);
-          const __bf16 lo1 = (__bf16)(acc[a][b][(2 * p + 1) * 4 + 2 * d] * g);
-          const __bf16 hi1 = (__bf16)(acc[a][b][(2 * p + 1) * 4 + 2 * d + 1] * g);
-          r0[d] = (uint32_t)__builtin_bit_cast(uint16_t, lo0) | ((uint32_t)__builtin_bit_cast(uint16_t, hi0) << 16);
-          r1[d] = (uint32_t)__builtin_bit_cast(uint16_t, lo1) | ((uint32_t)__builtin_bit_cast(uint16_t, hi1) << 16);
-        }
-        const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r1[0], false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(r0[1], r1[1], false, false);
-        const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-        const int64_t n = n_blk + wave * 64 + a * 32 + 16 * p + 8 * h;
-        if (m >= M) continue;
-        __bf16* q = out + m * N + n;
-        if (vec_ok && n + 7 < N) {
-          *reinterpret_cast<uint4*>(q) = v;
-        } else {
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (n + i < N) q[i] = __builtin_bit_cast(__bf16, (uint16_t)(wv[i / 2] >> (16 * (i % 2))));
-        }
-      }
-    }
-  }
+  v3_store_tile<TO>(acc, out, M, N, m_blk, n_blk, global_factor(gs, 0), wave, l32, h);
 }
 
 // out = round(g * sum over splits of ws[split]), splits added in order.
+template <typename TO>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws, int64_t splits,
                                                            int64_t MN, const float* __restrict__ gs,
-                                                           __bf16* __restrict__ out) {
+                                                           TO* __restrict__ out) {
+  static_assert(sizeof(TO) == 2, "partials are reduced into 2-byte outputs");
   const float g = global_factor(gs, 0);
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < MN; e += stride * 4) {
@@ -576,15 +657,44 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
         const float4 u = *reinterpret_cast<const float4*>(ws + sp * MN + e);
         v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
       }
-      const __bf16 o[4] = {(__bf16)(v.x * g), (__bf16)(v.y * g), (__bf16)(v.z * g), (__bf16)(v.w * g)};
+      const TO o[4] = {(TO)(v.x * g), (TO)(v.y * g), (TO)(v.z * g), (TO)(v.w * g)};
       *reinterpret_cast<uint2*>(out + e) = __builtin_bit_cast(uint2, o);
     } else {
       for (int64_t i = e; i < MN; ++i) {
         float v = ws[i];
         for (int64_t sp = 1; sp < splits; ++sp) v += ws[sp * MN + i];
-        out[i] = (__bf16)(v * g);
+        out[i] = (TO)(v * g);
       }
     }
+  }
+}
+
+// float32 activations for the MFMA GEMM: row m of x [M, K] becomes row m of
+// xs [M, 3K], its exact three-part bf16 split (split3_bits) laid end to end:
+// hi in [0, K), mid in [K, 2K), lo in [2K, 3K).  One thread per eight
+// consecutive elements (K % 64 == 0, so a group never crosses a row).
+__global__ __launch_bounds__(256) void split_f32_kernel(const float* __restrict__ x, int64_t M, int64_t K,
+                                                        uint16_t* __restrict__ xs) {
+  const int64_t groups = M * K / 8;
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups; gi += (int64_t)gridDim.x * 256) {
+    const int64_t m = gi / (K / 8), k = (gi - m * (K / 8)) * 8;
+    const uint4 a = reinterpret_cast<const uint4*>(x + m * K + k)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(x + m * K + k)[1];
+    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t hv[8], mv[8], lv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split3_bits(u[e], hv[e], mv[e], lv[e]);
+    uint32_t ph[4], pm[4], pl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ph[j] = __builtin_amdgcn_perm(hv[2 * j + 1], hv[2 * j], 0x07060302u);
+      pm[j] = __builtin_amdgcn_perm(mv[2 * j + 1], mv[2 * j], 0x07060302u);
+      pl[j] = __builtin_amdgcn_perm(lv[2 * j + 1], lv[2 * j], 0x07060302u);
+    }
+    uint16_t* row = xs + m * 3 * K + k;
+    *reinterpret_cast<uint4*>(row) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    *reinterpret_cast<uint4*>(row + K) = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+    *reinterpret_cast<uint4*>(row + 2 * K) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
   }
 }
 
@@ -775,39 +885,77 @@ int64_t gemm_splits(int64_t M, int64_t K, int64_t N) {
   return best;
 }
 
-void launch_gemm_mfma(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* w,
-                      const uint8_t* sc, const float* gs, void* out, hipStream_t s, void* ws,
-                      int64_t ws_bytes) {
-  if (K % kV3BK == 0 && (reinterpret_cast<uintptr_t>(sc) & 3) == 0) {
-    const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
-    const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
-    const int64_t sp = ws ? gemm_splits(M, K, N) : 1;
-    if (sp > 1 && ws_bytes >= sp * M * N * 4 && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
-      const int64_t per = v3_piece(K / kV3BK, sp);
-      const int64_t grid = (tiles * sp + 7) / 8 * 8;
-      gemm_mfma_v3_kernel<kV3Split><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-          static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, per,
-          static_cast<float*>(ws), nullptr, nullptr, nullptr, 0);
-      const int64_t MN = M * N;
-      int64_t rgrid = (MN / 4 + 255) / 256;
-      if (rgrid > 4096) rgrid = 4096;
-      if (rgrid < 1) rgrid = 1;
-      split_reduce_kernel<<<dim3((unsigned)rgrid), dim3(256), 0, s>>>(static_cast<const float*>(ws), sp, MN, gs,
-                                                                     static_cast<__bf16*>(out));
-      return;
-    }
-    const int64_t grid = (tiles + 7) / 8 * 8;
-    gemm_mfma_v3_kernel<kV3Plain><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-        static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, 0, nullptr,
-        nullptr, nullptr, nullptr, 0);
+// The two-byte MFMA GEMM (bf16 or f16 activations and output) with an
+// optional K split through the workspace.
+template <typename T>
+static void launch_v3(const T* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
+                      const float* gs, T* out, hipStream_t s, void* ws, int64_t ws_bytes) {
+  const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
+  const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
+  const int64_t sp = ws ? gemm_splits(M, K, N) : 1;
+  if (sp > 1 && ws_bytes >= sp * M * N * 4 && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
+    const int64_t per = v3_piece(K / kV3BK, sp);
+    const int64_t grid = (tiles * sp + 7) / 8 * 8;
+    gemm_mfma_v3_kernel<kV3Split, 0, T, T><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+        x, w, sc, gs, out, M, K, N, tiles_m, tiles, per, static_cast<float*>(ws), nullptr, nullptr, nullptr, 0,
+        K / kV3BK);
+    const int64_t MN = M * N;
+    int64_t rgrid = (MN / 4 + 255) / 256;
+    if (rgrid > 4096) rgrid = 4096;
+    if (rgrid < 1) rgrid = 1;
+    split_reduce_kernel<T><<<dim3((unsigned)rgrid), dim3(256), 0, s>>>(static_cast<const float*>(ws), sp, MN, gs, out);
     return;
   }
-  const int64_t tiles_m = (M + kBM - 1) / kBM;
-  const int64_t tiles_n = (N + kBN - 1) / kBN;
-  const int64_t tiles = tiles_m * tiles_n;
   const int64_t grid = (tiles + 7) / 8 * 8;
-  gemm_mfma_kernel<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-      static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
+  gemm_mfma_v3_kernel<kV3Plain, 0, T, T><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+      x, w, sc, gs, out, M, K, N, tiles_m, tiles, 0, nullptr, nullptr, nullptr, nullptr, 0, K / kV3BK);
+}
+
+// Workspace of the float32 form: the [M, 3K] bf16 split of the activations.
+static int64_t f32_split_bytes(int64_t M, int64_t K) { return (M * 3 * K * 2 + 255) / 256 * 256; }
+
+bool launch_gemm_mfma(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                      const uint8_t* sc, const float* gs, void* out, hipStream_t s, void* ws, int64_t ws_bytes) {
+  const bool v3 = K % kV3BK == 0 && (reinterpret_cast<uintptr_t>(sc) & 3) == 0;
+  switch (dt) {
+    case NVFP4_BF16:
+      if (v3) {
+        launch_v3(static_cast<const __bf16*>(x), M, K, N, w, sc, gs, static_cast<__bf16*>(out), s, ws, ws_bytes);
+        return true;
+      }
+      if (K % 32 == 0) {
+        const int64_t tiles_m = (M + kBM - 1) / kBM;
+        const int64_t tiles = tiles_m * ((N + kBN - 1) / kBN);
+        const int64_t grid = (tiles + 7) / 8 * 8;
+        gemm_mfma_kernel<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+            static_cast<const __bf16*>(x), w, sc, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles);
+        return true;
+      }
+      return false;
+    case NVFP4_F16:
+      if (!v3) return false;
+      launch_v3(static_cast<const _Float16*>(x), M, K, N, w, sc, gs, static_cast<_Float16*>(out), s, ws, ws_bytes);
+      return true;
+    case NVFP4_F32: {
+      // The exact three-part bf16 split of the activations goes to the
+      // workspace; the bf16 kernel then runs over rows of 3K against the one
+      // plane (weight slab s mod K/64), so the three partial products sum in
+      // its float32 accumulators, and stores float32.
+      if (!v3 || !ws || ws_bytes < f32_split_bytes(M, K) || (reinterpret_cast<uintptr_t>(ws) & 15) != 0) return false;
+      uint16_t* xs = static_cast<uint16_t*>(ws);
+      int64_t sgrid = (M * K / 8 + 255) / 256;
+      if (sgrid > 8192) sgrid = 8192;
+      split_f32_kernel<<<dim3((unsigned)sgrid), dim3(256), 0, s>>>(static_cast<const float*>(x), M, K, xs);
+      const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
+      const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
+      const int64_t grid = (tiles + 7) / 8 * 8;
+      gemm_mfma_v3_kernel<kV3Plain, 0, __bf16, float><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+          reinterpret_cast<const __bf16*>(xs), w, sc, gs, static_cast<float*>(out), M, 3 * K, N, tiles_m, tiles, 0,
+          nullptr, nullptr, nullptr, nullptr, 0, K / kV3BK);
+      return true;
+    }
+  }
+  return false;
 }
 
 // K-split of the gated projection's last, partial round of tiles: with
@@ -858,14 +1006,14 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
     if (act == NVFP4_ACT_GELU) glu = gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU>;
     glu<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate,
                                                           static_cast<__bf16*>(out), M, K, F, tiles_m, dp, 0, nullptr,
-                                                          w_up, s_up, gs_up, 0);
+                                                          w_up, s_up, gs_up, 0, K / kV3BK);
   }
   if (tail == 0) return;
   const int64_t per = v3_piece(K / kV3BK, sp);
   const int64_t grid = (tail * sp + 7) / 8 * 8;
   gemm_mfma_v3_kernel<kV3GluSplit><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
       static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, tail, per,
-      static_cast<float*>(ws), w_up, s_up, gs_up, dp);
+      static_cast<float*>(ws), w_up, s_up, gs_up, dp, K / kV3BK);
   int64_t rgrid = (tail * 256 * 32 + 255) / 256;
   if (rgrid > 4096) rgrid = 4096;
   glu_tail_reduce_kernel<<<dim3((unsigned)rgrid), dim3(256), 0, s>>>(static_cast<const float*>(ws), sp, tail, dp,
@@ -877,7 +1025,8 @@ int64_t gemm_glu_tiles(int64_t M, int64_t F) {
   return ((M + kV3BM - 1) / kV3BM) * ((F + kV3BN / 2 - 1) / (kV3BN / 2));
 }
 
-int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, nvfp4_dtype_t dt) {
+  if (dt == NVFP4_F32) return K % kV3BK == 0 ? f32_split_bytes(M, K) : 0;
   const int64_t sp = gemm_splits(M, K, N);
   return sp > 1 ? sp * M * N * 4 : 0;
 }

@@ -24,6 +24,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 // The divisor of the global scale: 448 (largest E4M3) * 6 (largest E2M1)
 // (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM", "Summary").
@@ -66,6 +68,38 @@ __device__ __forceinline__ bf16x8_t decode_word_bf16(uint32_t w, float s) {
   d[2] = pack_bf16_exact(p2.x * s, p2.y * s);
   d[3] = pack_bf16_exact(p3.x * s, p3.y * s);
   return __builtin_bit_cast(bf16x8_t, d);
+}
+
+// Eight elements of one word times the block scale s as exact f16 (every
+// product e2m1 * e4m3 lies in [2^-10, 2688] with at most 6 significant
+// bits, and every E4M3 value is an f16).  One FP4 convert and one packed
+// f16 multiply per pair.
+__device__ __forceinline__ f16x8_t decode_word_f16(uint32_t w, float s) {
+  const _Float16 h = (_Float16)s;
+  const f16x2_t ss = {h, h};
+  const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  const uint32_t d[4] = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                         __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+  return __builtin_bit_cast(f16x8_t, d);
+}
+
+// A float32 split exactly into three bf16 values whose sum is the input
+// (bit patterns, low halves zero): hi keeps the top 8 significand bits
+// (truncation), mid the next 8 of the remainder, lo the rest (at most 8
+// bits, so exact).  The products of an exact bf16 weight with each part are
+// exact in an MFMA, so three MFMAs accumulate float32-level products.
+// Infinities and NaNs go whole into hi (a NaN keeps a mantissa bit), with mid
+// and lo zero.
+__device__ __forceinline__ void split3_bits(uint32_t u, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const bool fin = (u & 0x7f800000u) != 0x7f800000u;
+  h = (u & 0xffff0000u) | ((!fin && (u & 0x007fffffu)) ? 0x00400000u : 0u);
+  const float r1 = fin ? __builtin_bit_cast(float, u) - __builtin_bit_cast(float, h) : 0.0f;
+  m = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
+  const float r2 = r1 - __builtin_bit_cast(float, m);
+  l = __builtin_bit_cast(uint32_t, r2);
 }
 
 // Eight elements of one word times s, as floats (exact).

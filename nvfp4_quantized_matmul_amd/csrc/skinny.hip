@@ -73,46 +73,16 @@ __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-
 // Activation types: 16-byte loads per MFMA step (8 activations per lane).
 template <typename TX> struct XLoads { static constexpr int n = sizeof(TX) / 2; };
 
-// Eight elements of one word times the block scale s as exact f16 (every
-// product e2m1 * e4m3 lies in [2^-10, 2688] with at most 6 significant
-// bits, and every E4M3 value is an f16).  One FP4 convert and one packed
-// f16 multiply per pair.
-__device__ __forceinline__ f16x8_t decode_word_f16(uint32_t w, float s) {
-  const _Float16 h = (_Float16)s;
-  const f16x2_t ss = {h, h};
-  const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-  const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-  const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-  const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
-  const uint32_t d[4] = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                         __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-  return __builtin_bit_cast(f16x8_t, d);
-}
-
 // Eight float32 activations split exactly into three bf16 vectors whose sum
-// is the input: hi keeps the top 8 significand bits (truncation), mid the
-// next 8 of the remainder, lo the rest (at most 8 bits, so exact).  The
-// products with an exact bf16 weight are exact in the MFMA, so three MFMAs
-// give the float32 products.  Infinities and NaNs go whole into hi (a NaN
-// keeps a mantissa bit), with mid and lo zero.
+// is the input (split3_bits per element).
 __device__ __forceinline__ void split3(const uint4 a, const uint4 b, bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
   const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t h[8], m[8], l[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bool fin = (u[e] & 0x7f800000u) != 0x7f800000u;
-    h[e] = (u[e] & 0xffff0000u) | ((!fin && (u[e] & 0x007fffffu)) ? 0x00400000u : 0u);
-    const float r1 = fin ? __builtin_bit_cast(float, u[e]) - __builtin_bit_cast(float, h[e]) : 0.0f;
-    m[e] = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
-    const float r2 = r1 - __builtin_bit_cast(float, m[e]);
-    l[e] = __builtin_bit_cast(uint32_t, r2);
-  }
+  for (int e = 0; e < 8; ++e) split3_bits(u[e], h[e], m[e], l[e]);
   uint32_t ph[4], pm[4], pl[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

@@ -109,7 +109,14 @@ def test_qmm_workspace_size_and_validation(lib):
     assert small > 0 and small % (128 * 21504 * 4) == 0
     assert ws(2048, 5376, 21504, 1, BF16, 0) == 0            # enough tiles: no split
     assert ws(16, 5376, 21504, 1, BF16, 0) == 0              # qmv route
-    assert ws(128, 5376, 21504, 1, F32, 0) == 0              # generic GEMM: no split
+    assert ws(128, 5376, 21504, 1, F16, 0) == small          # f16 splits like bf16
+    # float32 on the matrix cores: the [M, 3K] bf16 copy, rounded up to 256
+    assert ws(128, 5376, 21504, 1, F32, 0) == 128 * 3 * 5376 * 2
+    assert ws(7, 64, 32, 1, F32, 2) == (7 * 3 * 64 * 2 + 255) // 256 * 256
+    assert ws(2048, 5376, 21504, 1, F32, 0) == 2048 * 3 * 5376 * 2
+    assert ws(128, 5392, 21504, 1, F32, 0) == 0              # K % 64 != 0: float32 FMA kernel
+    assert ws(300, 5376, 21504, 0, F32, 0) == 0              # transpose = 0: float32 FMA kernel
+    assert ws(128, 5392, 21504, 1, BF16, 0) == 0             # K % 64 != 0: no split
     assert ws(128, 5376, 21504, 1, BF16, 1) == 0             # forced qmv
     assert ws(128, 24, 64, 1, BF16, 0) == SHAPE
     qws = lib.nvfp4_qmm_ws

@@ -524,6 +524,95 @@ def test_prefill_gemm_full_size_sampled():
 
 
 # ----------------------------------------------------------------------------
+# f16 and float32 activations on the matrix cores
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(300, 576, 520), (513, 128, 264), (96, 4352, 264), (1, 64, 16)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_gemm_f16_f32_matrix_cores_ragged(shape, dtype):
+    """K % 64 == 0 on the GEMM route: f16 runs the f16 matrix-core GEMM (with
+    the K split for few tiles), float32 the three-part bf16 copy through the
+    binding's workspace; partial row and column tiles; full comparison."""
+    M, K, N = shape
+    code = 0 if dtype == torch.float32 else 2
+    need = int(nv.load_library().nvfp4_qmm_workspace_size(M, K, N, 1, code, 2))
+    if dtype == torch.float32:
+        assert need == (M * 3 * K * 2 + 255) // 256 * 256
+    case = synth.dense_case(4100 + M + K + N, M, K, N, with_gs=True)
+    out, ref = run_qmm(case, dtype, "gemm", guard=True)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+def test_gemm_f32_matrix_cores_match_fma_kernel():
+    """The three-part copy and the float32 FMA kernel (nvfp4_qmm without a
+    workspace) compute the same products exactly; they differ only in float32
+    summation order."""
+    M, K, N = 300, 1024, 520
+    case = synth.dense_case(4190, M, K, N, with_gs=True)
+    x_t, x_ref = activations(case.x, torch.float32)
+    w_t, s_t, gs_t = words(case.w), u8(case.scales), f32(case.gs)
+    lib = nv.load_library()
+    need = int(lib.nvfp4_qmm_workspace_size(M, K, N, 1, 0, 0))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    mfma = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    fma = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    assert lib.nvfp4_qmm_ws(P(x_t), 0, M, K, N, P(w_t), P(s_t), P(gs_t), 1, 0, P(ws), need, P(mfma), None) == 0
+    assert lib.nvfp4_qmm(P(x_t), 0, M, K, N, P(w_t), P(s_t), P(gs_t), 1, 0, P(fma), None) == 0
+    torch.cuda.synchronize()
+    assert oracle.relative_error(host(mfma), host(fma)) <= TOL[torch.float32]
+    ref = oracle.qmm(x_ref, case.w, case.scales, case.gs[0])
+    assert rel(mfma, ref) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_gemm_matrix_cores_nonfinite_activations(dtype):
+    """An infinity or NaN among the activations reaches the outputs of its
+    row as in IEEE arithmetic (inf * 0 is NaN, inf + -inf is NaN), the other
+    rows stay finite; float32 infinities go whole into the copy's first part."""
+    M, K, N = 70, 128, 96
+    case = synth.dense_case(4195, M, K, N, with_gs=True)
+    x = case.x.astype(np.float32).copy()
+    x[0, 5] = np.inf
+    x[1, 7] = -np.inf
+    x[2, 9] = np.nan
+    x[3, 11] = np.inf
+    x[3, 12] = -np.inf
+    x_t, x_ref = activations(x, dtype)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = oracle.qmm(x_ref, case.w, case.scales, case.gs[0])
+    out = nv.qmm(x_t, words(case.w), u8(case.scales), f32(case.gs), route="gemm")
+    got = host(out)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    assert np.array_equal(np.sign(got[np.isinf(ref)]), np.sign(ref[np.isinf(ref)]))
+    assert np.isfinite(ref[4:]).all()
+    assert oracle.relative_error(got[4:], ref[4:]) <= TOL[dtype]
+
+
+def test_prefill_plane_f16_and_f32_sampled():
+    """The prefill plane (M=2048, K=5376, N=21504) with f16 activations and
+    with float32 activations (the three-part copy, 66 MB, through the
+    binding's workspace): 45 sampled rows of each against the oracle."""
+    wl = synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]
+    case = synth.dense_case(wl["seed"] + 7, 2048, 5376, 21504, with_gs=True)
+    w_t, s_t, gs_t = words(case.w), u8(case.scales), f32(case.gs)
+    rows = np.unique(np.concatenate([np.arange(0, 2048, 53), [1, 255, 256, 1023, 2047]]))
+    got, refs = [], []
+    for dtype in (torch.float16, torch.float32):
+        x_t, x_ref = activations(case.x, dtype)
+        out = nv.qmm(x_t, w_t, s_t, gs_t)
+        torch.cuda.synchronize()
+        got.append(host(out)[rows])
+        refs.append(x_ref[rows])
+        del x_t, out
+    ref = oracle.qmm(np.concatenate(refs), case.w, case.scales, case.gs[0])
+    n = len(rows)
+    assert oracle.relative_error(got[0], ref[:n]) <= TOL[torch.float16]
+    assert oracle.relative_error(got[1], ref[n:]) <= TOL[torch.float32]
+
+
+# ----------------------------------------------------------------------------
 # gated MLP projection
 # ----------------------------------------------------------------------------
 

@@ -1,8 +1,9 @@
 """nvfp4_qmm_noalloc: nvfp4_qmm for callers that cannot allocate, whose
-K-split partials live in the library's static device scratch.  Checked
-through the C ABI against nvfp4_qmm_ws with a caller workspace (the same
-kernels and split, so the same bits) on two calls in a row, the second
-smaller, and against the oracle."""
+K-split partials (or the three-part bf16 copy of float32 activations) live
+in the library's static device scratch.  Checked through the C ABI against
+nvfp4_qmm_ws with a caller workspace (the same kernels and split, so the
+same bits) on two calls in a row, the second smaller, and against the
+oracle."""
 
 import ctypes
 
@@ -62,14 +63,31 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
         assert oracle.relative_error(host(got)[rows], ref) <= TOL[torch.bfloat16]
 
 
-def test_noalloc_without_a_split_is_nvfp4_qmm():
-    """Shapes that need no scratch (decode qmv, float32 GEMM) give nvfp4_qmm's
-    bits."""
+def test_noalloc_float32_copy_matches_workspace_call_twice_second_smaller():
+    """Float32 activations on the matrix cores: the three-part copy lives in
+    the scratch; the second, smaller call reuses its start."""
+    lib = nv.load_library()
+    for seed, (M, K, N) in ((9105, (300, 512, 272)), (9106, (70, 192, 96))):
+        case, x_t, x_ref, w_t, s_t, gs_t = _inputs(seed, M, K, N, torch.float32)
+        want, need = _with_workspace(lib, 0, x_t, w_t, s_t, gs_t, M, K, N)
+        assert need == (M * 3 * K * 2 + 255) // 256 * 256, (M, K, N, need)
+        got = _noalloc(lib, 0, x_t, w_t, s_t, gs_t, M, K, N)
+        assert torch.equal(got, want), (M, K, N)
+        ref = oracle.qmm(x_ref, case.w, case.scales, case.gs[0])
+        assert oracle.relative_error(host(got), ref) <= TOL[torch.float32]
+
+
+def test_noalloc_without_scratch_is_nvfp4_qmm():
+    """Shapes that need no scratch (decode qmv; float32 with K % 64 != 0) and
+    float32 whose copy would not fit the scratch (M * 3K * 2 bytes above
+    64 MiB: the float32 FMA kernel) give nvfp4_qmm's bits."""
     lib = nv.load_library()
     for seed, (M, K, N), dt, code in ((9110, (1, 4096, 1000), torch.bfloat16, 1),
-                                      (9111, (300, 512, 272), torch.float32, 0)):
+                                      (9111, (300, 528, 272), torch.float32, 0),
+                                      (9112, (2048, 5632, 128), torch.float32, 0)):
         case, x_t, x_ref, w_t, s_t, gs_t = _inputs(seed, M, K, N, dt)
-        assert int(lib.nvfp4_qmm_workspace_size(M, K, N, 1, code, 0)) == 0
+        need = int(lib.nvfp4_qmm_workspace_size(M, K, N, 1, code, 0))
+        assert need == 0 or need > lib.nvfp4_static_scratch_bytes(), (M, K, N, need)
         got = _noalloc(lib, code, x_t, w_t, s_t, gs_t, M, K, N)
         want = torch.empty((M, N), dtype=dt, device=DEV)
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
