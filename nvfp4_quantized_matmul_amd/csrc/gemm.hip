@@ -203,10 +203,15 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_kernel(
 // block (into the A operand of two 32x32x16 MFMAs) and feeds 8 activation
 // fragments.  Per slab, each wavefront issues 11 direct-to-LDS loads (8 of
 // activations, 2 of packed weights, 1 of scale bytes) and nothing passes
-// through registers on the way.  Three LDS stages keep two slabs in flight
-// while a third is multiplied; a stage is released by an explicit wait on
-// the vector-memory counter followed by a plain barrier (a fenced
-// __syncthreads would drain the prefetches).  The activation and weight
+// through registers on the way.  The activations move through three LDS
+// stages (two slabs in flight while a third is multiplied) and the small
+// weight and scale parts through six, queued three slabs ahead: loads
+// complete in issue order, so a weight load queued before a slab's
+// activations must land by the time those are waited for, and queuing it a
+// step earlier gives the weights (streamed from HBM, where the activations
+// mostly hit L2) three slab times instead of two.  A stage is released by an
+// explicit wait on the vector-memory counter followed by a plain barrier (a
+// fenced __syncthreads would drain the prefetches).  The activation and weight
 // tiles keep their 16-byte chunks XOR-swizzled by row, which keeps the
 // fragment reads free of bank conflicts without padding.
 // ----------------------------------------------------------------------------
@@ -214,13 +219,19 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_kernel(
 constexpr int kV3BN = 256;
 constexpr int kV3BM = 256;
 constexpr int kV3BK = 64;
-constexpr int kV3LoadsPerSlab = 11;   // direct-to-LDS loads per wavefront per slab
+// Direct-to-LDS loads per wavefront and step: 8 of activations, then 2 of
+// packed weights and 1 of scale bytes.  When a step starts, the loads queued
+// after that slab's activations are the weights of the same step (3) and the
+// whole next step (11): 14 may still be in flight.
+constexpr int kV3WaitLoads = 14;
 
 // One pipeline stage in LDS: the activation tile (256 rows x 8 swizzled
 // 16-byte chunks, 32 KiB), the packed words (256 rows x 32 bytes, 8 KiB)
-// and the scale bytes (256 rows x 4 bytes, 1 KiB) of one slab.  Each part is
-// its own __shared__ array so the compiler can tell a stage being read from
-// the stages being filled and does not wait for those loads.
+// and the scale bytes (256 rows x 4 bytes, 1 KiB) of one slab; a step reads
+// the activation part of one activation stage and the weight and scale parts
+// of one weight stage.  Each part is its own __shared__ array so the compiler
+// can tell a stage being read from the stages being filled and does not wait
+// for those loads.
 struct V3Stage {
   uint4* x;
   uint4* w;
@@ -238,9 +249,9 @@ __device__ __forceinline__ int xslot(int row, int chunk) { return row * 8 + (chu
 __device__ __forceinline__ int wslot(int row, int half) { return row * 2 + (half ^ ((row >> 3) & 1)); }
 
 // vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
-__device__ __forceinline__ void wait_vmem(bool keep_one_slab) {
-  if (keep_one_slab)
-    __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | kV3LoadsPerSlab);
+__device__ __forceinline__ void wait_vmem(bool keep_in_flight) {
+  if (keep_in_flight)
+    __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | kV3WaitLoads);
   else
     __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | 0);
 }
@@ -254,11 +265,12 @@ struct V3Src {
 // Queues slab `slab` of the activations and slab `wslab` of the weights and
 // scales (the same slab, except for the float32 form, whose activation rows
 // are three bf16 parts laid end to end against one weight row).
-__device__ __forceinline__ void v3_issue(const V3Stage& st, const V3Src& src, int64_t slab, int64_t wslab,
-                                         int wave) {
+__device__ __forceinline__ void v3_issue_x(const V3Stage& st, const V3Src& src, int64_t slab, int wave) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_global_load_lds(src.x[i] + slab * kV3BK, NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, 0, 0);
+}
+__device__ __forceinline__ void v3_issue_w(const V3Stage& st, const V3Src& src, int64_t wslab, int wave) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     __builtin_amdgcn_global_load_lds(src.w[i] + wslab * 8, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, 0, 0);
@@ -326,17 +338,18 @@ __device__ __forceinline__ void v3_compute(f32x16_t (&acc)[2][8], const V3Stage&
   }
 }
 
-// Zeroes the accumulators, then streams `nslabs` slabs through the three
-// LDS stages and multiplies them.  One step: wait for slab s, release the
-// stage read two steps ago, queue slab s + 2 into it (the last slab again
-// near the end, so the issue is unconditional and the compiler keeps exact
-// track of what is in flight), multiply slab s.  The load counter is
+// Zeroes the accumulators, then streams `nslabs` slabs through the LDS
+// stages (X: activations, three; W: weights and scales, six) and multiplies
+// them.  One step: wait for slab s, release the stages read in earlier
+// steps, queue the activations of slab s + 2 and the weights of slab s + 3
+// (the last slab again near the end, so the issue is unconditional and the
+// compiler keeps exact track of what is in flight), multiply slab s.  The load counter is
 // drained before returning, so no load-to-LDS lands after the caller moves
 // on.  Weight rows hold wslabs slabs; activation slab s meets weight slab
 // s mod wslabs (the same slab unless the activation rows are longer).
 template <typename TA>
-__device__ __forceinline__ void v3_mainloop(f32x16_t (&acc)[2][8], const V3Stage& st0, const V3Stage& st1,
-                                            const V3Stage& st2, const V3Src& src, int64_t nslabs, int64_t wslabs,
+__device__ __forceinline__ void v3_mainloop(f32x16_t (&acc)[2][8], const V3Stage (&X)[3], const V3Stage (&W)[6],
+                                            const V3Src& src, int64_t nslabs, int64_t wslabs,
                                             int wave, int l32, int h) {
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -345,27 +358,38 @@ __device__ __forceinline__ void v3_mainloop(f32x16_t (&acc)[2][8], const V3Stage
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  const int64_t s1 = nslabs > 1 ? 1 : 0;
-  v3_issue(st0, src, 0, 0, wave);
-  v3_issue(st1, src, s1, s1 < wslabs ? s1 : s1 - wslabs, wave);
+  auto wsl = [&](int64_t q) { return q < wslabs ? q : q % wslabs; };
+  auto cl = [&](int64_t q) { return q < nslabs ? q : nslabs - 1; };
+  v3_issue_w(W[0], src, 0, wave);
+  v3_issue_x(X[0], src, 0, wave);
+  v3_issue_w(W[1], src, wsl(cl(1)), wave);
+  v3_issue_x(X[1], src, cl(1), wave);
+  v3_issue_w(W[2], src, wsl(cl(2)), wave);
 
-#define NVFP4_V3_STEP(S, CUR, FREE)                                              \
-  do {                                                                           \
-    wait_vmem(true);                                                             \
-    __builtin_amdgcn_s_barrier();                                                \
-    const int64_t nx = ((S) + 2 < nslabs) ? (S) + 2 : nslabs - 1;                \
-    v3_issue(FREE, src, nx, nx < wslabs ? nx : nx % wslabs, wave);               \
-    v3_compute<TA>(acc, CUR, wave, l32, h);                                      \
+#define NVFP4_V3_STEP(S, XI, WI)                                                     \
+  do {                                                                               \
+    wait_vmem(true);                                                                 \
+    __builtin_amdgcn_s_barrier();                                                    \
+    v3_issue_x(X[((XI) + 2) % 3], src, cl((S) + 2), wave);                           \
+    v3_issue_w(W[((WI) + 3) % 6], src, wsl(cl((S) + 3)), wave);                      \
+    const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
+    v3_compute<TA>(acc, cur, wave, l32, h);                                          \
   } while (0)
 
   int64_t s = 0;
-  for (; s + 3 <= nslabs; s += 3) {
-    NVFP4_V3_STEP(s, st0, st2);
-    NVFP4_V3_STEP(s + 1, st1, st0);
-    NVFP4_V3_STEP(s + 2, st2, st1);
+  for (; s + 6 <= nslabs; s += 6) {
+    NVFP4_V3_STEP(s, 0, 0);
+    NVFP4_V3_STEP(s + 1, 1, 1);
+    NVFP4_V3_STEP(s + 2, 2, 2);
+    NVFP4_V3_STEP(s + 3, 0, 3);
+    NVFP4_V3_STEP(s + 4, 1, 4);
+    NVFP4_V3_STEP(s + 5, 2, 5);
   }
-  if (s < nslabs) NVFP4_V3_STEP(s, st0, st2);
-  if (s + 1 < nslabs) NVFP4_V3_STEP(s + 1, st1, st0);
+  if (s < nslabs) NVFP4_V3_STEP(s, 0, 0);
+  if (s + 1 < nslabs) NVFP4_V3_STEP(s + 1, 1, 1);
+  if (s + 2 < nslabs) NVFP4_V3_STEP(s + 2, 2, 2);
+  if (s + 3 < nslabs) NVFP4_V3_STEP(s + 3, 0, 3);
+  if (s + 4 < nslabs) NVFP4_V3_STEP(s + 4, 1, 4);
   wait_vmem(false);   // no load-to-LDS may land after this point
 #undef NVFP4_V3_STEP
 }
@@ -480,9 +504,11 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   constexpr bool kSplit = kMode == kV3Split || kMode == kV3GluSplit;
   constexpr bool kGlu = kMode == kV3Glu || kMode == kV3GluSplit;
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
-  __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2];
-  __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN];
+  __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2], w3[kV3BN * 2], w4[kV3BN * 2], w5[kV3BN * 2];
+  __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN], s3[kV3BN], s4[kV3BN], s5[kV3BN];
   const V3Stage st0{x0, w0, s0}, st1{x1, w1, s1}, st2{x2, w2, s2};
+  const V3Stage XS[3] = {st0, st1, st2};   // only .x is read
+  const V3Stage WS[6] = {st0, st1, st2, {x0, w3, s3}, {x0, w4, s4}, {x0, w5, s5}};   // only .w and .s
 
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
   // each XCD gets a contiguous run of logical tiles (activation tiles
@@ -553,7 +579,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   }
 
   f32x16_t acc[2][8];
-  v3_mainloop<TA>(acc, st0, st1, st2, src, nslabs, wslabs, wave, l32, h);
+  v3_mainloop<TA>(acc, XS, WS, src, nslabs, wslabs, wave, l32, h);
 
   if constexpr (kMode == kV3GluSplit) {
     // Tile-local partial: fragment (a, b) holds C[n][m] with tile row
