@@ -19,7 +19,9 @@ batched-weight qmm and the load-time transcode / dequantize / quantize.
 Kernel durations come from HIP events around back-to-back launches on the
 launch stream.  ``stream_ceiling`` is the best plain streaming read of the
 decode workload's byte count on the same device, for context.  The CPU oracle is timed on the host
-on the full decode workload (cpu_baseline).
+on the full decode workload (cpu_baseline) and on the full prefill workload
+(prefill.cpu_baseline).  The prefill is also timed with f16 and float32
+activations.
 
 Prints one JSON line.
 """
@@ -117,24 +119,31 @@ class Decode:
                  P(self.out), st) for c in range(self.copies)]
 
 
+DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
 class Prefill:
-    """qmm M=2048, K=5376, N=21504, bf16, gs after the matmul.  With
-    `workspace` (what the Python binding passes) the call is nvfp4_qmm_ws
-    with the workspace nvfp4_qmm_workspace_size asks for; without, the
-    one-launch nvfp4_qmm."""
+    """qmm M=2048, K=5376, N=21504, gs after the matmul; bf16 activations and
+    output unless `dtype` says otherwise.  With `workspace` (what the Python
+    binding passes) the call is nvfp4_qmm_ws with the workspace
+    nvfp4_qmm_workspace_size asks for (none for bf16 and f16 at this size;
+    the three-part bf16 copy for float32); without, the one-launch
+    nvfp4_qmm."""
     M, K, N = 2048, 5376, 21504
 
-    def __init__(self, decode: Decode, workspace: bool = True):
+    def __init__(self, decode: Decode, workspace: bool = True, dtype=torch.bfloat16):
         wl = synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]
         g = synth.rng(wl["seed"])
-        self.x = torch.from_numpy(synth.activations(g, (self.M, self.K))).to(torch.bfloat16).to(DEV)
+        self.code = DTYPE_CODES[dtype]
+        self.x = torch.from_numpy(synth.activations(g, (self.M, self.K))).to(dtype).to(DEV)
         self.w, self.s, self.gs = decode.w, decode.s, decode.gs   # same plane distribution
-        self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=DEV)
+        self.out = torch.empty((self.M, self.N), dtype=dtype, device=DEV)
         self.lib = decode.lib
         self.flops = 2.0 * self.M * self.N * self.K
-        self.bytes = (decode.w[0].numel() * 4 + decode.s[0].numel() + 4 + self.x.numel() * 2
-                      + self.out.numel() * 2)
-        nbytes = int(self.lib.nvfp4_qmm_workspace_size(self.M, self.K, self.N, 1, BF16, 0)) if workspace else 0
+        esz = self.x.element_size()
+        self.bytes = (decode.w[0].numel() * 4 + decode.s[0].numel() + 4 + self.x.numel() * esz
+                      + self.out.numel() * esz)
+        nbytes = int(self.lib.nvfp4_qmm_workspace_size(self.M, self.K, self.N, 1, self.code, 0)) if workspace else 0
         self.ws_bytes = nbytes
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV) if nbytes > 0 else None
         self.fn = self.lib.nvfp4_qmm_ws if self.ws is not None else self.lib.nvfp4_qmm
@@ -142,9 +151,9 @@ class Prefill:
     def prebuilt(self):
         st = stream_ptr()
         if self.ws is not None:
-            return [(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
+            return [(P(self.x), self.code, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
                      P(self.ws), self.ws_bytes, P(self.out), st) for c in range(len(self.w))]
-        return [(P(self.x), BF16, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
+        return [(P(self.x), self.code, self.M, self.K, self.N, P(self.w[c]), P(self.s[c]), P(self.gs), 1, 0,
                  P(self.out), st) for c in range(len(self.w))]
 
     def launch(self, i):
@@ -578,29 +587,63 @@ def other_configs():
     return out
 
 
-def cpu_baseline(decode_bytes: float):
-    """The oracle, untuned, on the host: one full decode workload."""
-    import oracle
+def _host_threads():
+    """(BLAS threads, host cores this process may run on)."""
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        blas_threads = 1
-    wl = synth.WORKLOADS["decode_qmv_m1_k5376_n21504_bf16"]
-    case = synth.dense_case(wl["seed"], 1, 5376, 21504, with_gs=True)
-    x = torch.from_numpy(case.x).to(torch.bfloat16).float().numpy()
+        blas = 1
+    try:
+        host = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - not on Linux
+        host = os.cpu_count() or 1
+    return int(blas), int(host)
+
+
+def _time_oracle(fn, max_reps: int, max_wall: float):
     reps, wall, cpu = 0, 0.0, 0.0
-    while reps < 3 and wall < 10.0:
+    while reps < max_reps and (reps == 0 or wall < max_wall):
         t0, c0 = time.perf_counter(), time.process_time()
-        oracle.qmm(x, case.w, case.scales, case.gs[0])
+        fn()
         wall += time.perf_counter() - t0
         cpu += time.process_time() - c0
         reps += 1
-    per = wall / reps
-    return {"value": round(decode_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
+    return reps, wall / reps, cpu / wall
+
+
+def cpu_baseline(decode_bytes: float):
+    """The oracle, untuned, on the host: the full decode workload (dequantize
+    the plane, then the float64 product), passes repeated up to about 10 s.  `cores` is the BLAS thread count
+    (the most threads the oracle runs at once: its dequantize runs on one,
+    its matmul on all); `host_cores` the cores the process may use."""
+    import oracle
+    blas, host = _host_threads()
+    wl = synth.WORKLOADS["decode_qmv_m1_k5376_n21504_bf16"]
+    case = synth.dense_case(wl["seed"], 1, 5376, 21504, with_gs=True)
+    x = torch.from_numpy(case.x).to(torch.bfloat16).float().numpy()
+    reps, per, busy = _time_oracle(lambda: oracle.qmm(x, case.w, case.scales, case.gs[0]), 16, 10.0)
+    return {"value": round(decode_bytes / per / 1e9, 4), "unit": "GB/s", "cores": blas, "host_cores": host,
+            "mean_busy_cores": round(busy, 2), "kind": "oracle",
             "sample": f"full decode workload M=1 K=5376 N=21504 (dequantize + float64 matmul), "
-                      f"{reps} pass(es), {per:.2f} s per pass, mean busy cores {cpu / wall:.2f}"}
+                      f"{reps} pass(es), {per:.2f} s per pass"}
+
+
+def cpu_baseline_prefill(flops: float):
+    """The oracle on the whole prefill workload (M=2048, K=5376, N=21504: the
+    plane dequantized once per pass, then a float64 product of all 2048
+    rows), passes repeated up to about 10 s, as TFLOP/s of the workload's
+    2MNK."""
+    import oracle
+    blas, host = _host_threads()
+    wl = synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]
+    case = synth.dense_case(wl["seed"], 1, 5376, 21504, with_gs=True)
+    x = torch.from_numpy(synth.activations(synth.rng(wl["seed"]), (2048, 5376))).to(torch.bfloat16).float().numpy()
+    reps, per, busy = _time_oracle(lambda: oracle.qmm(x, case.w, case.scales, case.gs[0]), 12, 10.0)
+    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": blas, "host_cores": host,
+            "mean_busy_cores": round(busy, 2), "kind": "oracle",
+            "sample": f"full prefill workload M=2048 K=5376 N=21504 (dequantize + float64 matmul), "
+                      f"{reps} pass(es), {per:.2f} s per pass"}
 
 
 COPY_BYTES = 256 << 20
@@ -711,6 +754,19 @@ def main():
     dense_us = timed_us(lambda i: torch.nn.functional.linear(pre.x, wd), 16, warmup=0)
     del wd
 
+    # the same call with f16 activations (the f16 matrix-core GEMM) and with
+    # float32 activations (their three-part bf16 copy in the binding's
+    # workspace, then the bf16 GEMM over 3K)
+    dt_rates = {}
+    for name, dt in (("f16", torch.float16), ("f32", torch.float32)):
+        pw = Prefill(dec, dtype=dt)
+        settle_clocks(pw, 150.0)
+        d = eager_launch_us(pw, 16, warmup=2)
+        dt_rates[name] = {"value": round(pw.flops / (d["mean_us"] * 1e-6) / 1e12, 2), "unit": "TFLOP/s",
+                          "workspace_bytes": pw.ws_bytes, "kernel_duration": d,
+                          "frac_of_bf16_peak": round(pw.flops / (d["mean_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del pw
+
     log("mlp gate/up")
     mlp = MlpGateUp(pre, dec)
     settle_clocks(mlp, 300.0)
@@ -768,10 +824,11 @@ def main():
     log("other configurations")
     others = other_configs()
 
-    cpu = None
+    cpu = cpu_pre = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(dec.bytes)
+        cpu_pre = cpu_baseline_prefill(pre.flops)
 
     line = {
         "metric": METRIC,
@@ -803,6 +860,9 @@ def main():
                     "roofline": {"bound": "mfma", "achieved": round(ptf, 2), "peak": BF16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(ptf / BF16_PEAK_TFLOPS, 4),
                                  "kernel": "gemm_mfma_v3_kernel", "kernel_duration": pdur},
+                    "cpu_baseline": cpu_pre,
+                    "activations_f16": dt_rates["f16"],
+                    "activations_f32": dt_rates["f32"],
                     "dense_bf16_gemm_reference": {"us": round(dense_us, 2),
                                                   "TFLOP_s": round(pre.flops / dense_us / 1e6, 2),
                                                   "note": "torch linear (vendor library) with a dense bf16 "
