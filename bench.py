@@ -479,8 +479,9 @@ def other_configs():
     """The remaining configurations, each as microseconds per call and the
     rate against its roofline: the tiny qmv (latency), multi-row qmv at every
     M in f32 and bf16, MoE unsorted decode at B = 1, 2, 4, 8, batched-weight
-    qmm (all back-to-back C ABI launches with prebuilt arguments), and the
-    load-time transcode, dequantize and quantize (through the binding)."""
+    qmm (all back-to-back C ABI launches with prebuilt arguments), the
+    load-time transcode, dequantize and quantize (through the binding), and
+    the non-transposed qmm at the prefill shape."""
     out = {}
     lib = nv.load_library()
     # tiny qmv: M=1, K=1024, N=512, f32, no global scale (launch-latency bound)
@@ -584,6 +585,30 @@ def other_configs():
     load["quantize_bf16"] = {"us": round(us, 2), "GB_s": round(q_bytes / us / 1e3, 1), "bytes": q_bytes,
                              "note": "two passes over the dense input (matrix maximum, then blocks)"}
     out["load_time_21504x5376"] = load
+    # non-transposed plane [K, N/8] at the prefill shape: the dense route
+    # (the plane's exact transposed bf16 copy in the workspace, then the
+    # matrix-core GEMM), beside the generic kernel (nvfp4_qmm, no workspace)
+    M, K, N = 2048, 5376, 21504
+    cn = synth.dense_case(synth.WORKLOADS["prefill_gemm_m2048_k5376_n21504_bf16"]["seed"] + 11, 1, K, N,
+                          transpose=False, with_gs=True)
+    wn, sn, gn = words_dev(cn.w), u8_dev(cn.scales), torch.from_numpy(cn.gs).to(DEV)
+    xn = torch.from_numpy(synth.activations(synth.rng(12), (M, K))).to(torch.bfloat16).to(DEV)
+    yn = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    need = int(lib.nvfp4_qmm_workspace_size(M, K, N, 0, BF16, 0))
+    wsn = torch.empty(need, dtype=torch.uint8, device=DEV)
+    st = stream_ptr()
+    dargs = (P(xn), BF16, M, K, N, P(wn), P(sn), P(gn), 0, 0, P(wsn), need, P(yn), st)
+    gargs = (P(xn), BF16, M, K, N, P(wn), P(sn), P(gn), 0, 0, P(yn), st)
+    flops = 2.0 * M * N * K
+    dense_us = timed_us(lambda i: lib.nvfp4_qmm_ws(*dargs), 16, warmup=4)
+    generic_us = timed_us(lambda i: lib.nvfp4_qmm(*gargs), 2, warmup=1)
+    out["non_transposed_gemm_m2048_k5376_n21504_bf16"] = {
+        "us": round(dense_us, 2), "TFLOP_s": round(flops / dense_us / 1e6, 2),
+        "frac_of_bf16_peak": round(flops / dense_us / 1e6 / BF16_PEAK_TFLOPS, 4), "workspace_bytes": need,
+        "generic_us": round(generic_us, 2),
+        "note": "us: nvfp4_qmm_ws (dense transposed copy of the plane, then the matrix-core GEMM on it); "
+                "generic_us: nvfp4_qmm without a workspace (float32 FMA kernel)"}
+    del wsn
     return out
 
 

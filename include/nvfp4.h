@@ -181,8 +181,9 @@ int nvfp4_quantize(const void* w, nvfp4_dtype_t dtype, int64_t batch,
  *
  * On the GEMM route with transpose = 1 and K % 64 == 0, bf16 and f16
  * activations run on the matrix cores with exact bf16/f16 weight operands;
- * float32 activations do so only through nvfp4_qmm_ws (below), and every
- * other case runs a float32 FMA kernel.  K = 0 gives an all-zero output.
+ * float32 activations, and non-transposed planes with K % 64 == 0, do so
+ * only through nvfp4_qmm_ws (below), and every other case runs a float32 FMA
+ * kernel.  K = 0 gives an all-zero output.
  */
 int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
               int64_t N, const uint32_t* w, const uint8_t* scales,
@@ -191,8 +192,8 @@ int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
 
 /*
  * nvfp4_qmm_ws -- nvfp4_qmm with a caller-owned workspace (device, 16-byte
- * aligned, not overlapping x or out), used in two cases of the GEMM route
- * with transpose = 1, each needing at least nvfp4_qmm_workspace_size() bytes:
+ * aligned, not overlapping x or out), used in three cases of the GEMM
+ * route, each needing at least nvfp4_qmm_workspace_size() bytes:
  *  * bf16/f16 with few output tiles for the device (small M, e.g. a prefill
  *    chunk of a few hundred rows): the contraction over K is split among
  *    several blocks per tile, their float32 partials are kept in the
@@ -202,7 +203,13 @@ int nvfp4_qmm(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
  *    bf16 parts (hi + mid + lo == x) written to the workspace as [M, 3K],
  *    and the bf16 matrix-core GEMM contracts them against the weight taken
  *    three times, so every product is exact and only the float32
- *    accumulation order differs from a plain float32 dot product.
+ *    accumulation order differs from a plain float32 dot product;
+ *  * transpose = 0 with K % 64 == 0 (the dequantize-then-GEMM order of the
+ *    pages' GEMM route): the plane is decoded into an exact dense copy
+ *    [N, K] of 2-byte values (bf16, or f16 for f16 activations; the block
+ *    scale applied, g not) at the start of the workspace, and a matrix-core
+ *    GEMM multiplies the activations (for float32, their three-part copy,
+ *    placed after the dense copy) against it; g follows in its epilogue.
  * With less (or NULL, 0) it is nvfp4_qmm.  Results equal nvfp4_qmm's up to
  * float32 summation order.
  */
@@ -216,7 +223,8 @@ int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K,
  * nvfp4_qmm_workspace_size -- bytes of workspace nvfp4_qmm_ws uses for this
  * call on the current device (0: it uses none), or a negative status for an
  * invalid request: splits * M * N * 4 for a K split, M * 3K * 2 rounded up to
- * 256 for float32 activations.  Host only.
+ * 256 for float32 activations; for a non-transposed plane N * K * 2 rounded
+ * up to 256, plus that float32 copy.  Host only.
  */
 int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
                                  nvfp4_dtype_t dtype, nvfp4_route_t route);
@@ -229,19 +237,20 @@ int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
 /*
  * nvfp4_qmm_noalloc -- nvfp4_qmm for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
- * forbid allocation).  Same arguments, results and errors as nvfp4_qmm, and
- * the same K split as nvfp4_qmm_ws would make with a workspace of
- * nvfp4_qmm_workspace_size() bytes; its float32 partials live in a static
- * device array of NVFP4_STATIC_SCRATCH_BYTES owned by the library instead of
- * a caller workspace, so results equal nvfp4_qmm_ws's bit for bit (the same
- * holds for the three-part copy of float32 activations).  Nothing is
- * allocated (no hipMalloc/hipFree or allocating library call).  A call whose
- * K split needs more than NVFP4_STATIC_SCRATCH_BYTES returns
- * NVFP4_ERR_SCRATCH and launches nothing; float32 activations whose copy does
- * not fit run nvfp4_qmm's float32 FMA kernel instead.  The device address of the array is
+ * forbid allocation).  Same arguments and errors as nvfp4_qmm, and the
+ * kernels nvfp4_qmm_ws would run with a workspace of
+ * nvfp4_qmm_workspace_size() bytes (a K split's float32 partials, the
+ * three-part copy of float32 activations, a non-transposed plane's dense
+ * copy), with that workspace taken from a static device array of
+ * NVFP4_STATIC_SCRATCH_BYTES owned by the library: results equal
+ * nvfp4_qmm_ws's bit for bit.  Nothing is allocated (no hipMalloc/hipFree or
+ * allocating library call).  A call whose K split needs more than
+ * NVFP4_STATIC_SCRATCH_BYTES returns NVFP4_ERR_SCRATCH and launches nothing;
+ * a float32 copy or a dense copy that does not fit runs nvfp4_qmm's float32
+ * FMA kernel instead, which needs none.  The device address of the array is
  * looked up once per device (NVFP4_ERR_HIP if the runtime cannot give it).
- * All calls on one GPU share that GPU's array and every split writes its
- * whole slice before it is read, so nothing carries over from an earlier
+ * All calls on one GPU share that GPU's array and every call writes what it
+ * reads there before reading it, so nothing carries over from an earlier
  * call; calls that overlap on one GPU (different streams, or another
  * thread) race on the array and must be serialized by the caller.
  */

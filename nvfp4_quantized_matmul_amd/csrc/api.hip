@@ -48,7 +48,7 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 // What one qmm call launches, decided on the host with every check done.
 struct QmmPlan {
-  enum Kind { kNothing, kZeroFill, kQmv, kGemmMfma, kGemmGeneric } kind;
+  enum Kind { kNothing, kZeroFill, kQmv, kGemmMfma } kind;
 };
 
 // All host checks of one nvfp4_qmm call (no launch).
@@ -75,14 +75,11 @@ int qmm_plan(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N
   if (r == NVFP4_ROUTE_QMV) {
     if ((N + 15) / 16 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
     plan->kind = QmmPlan::kQmv;
-  } else if (transpose) {
+  } else {
     // the MFMA GEMM where one of its forms applies, else the generic kernel
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
     if (tiles + 8 > nvfp4host::kMaxGridX || (N + 63) / 64 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
     plan->kind = QmmPlan::kGemmMfma;
-  } else {
-    if ((N + 63) / 64 > nvfp4host::kMaxGridX) return NVFP4_ERR_GRID;
-    plan->kind = QmmPlan::kGemmGeneric;
   }
   return NVFP4_OK;
 }
@@ -96,11 +93,8 @@ void qmm_launch(const QmmPlan& plan, const void* x, nvfp4_dtype_t dtype, int64_t
     case QmmPlan::kZeroFill: nvfp4host::launch_fill_zero(out, M * N * dtype_size(dtype), stream); break;
     case QmmPlan::kQmv: nvfp4host::launch_qmv(x, dtype, M, K, N, w, scales, gs, out, stream); break;
     case QmmPlan::kGemmMfma:
-      if (!nvfp4host::launch_gemm_mfma(x, dtype, M, K, N, w, scales, gs, out, stream, ws, ws_bytes))
+      if (!nvfp4host::launch_gemm_mfma(x, dtype, M, K, N, w, scales, gs, transpose, out, stream, ws, ws_bytes))
         nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
-      break;
-    case QmmPlan::kGemmGeneric:
-      nvfp4host::launch_gemm_generic(x, dtype, M, K, N, w, scales, gs, transpose, out, stream);
       break;
   }
 }
@@ -232,8 +226,8 @@ int64_t nvfp4_qmm_workspace_size(int64_t M, int64_t K, int64_t N, int transpose,
   int64_t t;
   if (!mul_ok(M, K, &t) || !mul_ok(M, N, &t) || !mul_ok(K, N, &t)) return NVFP4_ERR_SHAPE;
   const int r = route == NVFP4_ROUTE_AUTO ? auto_route : (int)route;
-  if (r != NVFP4_ROUTE_GEMM || !transpose || M == 0 || N == 0 || K == 0) return 0;
-  return nvfp4host::gemm_workspace_bytes(M, K, N, dtype);
+  if (r != NVFP4_ROUTE_GEMM || M == 0 || N == 0 || K == 0) return 0;
+  return nvfp4host::gemm_workspace_bytes(M, K, N, dtype, transpose);
 }
 
 int nvfp4_qmm_ws(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int64_t N, const uint32_t* w,
@@ -302,9 +296,10 @@ int nvfp4_qmm_noalloc(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, 
   int64_t need = nvfp4_qmm_workspace_size(M, K, N, transpose, dtype, route);
   if (need < 0) return (int)need;
   if (need > kStaticScratchBytes) {
-    // float32 activations whose three-part copy does not fit take the generic
-    // kernel, which needs no scratch; a K split that does not fit is refused
-    if (dtype != NVFP4_F32) return NVFP4_ERR_SCRATCH;
+    // a float32 copy or a non-transposed plane's dense copy that does not
+    // fit leaves the generic kernel, which needs no scratch; a K split that
+    // does not fit is refused
+    if (dtype != NVFP4_F32 && transpose) return NVFP4_ERR_SCRATCH;
     need = 0;
   }
   void* ws = nullptr;

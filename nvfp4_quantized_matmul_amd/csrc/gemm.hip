@@ -668,6 +668,145 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   v3_store_tile<TO>(acc, out, M, N, m_blk, n_blk, global_factor(gs, 0), wave, l32, h);
 }
 
+// ----------------------------------------------------------------------------
+// Non-transposed planes (w [K, N/8], quantized along N): dequantize, then a
+// matrix-core GEMM on the dense copy, the order of the pages' own GEMM route.
+// ----------------------------------------------------------------------------
+
+// Dense copy of a non-transposed plane, transposed: wt[n][k] =
+// e2m1(w[k][n]) * e4m3(scale[k][n / 16]) as bf16 or f16 bits (exact in both:
+// at most 6 significant bits, magnitudes in [2^-10, 2688]); the global factor
+// is left to the GEMM's epilogue.  Block (kb, nb) covers k in [64 kb, 64 kb
+// + 64) and n in [64 nb, 64 nb + 64): thread t decodes words 2 (t & 3) and
+// 2 (t & 3) + 1 of row k = 64 kb + (t >> 2) (sixteen n, one scale block) into
+// an LDS tile that is written back along k, 16 bytes per store.
+constexpr int kNtTile = 64;
+template <typename TW>
+__global__ __launch_bounds__(256) void dequant_nt_kernel(const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
+                                                         int64_t K, int64_t N, uint16_t* __restrict__ wt) {
+  __shared__ __align__(16) uint16_t tile[kNtTile][kNtTile + 8];   // [n][k], rows padded by 16 bytes
+  const int t = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * kNtTile, n0 = (int64_t)blockIdx.y * kNtTile;
+  {
+    const int kl = t >> 2, g = t & 3;
+    const int64_t k = k0 + kl, n = n0 + 16 * g;     // N % 16 == 0: a group is wholly in or out
+    if (k < K && n < N) {
+      const uint2 wv = *reinterpret_cast<const uint2*>(w + k * (N / 8) + n / 8);
+      const float s = e4m3<0>(sc[k * (N / 16) + n / 16]);
+      const uint4 ua = __builtin_bit_cast(uint4, V3Ops<TW>::decode(wv.x, s));
+      const uint4 ub = __builtin_bit_cast(uint4, V3Ops<TW>::decode(wv.y, s));
+      const uint32_t d[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        tile[16 * g + 2 * i][kl] = (uint16_t)d[i];
+        tile[16 * g + 2 * i + 1][kl] = (uint16_t)(d[i] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = r * 256 + t, nl = idx >> 3, c = idx & 7;
+    const int64_t n = n0 + nl, k = k0 + 8 * c;
+    if (n < N && k < K)
+      *reinterpret_cast<uint4*>(wt + n * K + k) = *reinterpret_cast<const uint4*>(&tile[nl][8 * c]);
+  }
+}
+
+// GEMM of 2-byte activations x [M, K] against a dense 2-byte weight copy
+// wt [N, wk] (rows of K elements when wk == K; the float32 form runs over
+// activation rows of three bf16 parts, K = 3 wk, and activation slab s meets
+// weight slab s mod (wk / 64)).  The tile and fragments are those of the
+// NVFP4 GEMM above (256 weight rows x 256 activation rows, wavefront w owning
+// weight rows [64w, 64w + 64)), with the weight fragments read from LDS like
+// the activation fragments.  Both operands move global -> LDS through two
+// stages of 32 KiB each: slab s + 1 is queued after the barrier that ends
+// slab s - 1, so it streams while slab s is multiplied.
+template <typename TA, typename TO>
+__global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_dense_kernel(
+    const TA* __restrict__ x, const uint16_t* __restrict__ wt, const float* __restrict__ gs, TO* __restrict__ out,
+    int64_t M, int64_t K, int64_t N, int64_t tiles_m, int64_t tiles_total, int64_t wk) {
+  typedef typename V3Ops<TA>::vec vec;
+  __shared__ uint4 xa[kV3BM * 8], xb[kV3BM * 8], wa[kV3BN * 8], wb[kV3BN * 8];
+
+  const int64_t per_xcd = (int64_t)gridDim.x / 8;
+  const int64_t tile = ((int64_t)blockIdx.x % 8) * per_xcd + (int64_t)blockIdx.x / 8;
+  if (tile >= tiles_total) return;   // whole block, before any barrier
+  const int64_t m_blk = (tile % tiles_m) * kV3BM;
+  const int64_t n_blk = (tile / tiles_m) * kV3BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t nslabs = K / kV3BK, wslabs = wk / kV3BK;
+
+  // Per load i: 16-byte chunk `slot` of the tile, the same placement for
+  // both operands; rows past M or N re-read the last row (never stored).
+  const uint16_t* xs[8];
+  const uint16_t* ws[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = (i * 4 + wave) * 64 + lane;
+    const int r = slot >> 3, c = (slot & 7) ^ swz(r);
+    const int64_t m = m_blk + r < M ? m_blk + r : M - 1;
+    const int64_t n = n_blk + r < N ? n_blk + r : N - 1;
+    xs[i] = reinterpret_cast<const uint16_t*>(x) + m * K + c * 8;
+    ws[i] = wt + n * wk + c * 8;
+  }
+  auto issue = [&](uint4* xd, uint4* wd, int64_t slab) {
+    const int64_t wsl = slab < wslabs ? slab : slab % wslabs;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(xs[i] + slab * kV3BK, NVFP4_LDS(&xd[(i * 4 + wave) * 64]), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(ws[i] + wsl * kV3BK, NVFP4_LDS(&wd[(i * 4 + wave) * 64]), 16, 0, 0);
+  };
+  auto compute = [&](f32x16_t (&acc)[2][8], const uint4* xd, const uint4* wd) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vec B[8], A[2];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(vec, xd[xslot(b * 32 + l32, 4 * h + j)]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) A[a] = __builtin_bit_cast(vec, wd[xslot(wave * 64 + a * 32 + l32, 4 * h + j)]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        acc[0][b] = V3Ops<TA>::mfma(A[0], B[b], acc[0][b]);
+        acc[1][b] = V3Ops<TA>::mfma(A[1], B[b], acc[1][b]);
+      }
+    }
+  };
+
+  f32x16_t acc[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  issue(xa, wa, 0);
+  int64_t s = 0;
+  for (; s + 2 <= nslabs; s += 2) {
+    wait_vmem(false);
+    __builtin_amdgcn_s_barrier();
+    issue(xb, wb, s + 1);
+    compute(acc, xa, wa);
+    wait_vmem(false);
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < nslabs) issue(xa, wa, s + 2);
+    compute(acc, xb, wb);
+  }
+  if (s < nslabs) {
+    wait_vmem(false);
+    __builtin_amdgcn_s_barrier();
+    compute(acc, xa, wa);
+  }
+  wait_vmem(false);   // nothing is in flight here; kept so no load-to-LDS can outlive the loop
+  v3_store_tile<TO>(acc, out, M, N, m_blk, n_blk, global_factor(gs, 0), wave, l32, h);
+}
+
 // out = round(g * sum over splits of ws[split]), splits added in order.
 template <typename TO>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws, int64_t splits,
@@ -940,8 +1079,60 @@ static void launch_v3(const T* x, int64_t M, int64_t K, int64_t N, const uint32_
 // Workspace of the float32 form: the [M, 3K] bf16 split of the activations.
 static int64_t f32_split_bytes(int64_t M, int64_t K) { return (M * 3 * K * 2 + 255) / 256 * 256; }
 
+// Non-transposed planes take the dense route whenever K % 64 == 0: the
+// generic kernel is latency-bound on them at every M (at K = N = 4096 it
+// took 515-575 us for M = 1..64, the dense route 118-121 us).
+static bool nt_applies(int64_t K, int64_t N) {
+  return K % kV3BK == 0 && (N + kNtTile - 1) / kNtTile <= 65535;
+}
+
+static int64_t nt_dense_bytes(int64_t K, int64_t N) { return (N * K * 2 + 255) / 256 * 256; }
+
+// Non-transposed plane: its dense transposed copy (and, for float32
+// activations, their three-part copy after it) in the workspace, then the
+// dense matrix-core GEMM.  False (nothing launched) when the route does not
+// apply or the workspace is short.
+static bool launch_gemm_mfma_nt(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                                const uint8_t* sc, const float* gs, void* out, hipStream_t s, void* ws,
+                                int64_t ws_bytes) {
+  if (!nt_applies(K, N) || !ws || (reinterpret_cast<uintptr_t>(ws) & 15) != 0) return false;
+  const int64_t dense = nt_dense_bytes(K, N);
+  if (ws_bytes < dense + (dt == NVFP4_F32 ? f32_split_bytes(M, K) : 0)) return false;
+  uint16_t* wt = static_cast<uint16_t*>(ws);
+  const dim3 dgrid((unsigned)(K / kNtTile), (unsigned)((N + kNtTile - 1) / kNtTile));
+  if (dt == NVFP4_F16)
+    dequant_nt_kernel<_Float16><<<dgrid, dim3(256), 0, s>>>(w, sc, K, N, wt);
+  else
+    dequant_nt_kernel<__bf16><<<dgrid, dim3(256), 0, s>>>(w, sc, K, N, wt);
+  const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
+  const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
+  const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
+  switch (dt) {
+    case NVFP4_BF16:
+      gemm_mfma_dense_kernel<__bf16, __bf16><<<grid, dim3(kMfmaThreads), 0, s>>>(
+          static_cast<const __bf16*>(x), wt, gs, static_cast<__bf16*>(out), M, K, N, tiles_m, tiles, K);
+      break;
+    case NVFP4_F16:
+      gemm_mfma_dense_kernel<_Float16, _Float16><<<grid, dim3(kMfmaThreads), 0, s>>>(
+          static_cast<const _Float16*>(x), wt, gs, static_cast<_Float16*>(out), M, K, N, tiles_m, tiles, K);
+      break;
+    case NVFP4_F32: {
+      uint16_t* xs = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + dense);
+      int64_t sgrid = (M * K / 8 + 255) / 256;
+      if (sgrid > 8192) sgrid = 8192;
+      split_f32_kernel<<<dim3((unsigned)sgrid), dim3(256), 0, s>>>(static_cast<const float*>(x), M, K, xs);
+      gemm_mfma_dense_kernel<__bf16, float><<<grid, dim3(kMfmaThreads), 0, s>>>(
+          reinterpret_cast<const __bf16*>(xs), wt, gs, static_cast<float*>(out), M, 3 * K, N, tiles_m, tiles, K);
+      break;
+    }
+  }
+  return true;
+}
+
 bool launch_gemm_mfma(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
-                      const uint8_t* sc, const float* gs, void* out, hipStream_t s, void* ws, int64_t ws_bytes) {
+                      const uint8_t* sc, const float* gs, int transpose, void* out, hipStream_t s, void* ws,
+                      int64_t ws_bytes) {
+  if (!transpose) return launch_gemm_mfma_nt(x, dt, M, K, N, w, sc, gs, out, s, ws, ws_bytes);
   const bool v3 = K % kV3BK == 0 && (reinterpret_cast<uintptr_t>(sc) & 3) == 0;
   switch (dt) {
     case NVFP4_BF16:
@@ -1051,7 +1242,9 @@ int64_t gemm_glu_tiles(int64_t M, int64_t F) {
   return ((M + kV3BM - 1) / kV3BM) * ((F + kV3BN / 2 - 1) / (kV3BN / 2));
 }
 
-int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, nvfp4_dtype_t dt) {
+int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, nvfp4_dtype_t dt, int transpose) {
+  if (!transpose)
+    return nt_applies(K, N) ? nt_dense_bytes(K, N) + (dt == NVFP4_F32 ? f32_split_bytes(M, K) : 0) : 0;
   if (dt == NVFP4_F32) return K % kV3BK == 0 ? f32_split_bytes(M, K) : 0;
   const int64_t sp = gemm_splits(M, K, N);
   return sp > 1 ? sp * M * N * 4 : 0;

@@ -65,22 +65,24 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
 bool launch_gather_mfma(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t M, int64_t K, const int32_t* lhs,
                         const int32_t* rhs, int64_t R, const uint32_t* w, const uint8_t* sc,
                         const float* gs, int64_t E, int64_t N, void* out, hipStream_t s);
-// MFMA GEMM, transposed plane.  bf16: the LDS-pipelined kernel (K % 64 ==
-// 0, 4-byte aligned scales) or the older one (K % 32 == 0); f16: the
-// pipelined kernel on the f16 MFMA; float32: the activations' exact
-// three-part bf16 split into the workspace, then the bf16 kernel over rows of
-// 3K (K % 64 == 0, a workspace of gemm_workspace_bytes).  With a workspace of
-// at least gemm_workspace_bytes(M, K, N, dt) bytes (16-byte aligned), the
-// 2-byte forms split the slabs of K among several blocks per tile when that
-// pays (few tiles) and add the float32 partials in a second kernel.  Returns
-// false, launching nothing, when no MFMA form applies.
+// MFMA GEMM.  Transposed plane: bf16 through the LDS-pipelined kernel (K %
+// 64 == 0, 4-byte aligned scales) or the older one (K % 32 == 0); f16
+// through the pipelined kernel on the f16 MFMA; float32 as the activations'
+// exact three-part bf16 split in the workspace, then the bf16 kernel over
+// rows of 3K (K % 64 == 0).  With a workspace of at least
+// gemm_workspace_bytes bytes (16-byte aligned) the 2-byte forms split the
+// slabs of K among several blocks per tile when that pays (few tiles) and add
+// the float32 partials in a second kernel.  Non-transposed plane (K % 64 ==
+// 0, a workspace of gemm_workspace_bytes): its exact dense copy,
+// transposed, in the workspace, then a matrix-core GEMM on the dense copy.
+// Returns false, launching nothing, when no MFMA form applies.
 bool launch_gemm_mfma(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
-                      const uint8_t* sc, const float* gs, void* out, hipStream_t s, void* ws = nullptr,
-                      int64_t ws_bytes = 0);
+                      const uint8_t* sc, const float* gs, int transpose, void* out, hipStream_t s,
+                      void* ws = nullptr, int64_t ws_bytes = 0);
 // Workspace the MFMA GEMM wants for this shape on the current device (0:
-// none): the K split's partials (2-byte types, few tiles) or the float32
-// form's split activations.
-int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, nvfp4_dtype_t dt);
+// none): the K split's partials (2-byte types, few tiles), the float32
+// form's split activations, or a non-transposed plane's dense copy.
+int64_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, nvfp4_dtype_t dt, int transpose);
 // Gated MLP projection as one MFMA GEMM: bf16 activations, transposed gate
 // and up planes [F, K/8] with K % 64 == 0 and 4-byte aligned scale planes;
 // a tile holds 128 features of both planes.  With a 16-byte aligned

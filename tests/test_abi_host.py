@@ -115,7 +115,15 @@ def test_qmm_workspace_size_and_validation(lib):
     assert ws(7, 64, 32, 1, F32, 2) == (7 * 3 * 64 * 2 + 255) // 256 * 256
     assert ws(2048, 5376, 21504, 1, F32, 0) == 2048 * 3 * 5376 * 2
     assert ws(128, 5392, 21504, 1, F32, 0) == 0              # K % 64 != 0: float32 FMA kernel
-    assert ws(300, 5376, 21504, 0, F32, 0) == 0              # transpose = 0: float32 FMA kernel
+    # non-transposed plane with K % 64 == 0: its dense copy [N, K]
+    # of 2-byte values (and the float32 copy of the activations after it)
+    dense = (21504 * 5376 * 2 + 255) // 256 * 256
+    assert ws(300, 5376, 21504, 0, BF16, 0) == dense
+    assert ws(300, 5376, 21504, 0, F16, 2) == dense
+    assert ws(300, 5376, 21504, 0, F32, 0) == dense + 300 * 3 * 5376 * 2
+    assert ws(1, 5376, 21504, 0, BF16, 0) == dense           # any M
+    assert ws(300, 5392, 21504, 0, BF16, 0) == 0             # K % 64 != 0: generic kernel
+    assert ws(300, 17, 32, 0, BF16, 0) == 0
     assert ws(128, 5392, 21504, 1, BF16, 0) == 0             # K % 64 != 0: no split
     assert ws(128, 5376, 21504, 1, BF16, 1) == 0             # forced qmv
     assert ws(128, 24, 64, 1, BF16, 0) == SHAPE

@@ -590,6 +590,47 @@ def test_gemm_matrix_cores_nonfinite_activations(dtype):
     assert oracle.relative_error(got[4:], ref[4:]) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("shape", [(300, 512, 272), (64, 128, 32), (257, 192, 528), (1030, 320, 4112),
+                                   (1, 64, 16), (33, 256, 48)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("with_gs", [False, True])
+def test_gemm_non_transposed_matrix_cores(shape, dtype, with_gs):
+    """Non-transposed planes [K, N/8] with K % 64 == 0: the
+    binding's workspace holds the plane's dense transposed copy (and the
+    float32 activations' three-part copy), the matrix-core GEMM runs on it;
+    partial row and column tiles (N = 272, 528, 4112), full comparison."""
+    M, K, N = shape
+    code = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}[dtype]
+    need = int(nv.load_library().nvfp4_qmm_workspace_size(M, K, N, 0, code, 0))
+    assert need >= N * K * 2
+    case = synth.dense_case(4300 + M + K + N, M, K, N, transpose=False, with_gs=with_gs)
+    out, ref = run_qmm(case, dtype, "auto", guard=True)
+    assert rel(out, ref) <= TOL[dtype]
+
+
+def test_gemm_non_transposed_matrix_cores_match_generic():
+    """The dense route (nvfp4_qmm_ws) and the generic kernel (nvfp4_qmm, no
+    workspace) on one non-transposed float32 call: the same exact products,
+    float32 summation order only."""
+    M, K, N = 300, 1024, 528
+    case = synth.dense_case(4390, M, K, N, transpose=False, with_gs=True)
+    x_t, x_ref = activations(case.x, torch.float32)
+    w_t, s_t, gs_t = words(case.w), u8(case.scales), f32(case.gs)
+    lib = nv.load_library()
+    need = int(lib.nvfp4_qmm_workspace_size(M, K, N, 0, 0, 0))
+    assert need == (N * K * 2 + 255) // 256 * 256 + M * 3 * K * 2
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    dense = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    generic = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    assert lib.nvfp4_qmm_ws(P(x_t), 0, M, K, N, P(w_t), P(s_t), P(gs_t), 0, 0, P(ws), need, P(dense), None) == 0
+    assert lib.nvfp4_qmm(P(x_t), 0, M, K, N, P(w_t), P(s_t), P(gs_t), 0, 0, P(generic), None) == 0
+    torch.cuda.synchronize()
+    assert oracle.relative_error(host(dense), host(generic)) <= TOL[torch.float32]
+    ref = oracle.qmm(x_ref, case.w, case.scales, case.gs[0], transpose=False)
+    assert rel(dense, ref) <= TOL[torch.float32]
+
+
 def test_prefill_plane_f16_and_f32_sampled():
     """The prefill plane (M=2048, K=5376, N=21504) with f16 activations and
     with float32 activations (the three-part copy, 66 MB, through the

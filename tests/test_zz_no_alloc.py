@@ -21,27 +21,27 @@ pytestmark = pytest.mark.gpu
 P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _inputs(seed, M, K, N, dtype):
-    case = synth.dense_case(seed, M, K, N, with_gs=True)
+def _inputs(seed, M, K, N, dtype, tr=1):
+    case = synth.dense_case(seed, M, K, N, with_gs=True, transpose=bool(tr))
     x_t, x_ref = activations(case.x, dtype)
     return case, x_t, x_ref, words(case.w), u8(case.scales), f32(case.gs)
 
 
-def _noalloc(lib, code, x_t, w_t, s_t, gs_t, M, K, N):
+def _noalloc(lib, code, x_t, w_t, s_t, gs_t, M, K, N, tr=1):
     out, check = guarded((M, N), x_t.dtype)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    assert lib.nvfp4_qmm_noalloc(P(x_t), code, M, K, N, P(w_t), P(s_t), P(gs_t), 1, 0, P(out), st) == 0
+    assert lib.nvfp4_qmm_noalloc(P(x_t), code, M, K, N, P(w_t), P(s_t), P(gs_t), tr, 0, P(out), st) == 0
     torch.cuda.synchronize()
     check()
     return out
 
 
-def _with_workspace(lib, code, x_t, w_t, s_t, gs_t, M, K, N):
-    need = int(lib.nvfp4_qmm_workspace_size(M, K, N, 1, code, 0))
+def _with_workspace(lib, code, x_t, w_t, s_t, gs_t, M, K, N, tr=1):
+    need = int(lib.nvfp4_qmm_workspace_size(M, K, N, tr, code, 0))
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
     out = torch.empty((M, N), dtype=x_t.dtype, device=DEV)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    assert lib.nvfp4_qmm_ws(P(x_t), code, M, K, N, P(w_t), P(s_t), P(gs_t), 1, 0, P(ws), need, P(out), st) == 0
+    assert lib.nvfp4_qmm_ws(P(x_t), code, M, K, N, P(w_t), P(s_t), P(gs_t), tr, 0, P(ws), need, P(out), st) == 0
     torch.cuda.synchronize()
     return out, need
 
@@ -75,6 +75,22 @@ def test_noalloc_float32_copy_matches_workspace_call_twice_second_smaller():
         assert torch.equal(got, want), (M, K, N)
         ref = oracle.qmm(x_ref, case.w, case.scales, case.gs[0])
         assert oracle.relative_error(host(got), ref) <= TOL[torch.float32]
+
+
+def test_noalloc_non_transposed_dense_copy_twice_second_smaller():
+    """A non-transposed plane's dense copy (and, for float32, the activations'
+    copy after it) lives in the scratch; the second, smaller call reuses its
+    start."""
+    lib = nv.load_library()
+    for seed, (M, K, N), dt, code in ((9107, (300, 512, 272), torch.bfloat16, 1),
+                                      (9108, (40, 256, 48), torch.float32, 0)):
+        case, x_t, x_ref, w_t, s_t, gs_t = _inputs(seed, M, K, N, dt, tr=0)
+        want, need = _with_workspace(lib, code, x_t, w_t, s_t, gs_t, M, K, N, tr=0)
+        assert need >= N * K * 2, (M, K, N, need)
+        got = _noalloc(lib, code, x_t, w_t, s_t, gs_t, M, K, N, tr=0)
+        assert torch.equal(got, want), (M, K, N)
+        ref = oracle.qmm(x_ref, case.w, case.scales, case.gs[0], transpose=False)
+        assert oracle.relative_error(host(got), ref) <= TOL[dt]
 
 
 def test_noalloc_without_scratch_is_nvfp4_qmm():
