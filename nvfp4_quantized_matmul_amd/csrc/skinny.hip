@@ -38,7 +38,9 @@
 //  * MFMA step (c, i) of chunk c takes word 4i+q of that chunk from lane q,
 //    so the activations it multiplies -- 8 bf16 per lane, one 16-byte load
 //    -- are again 64 contiguous bytes across the q lanes;
-//  * the 16 scale bytes of a row's pair-group come in one 16-byte load;
+//  * the 16 scale bytes of a row's pair-group come in one 16-byte load by
+//    the row's q = 0 lane (the other three lanes' loads are out of range, so
+//    they make no memory access) and two lane swaps give them to the others;
 //    word 4i+q uses byte 2i + q/2 of its chunk's eight;
 //  * the wavefronts' partial sums meet in LDS at the end, are added in a
 //    fixed order and scaled by g once.
@@ -61,6 +63,9 @@ constexpr int kRows = 16 * kTiles;
 constexpr int kPG = 256;        // k per pair-group
 constexpr int64_t kMaxPlaneBytes = (int64_t)1 << 31;   // offsets and sizes stay below 2^31
 constexpr int kScanPerThread = 4;   // pairs each thread examines per round of the gather scan
+// A buffer-load offset past every plane (planes stay below 2^31 bytes): the
+// load returns 0 without a memory access.
+constexpr uint32_t kNoLoad = 0x80000000u;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -145,7 +150,8 @@ __device__ __forceinline__ void load_pg(PairGroup<MF, TX>& p, const Sources<MF>&
     for (int t = 0; t < kTiles; ++t) {
       const rsrc_t& wr = (GLU && t >= 2) ? src.w2 : src.w;
       const rsrc_t& sr = (GLU && t >= 2) ? src.s2 : src.s;
-      if (c == 0) p.s[t] = load16(sr, src.so[t], pg * 16u);             // 16 scale bytes per pair-group
+      // 16 scale bytes per pair-group, fetched by the row's q = 0 lane only
+      if (c == 0) p.s[t] = load16(sr, (threadIdx.x & 48) ? kNoLoad : src.so[t], pg * 16u);
       p.w[t][c] = load16(wr, src.wo[t], pg * 128u + c * 64u);           // 32 words per pair-group
     }
   }
@@ -164,8 +170,19 @@ __device__ __forceinline__ void transpose_q(const uint4 v, uint32_t (&o)[4]) {
   o[3] = d[1];
 }
 
+// Lane r's value to lanes r + 16, r + 32 and r + 48 (r < 16): the upper half
+// takes the lower half's values, then the odd rows of 16 the even rows'.
+__device__ __forceinline__ uint32_t from_row0(uint32_t v) {
+  const uint32_t t = __builtin_amdgcn_permlane32_swap(v, v, false, false)[0];
+  return __builtin_amdgcn_permlane16_swap(t, t, false, false)[0];
+}
+
 template <typename TX, int MF>
 __device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const PairGroup<MF, TX>& p, int half) {
+  uint4 sv[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+    sv[t] = make_uint4(from_row0(p.s[t].x), from_row0(p.s[t].y), from_row0(p.s[t].z), from_row0(p.s[t].w));
   // word 4i+q of chunk c uses scale byte 8c + 2i + q/2: dword 2c + i/2,
   // byte 2(i%2) + q/2
   const uint32_t sh = 8u * (uint32_t)half;
@@ -173,8 +190,8 @@ __device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const Pai
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      const uint32_t d0 = (c == 0 ? p.s[t].x : p.s[t].z) >> sh;
-      const uint32_t d1 = (c == 0 ? p.s[t].y : p.s[t].w) >> sh;
+      const uint32_t d0 = (c == 0 ? sv[t].x : sv[t].z) >> sh;
+      const uint32_t d1 = (c == 0 ? sv[t].y : sv[t].w) >> sh;
       uint32_t wd[4];
       transpose_q(p.w[t][c], wd);
       const float sc[4] = {e4m3<0>(d0), e4m3<2>(d0), e4m3<0>(d1), e4m3<2>(d1)};
