@@ -38,9 +38,9 @@
 //  * MFMA step (c, i) of chunk c takes word 4i+q of that chunk from lane q,
 //    so the activations it multiplies -- 8 bf16 per lane, one 16-byte load
 //    -- are again 64 contiguous bytes across the q lanes;
-//  * the 16 scale bytes of a row's pair-group come in one 16-byte load by
-//    the row's q = 0 lane (the other three lanes' loads are out of range, so
-//    they make no memory access) and two lane swaps give them to the others;
+//  * the 16 scale bytes of the pair-group of all 64 rows come in one load,
+//    lane l taking row l (the gated form: one load per plane, each for its
+//    32 lanes), and lane swaps give each tile's 16 rows to its four q lanes;
 //    word 4i+q uses byte 2i + q/2 of its chunk's eight;
 //  * the wavefronts' partial sums meet in LDS at the end, are added in a
 //    fixed order and scaled by g once.
@@ -104,7 +104,7 @@ __device__ __forceinline__ void split3(const uint4 a, const uint4 b, bf16x8_t& h
 template <int MF, typename TX = __bf16>
 struct PairGroup {
   uint4 w[kTiles][2]; // [tile][chunk]: words 4q..4q+3 of the chunk
-  uint4 s[kTiles];    // [tile]: the row's 16 scale bytes of the pair-group
+  uint4 s;            // the 16 scale bytes of the pair-group of block row `lane`
   uint4 x[MF][8][XLoads<TX>::n];  // [fragment][step 4c+i]: activations of word 16c+4i+q
 };
 
@@ -113,20 +113,29 @@ struct Sources {
   rsrc_t w, s, x;         // weight plane, scale plane, activations
   rsrc_t w2, s2;          // gated form: the up plane and its scales (tiles 2 and 3)
   uint32_t wo[kTiles];    // byte offset of this lane's weight row in tile t, + 16q
-  uint32_t so[kTiles];    // byte offset of its scale row
+  uint32_t so;            // byte offset of the scale row of block row `lane`
+  uint32_t so2;           // gated form: the up plane's (lanes 32..63; the gate plane's lanes 0..31 in so)
   uint32_t xo[MF];        // byte offset of this lane's activation row in fragment f, + 8q elements
 };
 
-// Offsets of weight rows n0 + 16t + r (lane r = lane % 16, q = lane / 16).
-// GLU: tiles 0, 1 are gate rows n0 .. n0 + 31 and tiles 2, 3 the up rows of
-// the same features.
+// Offsets of weight rows n0 + 16t + r (lane r = lane % 16, q = lane / 16)
+// and of scale row n0 + lane.  GLU: tiles 0, 1 are gate rows n0 .. n0 + 31
+// and tiles 2, 3 the up rows of the same features; lanes 0..31 take the gate
+// scale rows, lanes 32..63 the up ones (each load's other half is out of
+// range).
 template <int MF, bool GLU = false>
 __device__ __forceinline__ void set_rows(Sources<MF>& src, int64_t n0, int r16, int q, int64_t K) {
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
     const int64_t row = n0 + 16 * (GLU ? (t & 1) : t) + r16;
     src.wo[t] = (uint32_t)(row * (K / 2) + 16 * q);
-    src.so[t] = (uint32_t)(row * (K / 16));
+  }
+  const int lane = r16 + 16 * q;
+  if constexpr (GLU) {
+    src.so = lane < 32 ? (uint32_t)((n0 + lane) * (K / 16)) : kNoLoad;
+    src.so2 = lane < 32 ? kNoLoad : (uint32_t)((n0 + lane - 32) * (K / 16));
+  } else {
+    src.so = (uint32_t)((n0 + lane) * (K / 16));
   }
 }
 
@@ -146,12 +155,16 @@ __device__ __forceinline__ void load_pg(PairGroup<MF, TX>& p, const Sources<MF>&
 #pragma unroll
         for (int h = 0; h < XLoads<TX>::n; ++h)
           p.x[f][4 * c + i][h] = load16(src.x, src.xo[f], (pg * 256u + c * 128u + i * 32u) * E + h * 16u);
+    if (c == 0) {
+      p.s = load16(src.s, src.so, pg * 16u);                            // 16 scale bytes per row
+      if constexpr (GLU) {
+        const uint4 u = load16(src.s2, src.so2, pg * 16u);              // zeros where the gate half loaded
+        p.s = make_uint4(p.s.x | u.x, p.s.y | u.y, p.s.z | u.z, p.s.w | u.w);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const rsrc_t& wr = (GLU && t >= 2) ? src.w2 : src.w;
-      const rsrc_t& sr = (GLU && t >= 2) ? src.s2 : src.s;
-      // 16 scale bytes per pair-group, fetched by the row's q = 0 lane only
-      if (c == 0) p.s[t] = load16(sr, (threadIdx.x & 48) ? kNoLoad : src.so[t], pg * 16u);
       p.w[t][c] = load16(wr, src.wo[t], pg * 128u + c * 64u);           // 32 words per pair-group
     }
   }
@@ -170,19 +183,31 @@ __device__ __forceinline__ void transpose_q(const uint4 v, uint32_t (&o)[4]) {
   o[3] = d[1];
 }
 
-// Lane r's value to lanes r + 16, r + 32 and r + 48 (r < 16): the upper half
-// takes the lower half's values, then the odd rows of 16 the even rows'.
-__device__ __forceinline__ uint32_t from_row0(uint32_t v) {
-  const uint32_t t = __builtin_amdgcn_permlane32_swap(v, v, false, false)[0];
-  return __builtin_amdgcn_permlane16_swap(t, t, false, false)[0];
+// Row t (lanes 16t .. 16t + 15) of v broadcast to all four rows of 16, for
+// t = 0..3: one permlane32 swap of v with itself gives rows (0, 1, 0, 1) and
+// (2, 3, 2, 3), and a permlane16 swap of each with itself gives (0, 0, 0, 0)
+// and (1, 1, 1, 1), resp. (2, 2, 2, 2) and (3, 3, 3, 3).
+__device__ __forceinline__ void rows_bcast(uint32_t v, uint32_t (&o)[kTiles]) {
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+  o[0] = a[0];
+  o[1] = a[1];
+  o[2] = b[0];
+  o[3] = b[1];
 }
 
 template <typename TX, int MF>
 __device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const PairGroup<MF, TX>& p, int half) {
+  // tile t's scale bytes (block rows 16t .. 16t + 15) on lanes r + 16q
+  uint32_t sx[kTiles], sy[kTiles], sz[kTiles], sw[kTiles];
+  rows_bcast(p.s.x, sx);
+  rows_bcast(p.s.y, sy);
+  rows_bcast(p.s.z, sz);
+  rows_bcast(p.s.w, sw);
   uint4 sv[kTiles];
 #pragma unroll
-  for (int t = 0; t < kTiles; ++t)
-    sv[t] = make_uint4(from_row0(p.s[t].x), from_row0(p.s[t].y), from_row0(p.s[t].z), from_row0(p.s[t].w));
+  for (int t = 0; t < kTiles; ++t) sv[t] = make_uint4(sx[t], sy[t], sz[t], sw[t]);
   // word 4i+q of chunk c uses scale byte 8c + 2i + q/2: dword 2c + i/2,
   // byte 2(i%2) + q/2
   const uint32_t sh = 8u * (uint32_t)half;
