@@ -50,55 +50,6 @@ __global__ void sidecar_kernel(const float* __restrict__ ws2, float* __restrict_
   if (i < batch) gs[i] = ws2[i] * kGlobalDivisor;
 }
 
-template <typename TO>
-__device__ __forceinline__ void store8(TO* p, const float (&v)[8]);
-
-template <>
-__device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
-}
-
-template <>
-__device__ __forceinline__ void store8<__bf16>(__bf16* p, const float (&v)[8]) {
-  __bf16 h[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = (__bf16)v[i];
-  *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, h);
-}
-
-template <>
-__device__ __forceinline__ void store8<_Float16>(_Float16* p, const float (&v)[8]) {
-  _Float16 h[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
-  *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, h);
-}
-
-// One thread per packed word: 8 output elements.
-template <typename TO>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __restrict__ w,
-                                                           const uint8_t* __restrict__ sc,
-                                                           const float* __restrict__ gs,
-                                                           int64_t nwords, int64_t kw,
-                                                           int64_t words_per_mat,
-                                                           TO* __restrict__ out) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < nwords; idx += stride) {
-    const int64_t row = idx / kw;
-    const int64_t wi = idx - row * kw;
-    const float s = e4m3<0>(sc[row * (kw >> 1) + (wi >> 1)]);
-    float v[8];
-    decode_word_f32(w[idx], s, v);
-    if (gs) {
-      const float g = gs[idx / words_per_mat] / kGlobalDivisor;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] *= g;
-    }
-    store8<TO>(out + idx * 8, v);
-  }
-}
-
 // Eight outputs as non-temporal 16-byte stores (the expanded plane is
 // written once and not read back by this call).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -116,32 +67,35 @@ __device__ __forceinline__ void store8_nt(TO* p, const float (&v)[8]) {
   }
 }
 
-// The same expansion with no index division: one block row per matrix, and
-// over a matrix's words taken as one flat array, word i uses scale byte i / 2
+// Dequantize, one thread per packed word (8 outputs), with no index
+// division: block row y takes matrices y, y + gridDim.y, ..., and over a
+// matrix's words taken as one flat array, word i uses scale byte i / 2
 // (every row holds an even number of words).  Lane l of a wavefront writes
 // the 8 outputs of word base + l, so each store instruction covers one
-// contiguous run; the per-element arithmetic is that of dequant_kernel.  The
-// word loads and output stores are non-temporal (each byte is touched once):
-// measured 9% faster (54.8 vs 60.0 us for bf16 at 21504 x 5376).
+// contiguous run.  The word loads and output stores are non-temporal (each
+// byte is touched once): measured 9% faster (54.8 vs 60.0 us for bf16 at
+// 21504 x 5376).  Earlier a separate kernel with a division per word served
+// batches beyond the grid's y limit; the matrix loop replaces it.
 template <typename TO>
 __global__ __launch_bounds__(kThreads) void dequant_flat_kernel(const uint32_t* __restrict__ w,
                                                                 const uint8_t* __restrict__ sc,
                                                                 const float* __restrict__ gs, int64_t wpm,
-                                                                TO* __restrict__ out) {
-  const int64_t mat = blockIdx.y;
-  const uint32_t* wm = w + mat * wpm;
-  const uint8_t* sm = sc + mat * (wpm >> 1);
-  TO* om = out + mat * wpm * 8;
-  const float g = gs ? gs[mat] / kGlobalDivisor : 1.0f;
+                                                                int64_t batch, TO* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < wpm; i += stride) {
-    float v[8];
-    decode_word_f32(__builtin_nontemporal_load(wm + i), e4m3<0>(sm[i >> 1]), v);
-    if (gs) {
+  for (int64_t mat = blockIdx.y; mat < batch; mat += gridDim.y) {
+    const uint32_t* wm = w + mat * wpm;
+    const uint8_t* sm = sc + mat * (wpm >> 1);
+    TO* om = out + mat * wpm * 8;
+    const float g = gs ? gs[mat] / kGlobalDivisor : 1.0f;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < wpm; i += stride) {
+      float v[8];
+      decode_word_f32(__builtin_nontemporal_load(wm + i), e4m3<0>(sm[i >> 1]), v);
+      if (gs) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] *= g;
+        for (int k = 0; k < 8; ++k) v[k] *= g;
+      }
+      store8_nt<TO>(om + i * 8, v);
     }
-    store8_nt<TO>(om + i * 8, v);
   }
 }
 
@@ -363,33 +317,17 @@ void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, in
   const int64_t nwords = batch * rows * kw;
   if (nwords == 0) return;
   const int64_t wpm = rows * kw;
-  if (batch <= kMaxGridY) {
-    const dim3 gridf((unsigned)grid_for(wpm, kThreads, 1 << 16), (unsigned)batch);
-    switch (dt) {
-      case NVFP4_F32:
-        dequant_flat_kernel<float><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, static_cast<float*>(out));
-        return;
-      case NVFP4_BF16:
-        dequant_flat_kernel<__bf16><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, static_cast<__bf16*>(out));
-        return;
-      case NVFP4_F16:
-        dequant_flat_kernel<_Float16><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, static_cast<_Float16*>(out));
-        return;
-    }
-  }
-  const int64_t grid = grid_for(nwords, kThreads, 1 << 20);
+  const dim3 gridf((unsigned)grid_for(wpm, kThreads, 1 << 16), (unsigned)(batch < kMaxGridY ? batch : kMaxGridY));
   switch (dt) {
     case NVFP4_F32:
-      dequant_kernel<float><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, sc, gs, nwords, kw, wpm,
-                                                                          static_cast<float*>(out));
+      dequant_flat_kernel<float><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, batch, static_cast<float*>(out));
       break;
     case NVFP4_BF16:
-      dequant_kernel<__bf16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, sc, gs, nwords, kw, wpm,
-                                                                           static_cast<__bf16*>(out));
+      dequant_flat_kernel<__bf16><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, batch, static_cast<__bf16*>(out));
       break;
     case NVFP4_F16:
-      dequant_kernel<_Float16><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(w, sc, gs, nwords, kw, wpm,
-                                                                             static_cast<_Float16*>(out));
+      dequant_flat_kernel<_Float16><<<gridf, dim3(kThreads), 0, s>>>(w, sc, gs, wpm, batch,
+                                                                      static_cast<_Float16*>(out));
       break;
   }
 }

@@ -179,6 +179,30 @@ def test_dequantize_batched_ragged_with_guard_bands(dtype):
                               oracle.f32_to_bf16_bits(want))
 
 
+def test_dequantize_batch_beyond_grid_y_limit():
+    """65,573 tiny matrices (one row of 16 elements each), more than the
+    65,535 block rows of the grid's y axis: the kernel's matrix loop covers
+    the rest.  Seven global scales in turn; bit-exact in bf16 against the
+    oracle per group of matrices sharing a scale."""
+    B = 65573
+    g = synth.rng(132)
+    w = synth.packed_words(g, (B, 1, 2))
+    sc = synth.scale_codes(g, (B, 1, 1), synth.FINITE_POSITIVE_CODES)
+    gs7 = synth.global_scales(g, 7)
+    gs = gs7[np.arange(B) % 7]
+    want = np.empty((B, 1, 16), dtype=np.float32)
+    for k in range(7):
+        want[k::7] = oracle.dequantize(w[k::7], sc[k::7], gs7[k])
+    lib = nv.load_library()
+    out, check = guarded((B, 1, 16), torch.bfloat16)
+    d_w, d_s, d_g = words(w), u8(sc), f32(gs)
+    st = lib.nvfp4_dequantize(ctypes.c_void_p(d_w.data_ptr()), ctypes.c_void_p(d_s.data_ptr()),
+                              ctypes.c_void_p(d_g.data_ptr()), B, 1, 16, 1, ctypes.c_void_p(out.data_ptr()), None)
+    assert st == 0
+    check()
+    assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), oracle.f32_to_bf16_bits(want))
+
+
 def test_dequantize_decode_row_length_bit_exact():
     """Rows of the decode workload's length (K = 5376), 2048 of them."""
     g = synth.rng(131)
