@@ -1117,6 +1117,28 @@ def test_moe_sorted_prefill_full_size(dtype):
     assert_zero_rows(out, case.rhs, case.lhs, 128, 128)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("sort", [True, False])
+def test_moe_prefill_large_batch(dtype, sort):
+    """512 tokens on the MoE shape: about 32 rows per expert, so each
+    (tile, expert) block makes two or more 16-row passes over the expert's
+    plane; sampled experts against the oracle."""
+    wl = synth.WORKLOADS["moe_gather_e128_n1536_k2048_top8"]
+    case = synth.gather_case(wl["seed"] + 3, tokens=512, E=128, N=1536, K=2048, top_k=8, sort=sort,
+                             with_gs=True, out_of_range=(128, INT32_MAX))
+    if dtype == torch.float16:  # keep the f16 outputs finite
+        case.scales = np.minimum(case.scales, 0x50).astype(np.uint8)
+    x_t, x_ref = activations(case.x, dtype)
+    out = nv.gather_qmm(x_t, words(case.w), u8(case.scales), i32(case.rhs), i32(case.lhs),
+                        f32(case.gs), sorted_indices=sort)
+    experts = np.unique(case.rhs[(case.rhs >= 0) & (case.rhs < 128)])
+    pick = experts[np.linspace(0, len(experts) - 1, 8).astype(int)]
+    rows, ref = moe_reference_sampled(case, x_ref, pick)
+    got = host(out)[rows, 0, :]
+    assert oracle.relative_error(got, ref) <= TOL[dtype]
+    assert_zero_rows(out, case.rhs, case.lhs, 128, 512)
+
+
 @pytest.mark.parametrize("tokens", [1, 2, 4, 8])
 def test_moe_unsorted_decode_full_size(tokens):
     wl = synth.WORKLOADS["moe_gather_e128_n1536_k2048_top8"]
