@@ -123,7 +123,9 @@ def _dtype_code(dtype) -> int:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: every library function declares c_void_p arguments, so
+    # ctypes converts it without a wrapper object per call
+    return None if t is None else t.data_ptr()
 
 
 def _check(fn: str, status: int) -> None:
@@ -131,24 +133,33 @@ def _check(fn: str, status: int) -> None:
         raise NVFP4Error(fn, status)
 
 
+# The current stream's handle as an int.  torch's raw accessor skips building
+# a Stream object per call (the per-token path goes through here); the public
+# API serves where it is absent.
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _require_gpu(*tensors: Optional[torch.Tensor]) -> torch.device:
-    dev = None
+    first, index = None, -1
     for t in tensors:
         if t is None:
             continue
-        if not t.is_cuda:
+        d = t.get_device()            # -1 on the CPU
+        if d < 0:
             raise ValueError("all tensors must be on the GPU")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-        if dev is None:
-            dev = t.device
-        elif t.device != dev:
+        if first is None:
+            first, index = t, d
+        elif d != index:
             raise ValueError("all tensors must be on the same device")
-    return dev
+    return None if first is None else first.device
 
 
 # nvfp4_qmm_workspace_size answers, per device and call shape: a per-token
