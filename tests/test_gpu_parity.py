@@ -1224,6 +1224,31 @@ def test_qmm_random_sweep(i, M, K, N, dtype, route, with_gs):
     assert rel(out, ref) <= TOL[dtype], (M, K, N, dtype, route)
 
 
+def _nt_sweep_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        K = int(g.choice([64, 128, 192, 512, 1024, 17, 40, 96 + 16]))      # K % 64 == 0: the dense route
+        if K % 64 == 0 and g.integers(0, 2):
+            K = 64 * int(g.integers(1, 40))
+        M = int(g.choice([1, 3, int(g.integers(4, 65)), int(g.integers(65, 600))]))
+        N = 16 * int(g.integers(1, 60))
+        dtype = [torch.float32, torch.bfloat16, torch.float16][int(g.integers(0, 3))]
+        cases.append((i, M, K, N, dtype, bool(g.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,K,N,dtype,with_gs", _nt_sweep_cases(24, 2026))
+def test_qmm_non_transposed_random_sweep(i, M, K, N, dtype, with_gs):
+    """Non-transposed planes through the binding: the dense copy and the
+    matrix-core GEMM where K % 64 == 0, the generic kernel otherwise."""
+    case = synth.dense_case(7300 + i, M, K, N, transpose=False, with_gs=with_gs)
+    if dtype == torch.float16:   # keep f16 outputs finite
+        case.scales = np.minimum(case.scales, 0x48).astype(np.uint8)
+    out, ref = run_qmm(case, dtype, "auto", guard=True)
+    assert rel(out, ref) <= TOL[dtype], (M, K, N, dtype)
+
+
 def _gather_sweep(n, seed):
     g = np.random.default_rng(seed)
     out = []
