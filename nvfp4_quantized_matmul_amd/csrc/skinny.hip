@@ -250,6 +250,78 @@ __device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const Pai
   }
 }
 
+// Half units for float32 activations with several fragments: unit u is
+// chunk u % 2 of pair-group u / 2 (128 k), so a wavefront holds half the
+// activation registers of a pair-group and twice as many wavefronts fit.
+template <int MF, typename TX>
+struct HalfUnit {
+  uint4 w[kTiles];                 // [tile]: words 4q..4q+3 of the chunk
+  uint4 s;                         // the pair-group's 16 scale bytes of block row `lane`
+  uint4 x[MF][4][XLoads<TX>::n];   // [fragment][step i]: activations of word 16c+4i+q
+};
+
+template <typename TX, int MF>
+__device__ __forceinline__ void load_half(HalfUnit<MF, TX>& p, const Sources<MF>& src, uint32_t u) {
+  constexpr uint32_t E = sizeof(TX);
+  const uint32_t pg = u >> 1, c = u & 1;
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < XLoads<TX>::n; ++h)
+        p.x[f][i][h] = load16(src.x, src.xo[f], (pg * 256u + c * 128u + i * 32u) * E + h * 16u);
+  p.s = load16(src.s, src.so, pg * 16u);
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) p.w[t] = load16(src.w, src.wo[t], pg * 128u + c * 64u);
+}
+
+template <typename TX, int MF>
+__device__ __forceinline__ void compute_half(f32x4_t (&acc)[kTiles][MF], const HalfUnit<MF, TX>& p, uint32_t c,
+                                             int half) {
+  uint32_t s0[kTiles], s1[kTiles];
+  rows_bcast(c == 0 ? p.s.x : p.s.z, s0);
+  rows_bcast(c == 0 ? p.s.y : p.s.w, s1);
+  const uint32_t sh = 8u * (uint32_t)half;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const uint32_t d0 = s0[t] >> sh, d1 = s1[t] >> sh;
+    uint32_t wd[4];
+    transpose_q(p.w[t], wd);
+    const float sc[4] = {e4m3<0>(d0), e4m3<2>(d0), e4m3<0>(d1), e4m3<2>(d1)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8_t A = decode_word_bf16(wd[i], sc[i]);
+#pragma unroll
+      for (int f = 0; f < MF; ++f) {
+        bf16x8_t hi, mid, lo;
+        split3(p.x[f][i][0], p.x[f][i][1], hi, mid, lo);
+        acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, hi, acc[t][f], 0, 0, 0);
+        acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, mid, acc[t][f], 0, 0, 0);
+        acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, lo, acc[t][f], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// This wavefront's half units wid, wid + nw, ... (float32 only) into acc.
+template <int MF>
+__device__ __forceinline__ void run_halves(f32x4_t (&acc)[kTiles][MF], const Sources<MF>& src, int wid, int nw,
+                                           int64_t npg, int half) {
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][f][i] = 0.0f;
+  HalfUnit<MF, float> p;
+  for (int64_t u = wid; u < 2 * npg; u += nw) {
+    load_half<float, MF>(p, src, (uint32_t)u);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_half<float, MF>(acc, p, (uint32_t)(u & 1), half);
+  }
+}
+
 // This wavefront's pair-groups wid, wid + nw, ... into acc.
 template <typename TX, int MF, bool GLU = false>
 __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const Sources<MF>& src, int wid,
@@ -292,7 +364,7 @@ __device__ __forceinline__ void store4(TO* out, int64_t orow, int64_t n, int64_t
 // NVFP4 prefill gap", "Activation-path follow-up"): a block covers 32
 // features, tiles 0 and 1 their gate rows (w, sc, gs) and tiles 2 and 3 their
 // up rows (wu, scu, gsu), and out = act(g * gate) * (g_u * up).
-template <typename TX, int MF, int MAXW, bool GLU = false>
+template <typename TX, int MF, int MAXW, bool GLU = false, bool HALF = false>
 __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict__ x,
                                                           const uint32_t* __restrict__ w,
                                                           const uint8_t* __restrict__ sc,
@@ -323,7 +395,12 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   for (int f = 0; f < MF; ++f) src.xo[f] = (uint32_t)(((16 * f + r16) * K + 8 * q) * (int64_t)sizeof(TX));
 
   f32x4_t acc[kTiles][MF];
-  run_pairgroups<TX, MF, GLU>(acc, src, wid, nw, K / kPG, q >> 1);
+  if constexpr (HALF) {
+    static_assert(__is_same(TX, float) && !GLU, "half units serve float32 activations");
+    run_halves<MF>(acc, src, wid, nw, K / kPG, q >> 1);
+  } else {
+    run_pairgroups<TX, MF, GLU>(acc, src, wid, nw, K / kPG, q >> 1);
+  }
 
   // Partial sums of the wavefronts, added in wavefront order.
 #pragma unroll
@@ -369,14 +446,16 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   }
 }
 
-// One wavefront per pair-group up to MAXW wavefronts.
-template <typename TX, int MF, int MAXW>
+// One wavefront per pair-group (per half unit with HALF) up to MAXW
+// wavefronts.
+template <typename TX, int MF, int MAXW, bool HALF = false>
 void launch_mf(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
                const float* gs, TX* out, hipStream_t s) {
   const int64_t blocks = (N + kRows - 1) / kRows;
-  const int64_t npg = K / kPG;
-  const int waves = (int)(npg < MAXW ? npg : MAXW);
-  skinny_kernel<TX, MF, MAXW><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, N);
+  const int64_t units = (HALF ? 2 : 1) * (K / kPG);
+  const int waves = (int)(units < MAXW ? units : MAXW);
+  skinny_kernel<TX, MF, MAXW, false, HALF><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out,
+                                                                                             M, K, N);
 }
 
 template <typename TX, int MF, int MAXW>
@@ -548,9 +627,9 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
       float* of = static_cast<float*>(out);
       switch ((M + 15) / 16) {
         case 1: launch_mf<float, 1, 8>(xf, M, K, N, w, sc, gs, of, s); break;
-        case 2: launch_mf<float, 2, 4>(xf, M, K, N, w, sc, gs, of, s); break;
-        case 3: launch_mf<float, 3, 4>(xf, M, K, N, w, sc, gs, of, s); break;
-        default: launch_mf<float, 4, 4>(xf, M, K, N, w, sc, gs, of, s); break;
+        case 2: launch_mf<float, 2, 8, true>(xf, M, K, N, w, sc, gs, of, s); break;
+        case 3: launch_mf<float, 3, 8, true>(xf, M, K, N, w, sc, gs, of, s); break;
+        default: launch_mf<float, 4, 4>(xf, M, K, N, w, sc, gs, of, s); break;   // half units would spill
       }
       break;
     }
