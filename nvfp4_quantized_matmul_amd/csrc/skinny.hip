@@ -622,13 +622,14 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
       break;
     case NVFP4_F32: {
       // float32 activations (three bf16 parts) hold more registers per row
-      // fragment: 179 / 280 / 380 / 460 for one to four fragments, all one
-      // wavefront per SIMD without spills, so every M <= 64 is one launch
-      // and the weight plane is read once.
+      // fragment; with one to three fragments a wavefront takes half
+      // pair-groups (120 / 178 / 243 registers: four, two and two
+      // wavefronts per SIMD), with four whole ones (460, one per SIMD).
+      // Every M <= 64 is one launch and the weight plane is read once.
       const float* xf = static_cast<const float*>(x);
       float* of = static_cast<float*>(out);
       switch ((M + 15) / 16) {
-        case 1: launch_mf<float, 1, 8>(xf, M, K, N, w, sc, gs, of, s); break;
+        case 1: launch_mf<float, 1, 16, true>(xf, M, K, N, w, sc, gs, of, s); break;
         case 2: launch_mf<float, 2, 8, true>(xf, M, K, N, w, sc, gs, of, s); break;
         case 3: launch_mf<float, 3, 8, true>(xf, M, K, N, w, sc, gs, of, s); break;
         default: launch_mf<float, 4, 4>(xf, M, K, N, w, sc, gs, of, s); break;   // half units would spill
