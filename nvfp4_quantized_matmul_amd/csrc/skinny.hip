@@ -42,6 +42,8 @@
 //    lane l taking row l (the gated form: one load per plane, each for its
 //    32 lanes), and lane swaps give each tile's 16 rows to its four q lanes;
 //    word 4i+q uses byte 2i + q/2 of its chunk's eight;
+//  * float32 activations walk half pair-groups (one chunk per step), which
+//    halves a wavefront's activation registers;
 //  * the wavefronts' partial sums meet in LDS at the end, are added in a
 //    fixed order and scaled by g once.
 // All operands are read with buffer loads: one descriptor per plane, a
@@ -250,9 +252,11 @@ __device__ __forceinline__ void compute_pg(f32x4_t (&acc)[kTiles][MF], const Pai
   }
 }
 
-// Half units for float32 activations with several fragments: unit u is
-// chunk u % 2 of pair-group u / 2 (128 k), so a wavefront holds half the
+// Half units for float32 activations (three bf16 parts per element): unit u
+// is chunk u % 2 of pair-group u / 2 (128 k), so a wavefront holds half the
 // activation registers of a pair-group and twice as many wavefronts fit.
+// The multi-row kernel with one to three fragments and the grouped gather
+// take these for float32.
 template <int MF, typename TX>
 struct HalfUnit {
   uint4 w[kTiles];                 // [tile]: words 4q..4q+3 of the chunk
