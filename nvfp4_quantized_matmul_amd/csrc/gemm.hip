@@ -2,9 +2,15 @@
 //
 // The pages' ROCm design (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/
 // GatherQMM", "Summary") dequantizes the whole plane and then calls a vendor
-// GEMM, applying the global scale after the matmul.  Here the dequantize is
-// fused into the GEMM instead, so no dense plane is written to HBM:
+// GEMM, applying the global scale after the matmul.  Here, for transposed
+// planes, the dequantize is fused into the GEMM instead, so no dense plane is
+// written to HBM:
 //
+//  * gemm_mfma_v3_kernel (transposed plane, K % 64 == 0): the main kernel,
+//    operands streamed global -> LDS, each packed word decoded once per block
+//    into exact bf16 (or f16) MFMA operands; float32 activations run it over
+//    their exact three-part bf16 split (split_f32_kernel); forms for the K
+//    split of few tiles and for the gated MLP projection.  Described below.
 //  * gemm_mfma_kernel (bf16 activations, transposed plane, K % 32 == 0):
 //    each wavefront decodes its weight rows straight from the packed words
 //    into bf16 MFMA operands (one 32-bit word = the eight k-values one lane
@@ -12,8 +18,11 @@
 //    (double buffered) and shared by the four wavefronts.  Products
 //    e2m1 * e4m3 are exact in bf16, the MFMA accumulates in float32, and
 //    g = gs / 2688 multiplies each output once at the end.
-//  * gemm_generic_kernel: a float32 FMA tiled GEMM used for float32/f16
-//    activations and for non-transposed planes (quantized along N, any K),
+//  * dequant_nt_kernel + gemm_mfma_dense_kernel (non-transposed planes,
+//    K % 64 == 0): the pages' order, an exact dense transposed copy of the
+//    plane in the caller's workspace, then a matrix-core GEMM on it.
+//  * gemm_generic_kernel: a float32 FMA tiled GEMM for the rest (K not a
+//    multiple of 64, or a form that needs a workspace called without one),
 //    with both tiles decoded to float32 in LDS.
 #include <atomic>
 
