@@ -555,8 +555,27 @@ def other_configs():
         us = timed_us(lambda i: lib.nvfp4_qmm_batched(*bargs), 32)
         nbytes = bc.w.nbytes + bc.scales.nbytes + 8 + xb.numel() * 2 + yb.numel() * 2
         brow.append({"B": 2, "M": M, "dtype": "bf16", "us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
-                     "note": "planes fit the MALL (cache-warm)"})
+                     "note": "planes fit the MALL (cache-warm); one launch for both matrices"})
     out["batched_qmm_b2_k4096_n14336"] = brow
+    # many small matrices (an expert's shape, K = 2048, N = 1536): the
+    # batch in one launch beside one call per matrix
+    bc = synth.batched_case(3610, B=64, M=8, K=2048, N=1536)
+    bw, bs, bg = words_dev(bc.w), u8_dev(bc.scales), torch.from_numpy(bc.gs).to(DEV)
+    brow = []
+    for M in (1, 8):
+        xb = torch.from_numpy(np.ascontiguousarray(bc.x[:, :M])).to(torch.bfloat16).to(DEV)
+        yb = torch.empty((64, M, 1536), dtype=torch.bfloat16, device=DEV)
+        st = stream_ptr()
+        bargs = (P(xb), BF16, 64, 64, M, 2048, 1536, P(bw), P(bs), P(bg), 1, 0, P(yb), st)
+        us = timed_us(lambda i: lib.nvfp4_qmm_batched(*bargs), 32)
+        per = [(P(xb[b]), BF16, M, 2048, 1536, P(bw[b]), P(bs[b]), P(bg[b:b + 1]), 1, 0, P(yb[b]), st)
+               for b in range(64)]
+        per_us = timed_us(lambda i: [lib.nvfp4_qmm(*a) for a in per], 8)
+        nbytes = bc.w.nbytes + bc.scales.nbytes + 256 + xb.numel() * 2 + yb.numel() * 2
+        brow.append({"B": 64, "M": M, "dtype": "bf16", "us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
+                     "per_matrix_calls_us": round(per_us, 3),
+                     "note": "one launch for the batch beside 64 nvfp4_qmm calls (cache-warm)"})
+    out["batched_qmm_b64_k2048_n1536"] = brow
     # MoE unsorted decode at B = 1, 2, 4, 8
     mrow = []
     for B in synth.WORKLOADS["moe_gather_e128_n1536_k2048_top8"]["decode_tokens"]:

@@ -333,10 +333,14 @@ int64_t nvfp4_qmm_glu_workspace_size(int64_t M, int64_t K, int64_t F, nvfp4_dtyp
  *   gs      float [B] or NULL; g[b] = fl32(gs[b] / 2688) (1 without gs)
  *   out     [B, M, N] of dtype
  *
- * Every matrix takes the route nvfp4_qmm would take for (M, K, N).  All
- * checks, including the alignment nvfp4_qmm needs of every matrix's x, w,
- * scales and out pointers, run before anything is enqueued: a negative
- * status launches nothing.  B = 0 is a no-op.
+ * Every matrix takes the route nvfp4_qmm would take for (M, K, N), with
+ * the same kernel and arithmetic, so out[b] equals nvfp4_qmm on matrix b bit
+ * for bit.  Where that kernel is the decode kernel (M = 1) or the multi-row
+ * kernel (2 <= M <= 64), one launch per 65535 matrices covers the batch;
+ * other routes launch once per matrix.  All checks, including the alignment
+ * nvfp4_qmm needs of every matrix's x, w, scales and out pointers, run
+ * before anything is enqueued: a negative status launches nothing.  B = 0 is
+ * a no-op.
  */
 int nvfp4_qmm_batched(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B,
                       int64_t M, int64_t K, int64_t N, const uint32_t* w,

@@ -32,6 +32,16 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
+# Per-source extra flags.  The one-row decode kernels take their first 16
+# argument dwords preloaded into SGPRs by the dispatcher (no scalar load of
+# the argument segment before the first address is known): measured 1.5-2%
+# faster on the decode workload, 2-3% on the MoE decode gather; the
+# multi-row kernel, the matrix-core gather and the GEMMs measured neutral to
+# 1% slower with it.
+FILE_FLAGS = {
+    "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -46,7 +56,7 @@ def sources(directory: str = CSRC):
 
 def _compile(src: str, cc: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
-    cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", os.path.dirname(src), "-c", src, "-o", obj]
+    cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-I", INCLUDE, "-I", os.path.dirname(src), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

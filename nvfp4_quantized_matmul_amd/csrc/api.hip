@@ -426,6 +426,12 @@ int nvfp4_qmm_batched(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B,
     if (st != NVFP4_OK) return st;
   }
   if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
+  // The decode and multi-row kernels take the whole batch in one launch
+  // (the same kernel and arithmetic as one call per matrix); other routes
+  // launch per matrix.
+  if (plan.kind == QmmPlan::kQmv && transpose &&
+      nvfp4host::launch_qmv_batched(x, dtype, B, xs, M, K, N, w, scales, gs, out, stream))
+    return launched();
   for (int64_t b = 0; b < B; ++b)
     qmm_launch(plan, xb ? xb + b * xs * ds : nullptr, dtype, M, K, N, w ? w + b * ws : nullptr,
                scales ? scales + b * ss : nullptr, gs ? gs + b : nullptr, transpose, ob + b * os * ds,

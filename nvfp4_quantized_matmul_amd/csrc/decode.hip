@@ -163,7 +163,9 @@ constexpr int kGatherPlaneLoad = 0;
 // close native NVFP4 prefill gap", "Activation-path follow-up").  The
 // wavefront's two rows are feature f of the gate plane (w, sc, gs) and of the
 // up plane (wu, scu, gsu), and lane 0 stores act(g * gate) * (g_u * up).
-template <typename TX, int CPL, int R, bool GLU = false>
+// BAT: batched weights, blockIdx.y selects the matrix (strides bst); a
+// separate instantiation so the single-matrix kernel reads no strides.
+template <typename TX, int CPL, int R, bool GLU = false, bool BAT = false>
 __global__ __launch_bounds__(64 * qmv1_waves<GLU>()) void qmv1_kernel(const TX* __restrict__ x,
                                                         const uint32_t* w,
                                                         const uint8_t* sc,
@@ -171,9 +173,18 @@ __global__ __launch_bounds__(64 * qmv1_waves<GLU>()) void qmv1_kernel(const TX* 
                                                         TX* __restrict__ out, int64_t K, int64_t N,
                                                         const uint32_t* wu = nullptr,
                                                         const uint8_t* scu = nullptr,
-                                                        const float* __restrict__ gsu = nullptr, int act = 0) {
+                                                        const float* __restrict__ gsu = nullptr, int act = 0,
+                                                        MatrixStrides bst = {}) {
   static_assert(!GLU || R == 2, "the gated form streams one gate row and one up row");
   extern __shared__ uint4 xl[];
+  if constexpr (BAT) {
+    const int64_t bm = blockIdx.y;
+    x += bm * bst.x;
+    w += bm * bst.w;
+    sc += bm * bst.s;
+    out += bm * bst.o;
+    if (gs) gs += bm;
+  }
   const int lane = threadIdx.x & 63;
   constexpr int kW = qmv1_waves<GLU>();
   const int64_t n0 = ((int64_t)blockIdx.x * kW + (threadIdx.x >> 6)) * (GLU ? 1 : R);
@@ -328,13 +339,18 @@ bool try_qmv1_gather(const TX* x, int64_t X, int64_t K, const int32_t* lhs, cons
 
 constexpr int kQmv1Rows = 1;
 
+// B matrices (B <= 65535) with strides bst, one per grid row.
 template <typename TX, int CPL>
 void qmv1_launch(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
-                 const float* gs, TX* out, hipStream_t s) {
+                 const float* gs, TX* out, hipStream_t s, int64_t B, MatrixStrides bst) {
   constexpr int kW = qmv1_waves<false>();
   const int64_t blocks = (N + kW * kQmv1Rows - 1) / (kW * kQmv1Rows);
   const size_t lds = staged_x_bytes<TX>(K);
-  qmv1_kernel<TX, CPL, kQmv1Rows><<<dim3((unsigned)blocks), dim3(64 * kW), lds, s>>>(x, w, sc, gs, out, K, N);
+  if (B > 1)
+    qmv1_kernel<TX, CPL, kQmv1Rows, false, true><<<dim3((unsigned)blocks, (unsigned)B), dim3(64 * kW), lds, s>>>(
+        x, w, sc, gs, out, K, N, nullptr, nullptr, nullptr, 0, bst);
+  else
+    qmv1_kernel<TX, CPL, kQmv1Rows><<<dim3((unsigned)blocks), dim3(64 * kW), lds, s>>>(x, w, sc, gs, out, K, N);
 }
 
 template <typename TX, int CPL>
@@ -364,17 +380,18 @@ bool try_qmv1_glu(const TX* x, int64_t K, int64_t F, const uint32_t* w, const ui
 
 // True when the M = 1 decode kernel handles this K (and launches it):
 // K % 32 == 0, at most 4 chunks per lane (K <= 8192, LDS <= 32 KiB) and a
-// weight plane below 2^31 bytes (32-bit buffer offsets).
+// weight plane below 2^31 bytes (32-bit buffer offsets).  B matrices with
+// strides bst (1 and zeros for one matrix), B <= 65535.
 template <typename TX>
 bool try_qmv1(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
-              const float* gs, TX* out, hipStream_t s) {
+              const float* gs, TX* out, hipStream_t s, int64_t B = 1, MatrixStrides bst = {}) {
   if (K % 32 != 0 || N * (K / 2) >= ((int64_t)1 << 31)) return false;
   const int64_t cpl = (K / 32 + 63) / 64;
   switch (cpl) {
-    case 1: qmv1_launch<TX, 1>(x, K, N, w, sc, gs, out, s); return true;
-    case 2: qmv1_launch<TX, 2>(x, K, N, w, sc, gs, out, s); return true;
-    case 3: qmv1_launch<TX, 3>(x, K, N, w, sc, gs, out, s); return true;
-    case 4: qmv1_launch<TX, 4>(x, K, N, w, sc, gs, out, s); return true;
+    case 1: qmv1_launch<TX, 1>(x, K, N, w, sc, gs, out, s, B, bst); return true;
+    case 2: qmv1_launch<TX, 2>(x, K, N, w, sc, gs, out, s, B, bst); return true;
+    case 3: qmv1_launch<TX, 3>(x, K, N, w, sc, gs, out, s, B, bst); return true;
+    case 4: qmv1_launch<TX, 4>(x, K, N, w, sc, gs, out, s, B, bst); return true;
     default: return false;
   }
 }
@@ -385,14 +402,16 @@ bool try_qmv1(const TX* x, int64_t K, int64_t N, const uint32_t* w, const uint8_
 namespace nvfp4host {
 
 bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const uint32_t* w,
-                   const uint8_t* sc, const float* gs, void* out, hipStream_t s) {
+                   const uint8_t* sc, const float* gs, void* out, hipStream_t s, int64_t B, int64_t x_stride) {
+  const MatrixStrides bst{x_stride, N * (K / 8), N * (K / 16), N};
   switch (dt) {
     case NVFP4_BF16:
-      return try_qmv1<__bf16>(static_cast<const __bf16*>(x), K, N, w, sc, gs, static_cast<__bf16*>(out), s);
+      return try_qmv1<__bf16>(static_cast<const __bf16*>(x), K, N, w, sc, gs, static_cast<__bf16*>(out), s, B, bst);
     case NVFP4_F32:
-      return try_qmv1<float>(static_cast<const float*>(x), K, N, w, sc, gs, static_cast<float*>(out), s);
+      return try_qmv1<float>(static_cast<const float*>(x), K, N, w, sc, gs, static_cast<float*>(out), s, B, bst);
     case NVFP4_F16:
-      return try_qmv1<_Float16>(static_cast<const _Float16*>(x), K, N, w, sc, gs, static_cast<_Float16*>(out), s);
+      return try_qmv1<_Float16>(static_cast<const _Float16*>(x), K, N, w, sc, gs, static_cast<_Float16*>(out), s,
+                                B, bst);
   }
   return false;
 }

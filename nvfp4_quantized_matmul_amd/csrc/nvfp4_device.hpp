@@ -27,6 +27,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
+// Per-matrix strides of a batch of weight matrices launched together (grid
+// dimension y is the matrix): elements of x and out, words of the weight
+// plane, bytes of the scale plane; the global scale advances by one float.
+// All zero for a single matrix.
+struct MatrixStrides {
+  int64_t x, w, s, o;
+};
+
 // The divisor of the global scale: 448 (largest E4M3) * 6 (largest E2M1)
 // (mlxcel PR "native NVFP4 for ROCm QuantizedMatmul/GatherQMM", "Summary").
 constexpr float kGlobalDivisor = 2688.0f;

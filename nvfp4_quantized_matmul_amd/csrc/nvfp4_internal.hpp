@@ -25,8 +25,6 @@ void launch_dequantize(const uint32_t* w, const uint8_t* sc, const float* gs, in
 // with gs_in, gs_out (if not NULL) receives a copy of it.
 void launch_quantize(const void* w, nvfp4_dtype_t dt, int64_t batch, int64_t rows, int64_t cols,
                      const float* gs_in, uint32_t* w_out, uint8_t* sc_out, float* gs_out, hipStream_t s);
-// Decode kernel (M = 1): returns false, launching nothing, when K is not
-// a multiple of 32, K > 8192 or the weight plane reaches 2^31 bytes.
 // Gated projection at M = 1 in one launch of the decode kernel (two rows
 // per wavefront: a feature's gate row and up row).  decode_glu_applies says
 // whether launch_decode_glu takes these sizes (it returns false otherwise).
@@ -48,16 +46,34 @@ bool launch_decode_gather(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t K,
                           const int32_t* rhs, int64_t R, const uint32_t* w, const uint8_t* sc, const float* gs,
                           int64_t E, int64_t N, void* out, hipStream_t s);
 
+// Decode kernel (M = 1): returns false, launching nothing, when K is not
+// a multiple of 32, K > 8192 or the weight plane reaches 2^31 bytes.
+// With B > 1 (B <= 65535), one launch serves B matrices: matrix b reads
+// x + b * x_stride (elements), plane b, scales b and gs[b] (when gs is not
+// NULL) and writes out + b * N.
 bool launch_decode(const void* x, nvfp4_dtype_t dt, int64_t K, int64_t N, const uint32_t* w,
-                   const uint8_t* sc, const float* gs, void* out, hipStream_t s);
+                   const uint8_t* sc, const float* gs, void* out, hipStream_t s, int64_t B = 1,
+                   int64_t x_stride = 0);
 // Dense qmv: out[M,N] = x[M,K] @ W[N,K]^T (transposed plane).
 void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
                 const uint32_t* w, const uint8_t* sc, const float* gs, void* out, hipStream_t s);
 // MFMA kernel for 2 <= M <= 64 (bf16, f16, or f32 activations split into
 // three bf16 parts), transposed plane, K % 256 == 0, 16-byte aligned x, w
-// and scales; returns false (launching nothing) otherwise.
+// and scales; returns false (launching nothing) otherwise.  With B > 1 (B <=
+// 65535) one launch serves B matrices as launch_decode's batched form does
+// (x + b * x_stride elements, plane, scales and gs[b] of matrix b; out + b *
+// M * N).
 bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
-                   const uint8_t* sc, const float* gs, void* out, hipStream_t s);
+                   const uint8_t* sc, const float* gs, void* out, hipStream_t s, int64_t B = 1,
+                   int64_t x_stride = 0);
+// launch_qmv over B weight matrices in one launch per 65535 of them, when the
+// kernel launch_qmv would pick for one matrix (decode at M = 1, multi-row
+// for 2 <= M <= 64) has a batched form and applies; returns false, launching
+// nothing, otherwise.  Matrix b: x + b * x_stride elements, w + b * N * K/8,
+// sc + b * N * K/16, gs + b (gs may be NULL), out + b * M * N.
+bool launch_qmv_batched(const void* x, nvfp4_dtype_t dt, int64_t B, int64_t x_stride, int64_t M, int64_t K,
+                        int64_t N, const uint32_t* w, const uint8_t* sc, const float* gs, void* out,
+                        hipStream_t s);
 // GatherQMM through the MFMA kernel (bf16 and f16 activations directly,
 // f32 as three bf16 parts): each expert's pairs are gathered and multiplied
 // together.  Needs K % 256 == 0, E >= 1, X >= 1, 16-byte aligned x, w and

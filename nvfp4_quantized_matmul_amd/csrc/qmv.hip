@@ -281,6 +281,29 @@ void gather_dispatch(const TX* x, int64_t X, int64_t M, int64_t K, const int32_t
 
 namespace nvfp4host {
 
+bool launch_qmv_batched(const void* x, nvfp4_dtype_t dt, int64_t B, int64_t x_stride, int64_t M, int64_t K,
+                        int64_t N, const uint32_t* w, const uint8_t* sc, const float* gs, void* out,
+                        hipStream_t s) {
+  if (B < 2 || M < 1 || M > 64) return false;
+  const int64_t ds = dt == NVFP4_F32 ? 4 : 2;
+  const char* xb = static_cast<const char*>(x);
+  char* ob = static_cast<char*>(out);
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxGridY) {
+    const int64_t nb = B - b0 < kMaxGridY ? B - b0 : kMaxGridY;
+    const void* xc = xb + b0 * x_stride * ds;
+    const uint32_t* wc = w + b0 * N * (K / 8);
+    const uint8_t* sc_c = sc + b0 * N * (K / 16);
+    const float* gc = gs ? gs + b0 : nullptr;
+    void* oc = ob + b0 * M * N * ds;
+    const bool ok = M == 1 ? launch_decode(xc, dt, K, N, wc, sc_c, gc, oc, s, nb, x_stride)
+                           : launch_skinny(xc, dt, M, K, N, wc, sc_c, gc, oc, s, nb, x_stride);
+    // Every chunk has the same sizes and alignment, so only the first can
+    // decline.
+    if (!ok) return false;
+  }
+  return true;
+}
+
 void launch_qmv(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N,
                 const uint32_t* w, const uint8_t* sc, const float* gs, void* out, hipStream_t s) {
   const bool vec4 = (K % 32) == 0;

@@ -368,7 +368,9 @@ __device__ __forceinline__ void store4(TO* out, int64_t orow, int64_t n, int64_t
 // NVFP4 prefill gap", "Activation-path follow-up"): a block covers 32
 // features, tiles 0 and 1 their gate rows (w, sc, gs) and tiles 2 and 3 their
 // up rows (wu, scu, gsu), and out = act(g * gate) * (g_u * up).
-template <typename TX, int MF, int MAXW, bool GLU = false, bool HALF = false>
+// BAT: batched weights, blockIdx.y selects the matrix (strides bst); a
+// separate instantiation so the single-matrix kernel reads no strides.
+template <typename TX, int MF, int MAXW, bool GLU = false, bool HALF = false, bool BAT = false>
 __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict__ x,
                                                           const uint32_t* __restrict__ w,
                                                           const uint8_t* __restrict__ sc,
@@ -377,8 +379,17 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
                                                           int64_t K, int64_t N,
                                                           const uint32_t* __restrict__ wu = nullptr,
                                                           const uint8_t* __restrict__ scu = nullptr,
-                                                          const float* __restrict__ gsu = nullptr, int act = 0) {
+                                                          const float* __restrict__ gsu = nullptr, int act = 0,
+                                                          MatrixStrides bst = {}) {
   __shared__ f32x4_t red[MAXW][kTiles * MF][64];
+  if constexpr (BAT) {
+    const int64_t bm = blockIdx.y;
+    x += bm * bst.x;
+    w += bm * bst.w;
+    sc += bm * bst.s;
+    out += bm * bst.o;
+    if (gs) gs += bm;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -451,15 +462,19 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
 }
 
 // One wavefront per pair-group (per half unit with HALF) up to MAXW
-// wavefronts.
+// wavefronts; B matrices (B <= 65535) with strides bst, one per grid row.
 template <typename TX, int MF, int MAXW, bool HALF = false>
 void launch_mf(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
-               const float* gs, TX* out, hipStream_t s) {
+               const float* gs, TX* out, hipStream_t s, int64_t B, const MatrixStrides& bst) {
   const int64_t blocks = (N + kRows - 1) / kRows;
   const int64_t units = (HALF ? 2 : 1) * (K / kPG);
   const int waves = (int)(units < MAXW ? units : MAXW);
-  skinny_kernel<TX, MF, MAXW, false, HALF><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out,
-                                                                                             M, K, N);
+  if (B > 1)
+    skinny_kernel<TX, MF, MAXW, false, HALF, true><<<dim3((unsigned)blocks, (unsigned)B), dim3(64 * waves), 0, s>>>(
+        x, w, sc, gs, out, M, K, N, nullptr, nullptr, nullptr, 0, bst);
+  else
+    skinny_kernel<TX, MF, MAXW, false, HALF><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M,
+                                                                                               K, N);
 }
 
 template <typename TX, int MF, int MAXW>
@@ -476,12 +491,12 @@ void launch_mf_glu(const TX* x, int64_t M, int64_t K, int64_t F, const uint32_t*
 // 16-bit activations: up to four 16-row fragments in one launch.
 template <typename TX>
 void launch_rows16(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, const uint8_t* sc,
-                   const float* gs, TX* out, hipStream_t s) {
+                   const float* gs, TX* out, hipStream_t s, int64_t B, const MatrixStrides& bst) {
   switch ((M + 15) / 16) {
-    case 1: launch_mf<TX, 1, 16>(x, M, K, N, w, sc, gs, out, s); break;
-    case 2: launch_mf<TX, 2, 8>(x, M, K, N, w, sc, gs, out, s); break;
-    case 3: launch_mf<TX, 3, 4>(x, M, K, N, w, sc, gs, out, s); break;
-    default: launch_mf<TX, 4, 4>(x, M, K, N, w, sc, gs, out, s); break;
+    case 1: launch_mf<TX, 1, 16>(x, M, K, N, w, sc, gs, out, s, B, bst); break;
+    case 2: launch_mf<TX, 2, 8>(x, M, K, N, w, sc, gs, out, s, B, bst); break;
+    case 3: launch_mf<TX, 3, 4>(x, M, K, N, w, sc, gs, out, s, B, bst); break;
+    default: launch_mf<TX, 4, 4>(x, M, K, N, w, sc, gs, out, s, B, bst); break;
   }
 }
 
@@ -611,7 +626,10 @@ void gather_mfma_kernel(
 namespace nvfp4host {
 
 bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_t N, const uint32_t* w,
-                   const uint8_t* sc, const float* gs, void* out, hipStream_t s) {
+                   const uint8_t* sc, const float* gs, void* out, hipStream_t s, int64_t B, int64_t x_stride) {
+  // Per-matrix offsets keep the 16-byte alignment: K % 256 == 0 makes every
+  // plane, scale plane and activation matrix a multiple of 16 bytes.
+  const MatrixStrides bst{x_stride, N * (K / 8), N * (K / 16), M * N};
   // 16-byte activation, word and scale loads; byte offsets within 32 bits.
   const bool aligned =
       ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(sc)) & 15) == 0;
@@ -619,10 +637,11 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
   if ((N + kRows) * (K / 2) >= kMaxPlaneBytes || 64 * K * 4 >= kMaxPlaneBytes) return false;
   switch (dt) {
     case NVFP4_BF16:
-      launch_rows16(static_cast<const __bf16*>(x), M, K, N, w, sc, gs, static_cast<__bf16*>(out), s);
+      launch_rows16(static_cast<const __bf16*>(x), M, K, N, w, sc, gs, static_cast<__bf16*>(out), s, B, bst);
       break;
     case NVFP4_F16:
-      launch_rows16(static_cast<const _Float16*>(x), M, K, N, w, sc, gs, static_cast<_Float16*>(out), s);
+      launch_rows16(static_cast<const _Float16*>(x), M, K, N, w, sc, gs, static_cast<_Float16*>(out), s, B,
+                    bst);
       break;
     case NVFP4_F32: {
       // float32 activations (three bf16 parts) hold more registers per row
@@ -633,10 +652,10 @@ bool launch_skinny(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int64_
       const float* xf = static_cast<const float*>(x);
       float* of = static_cast<float*>(out);
       switch ((M + 15) / 16) {
-        case 1: launch_mf<float, 1, 16, true>(xf, M, K, N, w, sc, gs, of, s); break;
-        case 2: launch_mf<float, 2, 8, true>(xf, M, K, N, w, sc, gs, of, s); break;
-        case 3: launch_mf<float, 3, 8, true>(xf, M, K, N, w, sc, gs, of, s); break;
-        default: launch_mf<float, 4, 4>(xf, M, K, N, w, sc, gs, of, s); break;   // half units would spill
+        case 1: launch_mf<float, 1, 16, true>(xf, M, K, N, w, sc, gs, of, s, B, bst); break;
+        case 2: launch_mf<float, 2, 8, true>(xf, M, K, N, w, sc, gs, of, s, B, bst); break;
+        case 3: launch_mf<float, 3, 8, true>(xf, M, K, N, w, sc, gs, of, s, B, bst); break;
+        default: launch_mf<float, 4, 4>(xf, M, K, N, w, sc, gs, of, s, B, bst); break;   // half units would spill
       }
       break;
     }

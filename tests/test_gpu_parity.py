@@ -461,6 +461,38 @@ def test_qmm_batched_multirow_plane(dtype):
     assert rel(out, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M", [1, 2, 16, 33, 64])
+@pytest.mark.parametrize("broadcast_x", [False, True])
+def test_qmm_batched_one_launch_equals_single_calls(dtype, M, broadcast_x):
+    """On the qmv route the decode (M = 1) and multi-row (2 <= M <= 64)
+    kernels take the whole batch in one launch: every matrix's result is
+    within tolerance of the oracle and bit for bit what one qmm call on that
+    matrix alone gives."""
+    c = synth.batched_case(3800 + M, B=5, M=M, K=512, N=272, broadcast_x=broadcast_x)
+    out, ref = run_qmm_batched(c, dtype)
+    assert rel(out, ref) <= TOL[dtype]
+    x_t, _ = activations(c.x, dtype)
+    for b in range(c.B):
+        single = nv.qmm(x_t[0 if broadcast_x else b], words(c.w[b]), u8(c.scales[b]), f32(c.gs[b:b + 1]))
+        assert torch.equal(out[b], single), f"matrix {b}"
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_qmm_batched_beyond_one_grid_row_limit(M):
+    """65540 matrices (K = 256, N = 16), more than one launch's 65535 grid
+    rows: the batch goes out in two launches; matrices on both sides of the
+    split are checked against the oracle one by one."""
+    B = 65540
+    c = synth.batched_case(3900 + M, B=B, M=M, K=256, N=16, broadcast_x=True)
+    x_t, x_ref = activations(c.x, torch.bfloat16)
+    out = nv.qmm_batched(x_t, words(c.w), u8(c.scales), f32(c.gs))
+    torch.cuda.synchronize()
+    for b in (0, 1, 65533, 65534, 65535, 65536, B - 1):
+        ref = oracle.qmm(x_ref[0], c.w[b], c.scales[b], c.gs[b])
+        assert rel(out[b], ref) <= TOL[torch.bfloat16], f"matrix {b}"
+
+
 def test_qmm_batched_empty_and_misaligned():
     c = synth.batched_case(3700, B=2, M=1, K=32, N=4)
     x_t, _ = activations(c.x, torch.bfloat16)
