@@ -42,6 +42,11 @@
 //    lane l taking row l (the gated form: one load per plane, each for its
 //    32 lanes), and lane swaps give each tile's 16 rows to its four q lanes;
 //    word 4i+q uses byte 2i + q/2 of its chunk's eight;
+//  * with bf16 activations (one 16-row fragment in the multi-row kernel,
+//    every pass of the gather) the weights go through a private LDS slice
+//    per wavefront instead, copied by load-to-LDS instructions that read 8
+//    whole rows of 128 bytes each, and are read back in the layout above
+//    (described at run_pairgroups_lds);
 //  * float32 activations walk half pair-groups (one chunk per step), which
 //    halves a wavefront's activation registers;
 //  * the wavefronts' partial sums meet in LDS at the end, are added in a
@@ -346,6 +351,152 @@ __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weights through LDS (2-byte activations).  In registers, a weight load
+// takes 64 bytes of each of 16 rows (the MFMA operand layout allows no more
+// per row), so every load touches 16 cache lines for half of each.  Here
+// each wavefront copies its pair-group's 64 rows x 128 bytes into its own
+// LDS slice with eight load-to-LDS instructions of 8 whole rows each (8
+// lines per instruction), then reads every lane's 16 bytes back in the MFMA
+// layout.  Tile t of the slice is its own __shared__ array (so the
+// compiler's wait for a tile's copies counts only the copies queued after
+// them, not every copy into the slice); load (t, h) fills units 64 h + l of
+// it: lane l takes row 16 t + 8 h + l / 8 of the block and its piece (l % 8)
+// ^ f, f = (row within the tile / 2) % 8, so the 16 lanes reading one piece
+// of 16 consecutive rows hit 16 distinct bank groups.  The slice is private
+// to the wavefront: its own load counter orders the copy and the reads, with
+// no barrier.  Rows past N read zeros (buffer range check).
+constexpr int kTileUnits = 128;   // 16-byte units of one tile's pair-group weights (16 rows x 128 bytes)
+#define NVFP4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+struct LdsWeights {
+  uint4* tile[kTiles];      // this wavefront's part of each tile array
+  uint32_t go[kTiles][2];   // plane byte offset of this lane's piece in load (t, h), pair-group 0
+  uint32_t ro[2];           // unit of words 4q..4q+3 of chunk c of row r16 in a tile
+};
+
+template <bool GLU>
+__device__ __forceinline__ void set_lds_rows(LdsWeights& lw, uint4* t0, uint4* t1, uint4* t2, uint4* t3,
+                                             int64_t n0, int lane, int64_t K) {
+  lw.tile[0] = t0;
+  lw.tile[1] = t1;
+  lw.tile[2] = t2;
+  lw.tile[3] = t3;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rt = 8 * h + (lane >> 3);                 // row within the tile
+      const int piece = (lane & 7) ^ ((rt >> 1) & 7);
+      const int64_t row = n0 + 16 * (GLU ? (t & 1) : t) + rt;
+      lw.go[t][h] = (uint32_t)(row * (K / 2) + 16 * piece);
+    }
+  const int r16 = lane & 15, q = lane >> 4;
+  const int base = (r16 >> 3) * 64 + (r16 & 7) * 8, f = (r16 >> 1) & 7;
+  lw.ro[0] = (uint32_t)(base + (q ^ f));
+  lw.ro[1] = (uint32_t)(base + ((4 + q) ^ f));
+}
+
+// One pair-group: activations and scales into registers (as load_pg), then
+// the eight weight copies, tile by tile.
+template <typename TX, int MF, bool GLU>
+__device__ __forceinline__ void load_pg_lds(PairGroup<MF, TX>& p, const Sources<MF>& src, const LdsWeights& lw,
+                                            uint32_t pg) {
+  constexpr uint32_t E = sizeof(TX);
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < XLoads<TX>::n; ++h)
+          p.x[f][4 * c + i][h] = load16(src.x, src.xo[f], (pg * 256u + c * 128u + i * 32u) * E + h * 16u);
+  p.s = load16(src.s, src.so, pg * 16u);
+  if constexpr (GLU) {
+    const uint4 u = load16(src.s2, src.so2, pg * 16u);
+    p.s = make_uint4(p.s.x | u.x, p.s.y | u.y, p.s.z | u.z, p.s.w | u.w);
+  }
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const rsrc_t& wr = (GLU && t >= 2) ? src.w2 : src.w;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, NVFP4_LDS(lw.tile[t] + 64 * h), 16, lw.go[t][h], pg * 128u, 0,
+                                               0);
+    }
+}
+
+// Tile-major multiply of a staged pair-group: tile t waits for its two
+// copies (issued last, in tile order: 2 (3 - t) loads may still be in
+// flight), reads both chunks' words from the slice and multiplies them as
+// compute_pg does (the same k order per accumulator, so the same sums).
+template <typename TX, int MF>
+__device__ __forceinline__ void compute_pg_lds(f32x4_t (&acc)[kTiles][MF], const PairGroup<MF, TX>& p,
+                                               const LdsWeights& lw, int half) {
+  uint32_t sx[kTiles], sy[kTiles], sz[kTiles], sw[kTiles];
+  rows_bcast(p.s.x, sx);
+  rows_bcast(p.s.y, sy);
+  rows_bcast(p.s.z, sz);
+  rows_bcast(p.s.w, sw);
+  const uint32_t sh = 8u * (uint32_t)half;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    __builtin_amdgcn_sched_barrier(0);
+    switch (t) {
+      case 0: __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | 6); break;
+      case 1: __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | 4); break;
+      case 2: __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | 2); break;
+      default: __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | 0); break;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 wv[2] = {lw.tile[t][lw.ro[0]], lw.tile[t][lw.ro[1]]};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t d0 = (c == 0 ? sx[t] : sz[t]) >> sh;
+      const uint32_t d1 = (c == 0 ? sy[t] : sw[t]) >> sh;
+      uint32_t wd[4];
+      transpose_q(wv[c], wd);
+      const float sc[4] = {e4m3<0>(d0), e4m3<2>(d0), e4m3<0>(d1), e4m3<2>(d1)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (__is_same(TX, _Float16)) {
+          const f16x8_t A = decode_word_f16(wd[i], sc[i]);
+#pragma unroll
+          for (int f = 0; f < MF; ++f)
+            acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                A, __builtin_bit_cast(f16x8_t, p.x[f][4 * c + i][0]), acc[t][f], 0, 0, 0);
+        } else {
+          const bf16x8_t A = decode_word_bf16(wd[i], sc[i]);
+#pragma unroll
+          for (int f = 0; f < MF; ++f)
+            acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A, __builtin_bit_cast(bf16x8_t, p.x[f][4 * c + i][0]), acc[t][f], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <typename TX, int MF, bool GLU>
+__device__ __forceinline__ void run_pairgroups_lds(f32x4_t (&acc)[kTiles][MF], const Sources<MF>& src,
+                                                   const LdsWeights& lw, int wid, int nw, int64_t npg, int half) {
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][f][i] = 0.0f;
+  PairGroup<MF, TX> p;
+  for (int64_t pg = wid; pg < npg; pg += nw) {
+    // the previous pair-group's slice reads have all been consumed (their
+    // multiplies waited for them), so the slice may be refilled
+    load_pg_lds<TX, MF, GLU>(p, src, lw, (uint32_t)pg);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_pg_lds<TX, MF>(acc, p, lw, half);
+  }
+}
+
 // C[n][m] of tile t: element i of lane l is weight row 16t + 4(l/16) + i,
 // activation row l % 16 of the fragment; four bf16 to out row `orow`.
 template <typename TO>
@@ -381,7 +532,29 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
                                                           const uint8_t* __restrict__ scu = nullptr,
                                                           const float* __restrict__ gsu = nullptr, int act = 0,
                                                           MatrixStrides bst = {}) {
-  __shared__ f32x4_t red[MAXW][kTiles * MF][64];
+  // bf16 activations with one fragment (the plain form) stage the weights
+  // in per-wavefront LDS slices, one array per tile (kPart units per
+  // wavefront each), which later hold the wavefront's partial sums of that
+  // tile; the other forms keep the weights in registers and the partial
+  // sums in a buffer of their own.  Measured, same process (K = 4096, N =
+  // 14336, bit-identical): M = 3 / 6 / 16 took 9.7-9.9 / 9.9-10.2 / 11.5
+  // us against 10.2-10.4 / 10.6 / 12.6 us; with two to four fragments or in
+  // the gated form the staging measured up to 10% slower (M = 17, 33, 64;
+  // gated M = 3).
+  constexpr bool kLW = __is_same(TX, __bf16) && MF == 1 && !GLU;
+  constexpr int kPart = kTileUnits > MF * 64 ? kTileUnits : MF * 64;
+  constexpr int kLwWaves = kLW ? MAXW : 1;
+  __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles * MF][kLW ? 1 : 64];
+  __shared__ uint4 wt0[kLwWaves * kPart], wt1[kLwWaves * kPart], wt2[kLwWaves * kPart], wt3[kLwWaves * kPart];
+  // partial sums of wavefront k, tile t, fragment f: 64 lanes from red(k, t, f)
+  auto red = [&](int k, int t, int f) -> f32x4_t* {
+    if constexpr (kLW) {
+      uint4* const tl = t == 0 ? wt0 : t == 1 ? wt1 : t == 2 ? wt2 : wt3;
+      return reinterpret_cast<f32x4_t*>(tl + k * kPart + f * 64);
+    } else {
+      return &red_s[k][t * MF + f][0];
+    }
+  };
   if constexpr (BAT) {
     const int64_t bm = blockIdx.y;
     x += bm * bst.x;
@@ -413,15 +586,20 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   if constexpr (HALF) {
     static_assert(__is_same(TX, float) && !GLU, "half units serve float32 activations");
     run_halves<MF>(acc, src, wid, nw, K / kPG, q >> 1);
+  } else if constexpr (kLW) {
+    LdsWeights lw;
+    set_lds_rows<GLU>(lw, wt0 + wid * kPart, wt1 + wid * kPart, wt2 + wid * kPart, wt3 + wid * kPart, n0, lane, K);
+    run_pairgroups_lds<TX, MF, GLU>(acc, src, lw, wid, nw, K / kPG, q >> 1);
   } else {
     run_pairgroups<TX, MF, GLU>(acc, src, wid, nw, K / kPG, q >> 1);
   }
 
-  // Partial sums of the wavefronts, added in wavefront order.
+  // Partial sums of the wavefronts, added in wavefront order (each
+  // wavefront's own slice, whose weights it no longer reads).
 #pragma unroll
   for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-    for (int f = 0; f < MF; ++f) red[wid][t * MF + f][lane] = acc[t][f];
+    for (int f = 0; f < MF; ++f) red(wid, t, f)[lane] = acc[t][f];
   __syncthreads();
 
   const float g = global_factor(gs, 0);
@@ -429,9 +607,10 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
     const float gu = global_factor(gsu, 0);
     for (int idx = threadIdx.x; idx < 2 * MF * 64; idx += blockDim.x) {
       const int tf = idx >> 6, l = idx & 63;   // tile t = tf / MF in {0, 1}, fragment f
-      f32x4_t gate = red[0][tf][l], up = red[0][tf + 2 * MF][l];
+      const int t = tf / MF, f = tf % MF;   // gate tile t, up tile t + 2
+      f32x4_t gate = red(0, t, f)[l], up = red(0, t + 2, f)[l];
       for (int k = 1; k < nw; ++k) {
-        const f32x4_t pg = red[k][tf][l], pu = red[k][tf + 2 * MF][l];
+        const f32x4_t pg = red(k, t, f)[l], pu = red(k, t + 2, f)[l];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           gate[i] += pg[i];
@@ -441,7 +620,6 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
       f32x4_t v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = glu_act(gate[i] * g, act) * (up[i] * gu);
-      const int t = tf / MF, f = tf % MF;
       const int64_t m = 16 * f + (l & 15);
       if (m < M) store4(out, m, n0 + 16 * t + 4 * (l >> 4), N, v, 1.0f);
     }
@@ -450,9 +628,9 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   for (int idx = threadIdx.x; idx < kTiles * MF * 64; idx += blockDim.x) {
     const int tf = idx >> 6, l = idx & 63;
     const int t = tf / MF, f = tf % MF;
-    f32x4_t v = red[0][tf][l];
+    f32x4_t v = red(0, t, f)[l];
     for (int k = 1; k < nw; ++k) {
-      const f32x4_t pk = red[k][tf][l];
+      const f32x4_t pk = red(k, t, f)[l];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] += pk[i];
     }
@@ -473,8 +651,8 @@ void launch_mf(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, 
     skinny_kernel<TX, MF, MAXW, false, HALF, true><<<dim3((unsigned)blocks, (unsigned)B), dim3(64 * waves), 0, s>>>(
         x, w, sc, gs, out, M, K, N, nullptr, nullptr, nullptr, 0, bst);
   else
-    skinny_kernel<TX, MF, MAXW, false, HALF><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M,
-                                                                                               K, N);
+    skinny_kernel<TX, MF, MAXW, false, HALF><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out,
+                                                                                                 M, K, N);
 }
 
 template <typename TX, int MF, int MAXW>
@@ -485,7 +663,7 @@ void launch_mf_glu(const TX* x, int64_t M, int64_t K, int64_t F, const uint32_t*
   const int64_t npg = K / kPG;
   const int waves = (int)(npg < MAXW ? npg : MAXW);
   skinny_kernel<TX, MF, MAXW, true><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, F,
-                                                                                       wu, scu, gsu, act);
+                                                                                         wu, scu, gsu, act);
 }
 
 // 16-bit activations: up to four 16-row fragments in one launch.
@@ -520,9 +698,30 @@ void gather_mfma_kernel(
     const TX* __restrict__ x, int X, int Mg, int64_t K, const int32_t* __restrict__ lhs,
     const int32_t* __restrict__ rhs, int R, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
     const float* __restrict__ gs, int E, int64_t N, TX* __restrict__ out) {
-  __shared__ f32x4_t red[MAXW][kTiles][64];
+  // bf16 activations stage the weights in per-wavefront LDS slices, one
+  // array per tile, as the multi-row kernel does; a wavefront's part of
+  // tile t then holds its partial sums of that tile, and the index scan's
+  // counts live in wt0 while no weights are in flight (the scan and the
+  // passes are separated by barriers).  With the two index lists that is 40
+  // KiB, four blocks per compute unit as before.  Other activation types
+  // keep the weights in registers.
+  constexpr bool kLW = __is_same(TX, __bf16);
+  __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles][kLW ? 1 : 64];
+  __shared__ uint4 wt0[(kLW ? MAXW : 1) * kTileUnits], wt1[(kLW ? MAXW : 1) * kTileUnits],
+      wt2[(kLW ? MAXW : 1) * kTileUnits], wt3[(kLW ? MAXW : 1) * kTileUnits];
   __shared__ int list_r[kScanPerThread * 64 * MAXW], list_x[kScanPerThread * 64 * MAXW];
-  __shared__ int wcount[kScanPerThread][MAXW];
+  __shared__ int wcount_s[kLW ? 1 : kScanPerThread * MAXW];
+  static_assert(kScanPerThread * MAXW * 4 <= kTileUnits * 16, "the scan counts fit in wt0");
+  int* const wcount_p = kLW ? reinterpret_cast<int*>(wt0) : wcount_s;
+  auto wcount = [&](int k, int wv) -> int& { return wcount_p[k * MAXW + wv]; };
+  auto red = [&](int k, int t) -> f32x4_t* {
+    if constexpr (kLW) {
+      uint4* const tl = t == 0 ? wt0 : t == 1 ? wt1 : t == 2 ? wt2 : wt3;
+      return reinterpret_cast<f32x4_t*>(tl + k * kTileUnits);
+    } else {
+      return &red_s[k][t][0];
+    }
+  };
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -564,7 +763,7 @@ void gather_mfma_kernel(
 #pragma unroll
     for (int k = 0; k < kScanPerThread; ++k) {
       bal[k] = __ballot(mine[k]);
-      if (lane == 0) wcount[k][wid] = __popcll(bal[k]);
+      if (lane == 0) wcount(k, wid) = __popcll(bal[k]);
     }
     __syncthreads();
     int total = 0;
@@ -572,8 +771,8 @@ void gather_mfma_kernel(
     for (int k = 0; k < kScanPerThread; ++k) {
       int off = total;
       for (int i = 0; i < nw; ++i) {
-        off += i < wid ? wcount[k][i] : 0;
-        total += wcount[k][i];
+        off += i < wid ? wcount(k, i) : 0;
+        total += wcount(k, i);
       }
       if (mine[k]) {
         const int pos = off + __popcll(bal[k] & ((1ull << lane) - 1));
@@ -597,16 +796,24 @@ void gather_mfma_kernel(
           src.xo[0] = (uint32_t)(list_x[j / Mg] * Mg + j % Mg) * xrow_bytes + (uint32_t)(8 * sizeof(TX)) * q;
         }
         f32x4_t acc[kTiles][1];
-        if constexpr (__is_same(TX, float)) run_halves<1>(acc, src, wid, nw, K / kPG, q >> 1);
-        else run_pairgroups<TX>(acc, src, wid, nw, K / kPG, q >> 1);
+        if constexpr (__is_same(TX, float)) {
+          run_halves<1>(acc, src, wid, nw, K / kPG, q >> 1);
+        } else if constexpr (kLW) {
+          LdsWeights lw;
+          set_lds_rows<false>(lw, wt0 + wid * kTileUnits, wt1 + wid * kTileUnits, wt2 + wid * kTileUnits,
+                              wt3 + wid * kTileUnits, n0, lane, K);
+          run_pairgroups_lds<TX, 1, false>(acc, src, lw, wid, nw, K / kPG, q >> 1);
+        } else {
+          run_pairgroups<TX>(acc, src, wid, nw, K / kPG, q >> 1);
+        }
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) red[wid][t][lane] = acc[t][0];
+        for (int t = 0; t < kTiles; ++t) red(wid, t)[lane] = acc[t][0];
         __syncthreads();
         for (int idx = threadIdx.x; idx < kTiles * 64; idx += blockDim.x) {
           const int t = idx >> 6, l = idx & 63;
-          f32x4_t v = red[0][t][l];
+          f32x4_t v = red(0, t)[l];
           for (int k = 1; k < nw; ++k) {
-            const f32x4_t pk = red[k][t][l];
+            const f32x4_t pk = red(k, t)[l];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] += pk[i];
           }
