@@ -42,8 +42,9 @@
 //    lane l taking row l (the gated form: one load per plane, each for its
 //    32 lanes), and lane swaps give each tile's 16 rows to its four q lanes;
 //    word 4i+q uses byte 2i + q/2 of its chunk's eight;
-//  * with bf16 activations (one 16-row fragment in the multi-row kernel,
-//    every pass of the gather) the weights go through a private LDS slice
+//  * with bf16 activations and one 16-row fragment in the multi-row kernel,
+//    and with bf16 or f16 in every pass of the gather, the weights go
+//    through a private LDS slice
 //    per wavefront instead, copied by load-to-LDS instructions that read 8
 //    whole rows of 128 bytes each, and are read back in the layout above
 //    (described at run_pairgroups_lds);
@@ -698,14 +699,14 @@ void gather_mfma_kernel(
     const TX* __restrict__ x, int X, int Mg, int64_t K, const int32_t* __restrict__ lhs,
     const int32_t* __restrict__ rhs, int R, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
     const float* __restrict__ gs, int E, int64_t N, TX* __restrict__ out) {
-  // bf16 activations stage the weights in per-wavefront LDS slices, one
+  // 2-byte activations stage the weights in per-wavefront LDS slices, one
   // array per tile, as the multi-row kernel does; a wavefront's part of
   // tile t then holds its partial sums of that tile, and the index scan's
   // counts live in wt0 while no weights are in flight (the scan and the
   // passes are separated by barriers).  With the two index lists that is 40
-  // KiB, four blocks per compute unit as before.  Other activation types
-  // keep the weights in registers.
-  constexpr bool kLW = __is_same(TX, __bf16);
+  // KiB, four blocks per compute unit as before (f16 fits in 128 registers
+  // with it).  float32 keeps the weights in registers.
+  constexpr bool kLW = sizeof(TX) == 2;
   __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles][kLW ? 1 : 64];
   __shared__ uint4 wt0[(kLW ? MAXW : 1) * kTileUnits], wt1[(kLW ? MAXW : 1) * kTileUnits],
       wt2[(kLW ? MAXW : 1) * kTileUnits], wt3[(kLW ? MAXW : 1) * kTileUnits];
