@@ -42,12 +42,12 @@
 //    lane l taking row l (the gated form: one load per plane, each for its
 //    32 lanes), and lane swaps give each tile's 16 rows to its four q lanes;
 //    word 4i+q uses byte 2i + q/2 of its chunk's eight;
-//  * with bf16 activations and one 16-row fragment in the multi-row kernel,
-//    and with bf16 or f16 in every pass of the gather, the weights go
-//    through a private LDS slice
-//    per wavefront instead, copied by load-to-LDS instructions that read 8
-//    whole rows of 128 bytes each, and are read back in the layout above
-//    (described at run_pairgroups_lds);
+//  * with bf16 activations and one, three or four 16-row fragments in the
+//    multi-row kernel, and with bf16 or f16 in every pass of the gather,
+//    the weights go through a private LDS slice per wavefront instead,
+//    copied by load-to-LDS instructions that read 8 whole rows of 128 bytes
+//    each, and are read back in the layout above (described before
+//    set_lds_rows);
 //  * float32 activations walk half pair-groups (one chunk per step), which
 //    halves a wavefront's activation registers;
 //  * the wavefronts' partial sums meet in LDS at the end, are added in a
@@ -479,6 +479,79 @@ __device__ __forceinline__ void compute_pg_lds(f32x4_t (&acc)[kTiles][MF], const
   }
 }
 
+// Chunk-major order for several fragments: the eight weight copies first,
+// then chunk 0's activations, the scales and chunk 1's activations, so
+// chunk 0 of every tile is multiplied while chunk 1's activations stream.
+template <typename TX, int MF, bool GLU>
+__device__ __forceinline__ void load_pg_lds_cm(PairGroup<MF, TX>& p, const Sources<MF>& src, const LdsWeights& lw,
+                                               uint32_t pg) {
+  constexpr uint32_t E = sizeof(TX);
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const rsrc_t& wr = (GLU && t >= 2) ? src.w2 : src.w;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, NVFP4_LDS(lw.tile[t] + 64 * h), 16, lw.go[t][h], pg * 128u, 0,
+                                               0);
+    }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < XLoads<TX>::n; ++h)
+          p.x[f][4 * c + i][h] = load16(src.x, src.xo[f], (pg * 256u + c * 128u + i * 32u) * E + h * 16u);
+    if (c == 0) {
+      p.s = load16(src.s, src.so, pg * 16u);
+      if constexpr (GLU) {
+        const uint4 u = load16(src.s2, src.so2, pg * 16u);
+        p.s = make_uint4(p.s.x | u.x, p.s.y | u.y, p.s.z | u.z, p.s.w | u.w);
+      }
+    }
+  }
+}
+
+template <typename TX, int MF>
+__device__ __forceinline__ void compute_pg_lds_cm(f32x4_t (&acc)[kTiles][MF], const PairGroup<MF, TX>& p,
+                                                  const LdsWeights& lw, int half) {
+  // the copies were issued first: with every activation and scale load
+  // still allowed in flight, they have landed
+  constexpr int kAfter = 8 * MF * XLoads<TX>::n + 1;
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (kAfter & 0xF) | ((kAfter >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t sx[kTiles], sy[kTiles], sz[kTiles], sw[kTiles];
+  rows_bcast(p.s.x, sx);
+  rows_bcast(p.s.y, sy);
+  rows_bcast(p.s.z, sz);
+  rows_bcast(p.s.w, sw);
+  const uint32_t sh = 8u * (uint32_t)half;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint4 wv[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) wv[t] = lw.tile[t][lw.ro[c]];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const uint32_t d0 = (c == 0 ? sx[t] : sz[t]) >> sh;
+      const uint32_t d1 = (c == 0 ? sy[t] : sw[t]) >> sh;
+      uint32_t wd[4];
+      transpose_q(wv[t], wd);
+      const float sc[4] = {e4m3<0>(d0), e4m3<2>(d0), e4m3<0>(d1), e4m3<2>(d1)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t A = decode_word_bf16(wd[i], sc[i]);
+#pragma unroll
+        for (int f = 0; f < MF; ++f)
+          acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              A, __builtin_bit_cast(bf16x8_t, p.x[f][4 * c + i][0]), acc[t][f], 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <typename TX, int MF, bool GLU>
 __device__ __forceinline__ void run_pairgroups_lds(f32x4_t (&acc)[kTiles][MF], const Sources<MF>& src,
                                                    const LdsWeights& lw, int wid, int nw, int64_t npg, int half) {
@@ -492,9 +565,15 @@ __device__ __forceinline__ void run_pairgroups_lds(f32x4_t (&acc)[kTiles][MF], c
   for (int64_t pg = wid; pg < npg; pg += nw) {
     // the previous pair-group's slice reads have all been consumed (their
     // multiplies waited for them), so the slice may be refilled
-    load_pg_lds<TX, MF, GLU>(p, src, lw, (uint32_t)pg);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_pg_lds<TX, MF>(acc, p, lw, half);
+    if constexpr (MF > 1) {
+      load_pg_lds_cm<TX, MF, GLU>(p, src, lw, (uint32_t)pg);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_pg_lds_cm<TX, MF>(acc, p, lw, half);
+    } else {
+      load_pg_lds<TX, MF, GLU>(p, src, lw, (uint32_t)pg);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_pg_lds<TX, MF>(acc, p, lw, half);
+    }
   }
 }
 
@@ -533,16 +612,17 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
                                                           const uint8_t* __restrict__ scu = nullptr,
                                                           const float* __restrict__ gsu = nullptr, int act = 0,
                                                           MatrixStrides bst = {}) {
-  // bf16 activations with one fragment (the plain form) stage the weights
-  // in per-wavefront LDS slices, one array per tile (kPart units per
-  // wavefront each), which later hold the wavefront's partial sums of that
-  // tile; the other forms keep the weights in registers and the partial
-  // sums in a buffer of their own.  Measured, same process (K = 4096, N =
-  // 14336, bit-identical): M = 3 / 6 / 16 took 9.7-9.9 / 9.9-10.2 / 11.5
-  // us against 10.2-10.4 / 10.6 / 12.6 us; with two to four fragments or in
-  // the gated form the staging measured up to 10% slower (M = 17, 33, 64;
-  // gated M = 3).
-  constexpr bool kLW = __is_same(TX, __bf16) && MF == 1 && !GLU;
+  // bf16 activations in the plain form with one, three or four fragments
+  // stage the weights in per-wavefront LDS slices, one array per tile
+  // (kPart units per wavefront each), which later hold the wavefront's
+  // partial sums of that tile; the other forms keep the weights in
+  // registers and the partial sums in a buffer of their own.  Measured,
+  // same process (K = 4096, N = 14336, bit-identical): M = 3 / 16 / 33 /
+  // 48 / 64 took 9.8-10.0 / 11.4-11.6 / 17.4 / 19.5 / 23.0 us against
+  // 10.2-10.4 / 12.6-12.7 / 18.4-18.5 / 21.3-21.4 / 25.3-25.4 us; with two
+  // fragments M = 17 took 14.1 against 13.3 us (M = 24: 15.4 against 15.9
+  // us), and the gated form at M = 3 22.9 against 21.0 us.
+  constexpr bool kLW = __is_same(TX, __bf16) && !GLU && MF != 2;
   constexpr int kPart = kTileUnits > MF * 64 ? kTileUnits : MF * 64;
   constexpr int kLwWaves = kLW ? MAXW : 1;
   __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles * MF][kLW ? 1 : 64];
