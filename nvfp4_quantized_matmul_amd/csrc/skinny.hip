@@ -601,7 +601,13 @@ __device__ __forceinline__ void store4(TO* out, int64_t orow, int64_t n, int64_t
 // up rows (wu, scu, gsu), and out = act(g * gate) * (g_u * up).
 // BAT: batched weights, blockIdx.y selects the matrix (strides bst); a
 // separate instantiation so the single-matrix kernel reads no strides.
-template <typename TX, int MF, int MAXW, bool GLU = false, bool HALF = false, bool BAT = false>
+//
+// LWS: the launcher allows the LDS weight slices (used for bf16 in the
+// plain form with one, three or four fragments, see kLW below); it does so
+// only when the block has all MAXW wavefronts, since the slices are sized
+// for MAXW and a smaller block would hold LDS that bounds the blocks per
+// compute unit for nothing.
+template <typename TX, int MF, int MAXW, bool GLU = false, bool HALF = false, bool BAT = false, bool LWS = false>
 __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict__ x,
                                                           const uint32_t* __restrict__ w,
                                                           const uint8_t* __restrict__ sc,
@@ -622,7 +628,7 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   // 10.2-10.4 / 12.6-12.7 / 18.4-18.5 / 21.3-21.4 / 25.3-25.4 us; with two
   // fragments M = 17 took 14.1 against 13.3 us (M = 24: 15.4 against 15.9
   // us), and the gated form at M = 3 22.9 against 21.0 us.
-  constexpr bool kLW = __is_same(TX, __bf16) && !GLU && MF != 2;
+  constexpr bool kLW = LWS && __is_same(TX, __bf16) && !GLU && MF != 2;
   constexpr int kPart = kTileUnits > MF * 64 ? kTileUnits : MF * 64;
   constexpr int kLwWaves = kLW ? MAXW : 1;
   __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles * MF][kLW ? 1 : 64];
@@ -728,12 +734,23 @@ void launch_mf(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, 
   const int64_t blocks = (N + kRows - 1) / kRows;
   const int64_t units = (HALF ? 2 : 1) * (K / kPG);
   const int waves = (int)(units < MAXW ? units : MAXW);
-  if (B > 1)
-    skinny_kernel<TX, MF, MAXW, false, HALF, true><<<dim3((unsigned)blocks, (unsigned)B), dim3(64 * waves), 0, s>>>(
-        x, w, sc, gs, out, M, K, N, nullptr, nullptr, nullptr, 0, bst);
-  else
-    skinny_kernel<TX, MF, MAXW, false, HALF><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out,
-                                                                                                 M, K, N);
+  // the LDS weight slices need a full block (bf16 only; one, three or four fragments)
+  constexpr bool kSlices = __is_same(TX, __bf16) && MF != 2;
+  const dim3 grid((unsigned)blocks, (unsigned)B);
+  if (kSlices && waves == MAXW) {
+    if (B > 1)
+      skinny_kernel<TX, MF, MAXW, false, HALF, true, kSlices><<<grid, dim3(64 * waves), 0, s>>>(
+          x, w, sc, gs, out, M, K, N, nullptr, nullptr, nullptr, 0, bst);
+    else
+      skinny_kernel<TX, MF, MAXW, false, HALF, false, kSlices><<<grid, dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M,
+                                                                                                K, N);
+  } else {
+    if (B > 1)
+      skinny_kernel<TX, MF, MAXW, false, HALF, true><<<grid, dim3(64 * waves), 0, s>>>(
+          x, w, sc, gs, out, M, K, N, nullptr, nullptr, nullptr, 0, bst);
+    else
+      skinny_kernel<TX, MF, MAXW, false, HALF><<<grid, dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, N);
+  }
 }
 
 template <typename TX, int MF, int MAXW>
@@ -773,7 +790,9 @@ void launch_rows16(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t*
 // against 112 us on the MoE prefill shape).
 template <typename TX> constexpr int gather_waves_per_eu() { return 4; }
 
-template <typename TX, int MAXW>
+// LWS as for the multi-row kernel: the LDS weight slices (2-byte
+// activations) only for blocks with all MAXW wavefronts.
+template <typename TX, int MAXW, bool LWS = false>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(gather_waves_per_eu<TX>())))
 void gather_mfma_kernel(
     const TX* __restrict__ x, int X, int Mg, int64_t K, const int32_t* __restrict__ lhs,
@@ -786,7 +805,7 @@ void gather_mfma_kernel(
   // passes are separated by barriers).  With the two index lists that is 40
   // KiB, four blocks per compute unit as before (f16 fits in 128 registers
   // with it).  float32 keeps the weights in registers.
-  constexpr bool kLW = sizeof(TX) == 2;
+  constexpr bool kLW = LWS && sizeof(TX) == 2;
   __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles][kLW ? 1 : 64];
   __shared__ uint4 wt0[(kLW ? MAXW : 1) * kTileUnits], wt1[(kLW ? MAXW : 1) * kTileUnits],
       wt2[(kLW ? MAXW : 1) * kTileUnits], wt3[(kLW ? MAXW : 1) * kTileUnits];
@@ -1015,14 +1034,24 @@ bool launch_gather_mfma(const void* x, nvfp4_dtype_t dt, int64_t X, int64_t M, i
   const dim3 grid((unsigned)((N + kRows - 1) / kRows), (unsigned)(E + 1));
   switch (dt) {
     case NVFP4_BF16:
-      gather_mfma_kernel<__bf16, 4><<<grid, dim3(64 * waves), 0, s>>>(
-          static_cast<const __bf16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
-          static_cast<__bf16*>(out));
+      if (waves == 4)
+        gather_mfma_kernel<__bf16, 4, true><<<grid, dim3(64 * waves), 0, s>>>(
+            static_cast<const __bf16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
+            static_cast<__bf16*>(out));
+      else
+        gather_mfma_kernel<__bf16, 4><<<grid, dim3(64 * waves), 0, s>>>(
+            static_cast<const __bf16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
+            static_cast<__bf16*>(out));
       break;
     case NVFP4_F16:
-      gather_mfma_kernel<_Float16, 4><<<grid, dim3(64 * waves), 0, s>>>(
-          static_cast<const _Float16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
-          static_cast<_Float16*>(out));
+      if (waves == 4)
+        gather_mfma_kernel<_Float16, 4, true><<<grid, dim3(64 * waves), 0, s>>>(
+            static_cast<const _Float16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
+            static_cast<_Float16*>(out));
+      else
+        gather_mfma_kernel<_Float16, 4><<<grid, dim3(64 * waves), 0, s>>>(
+            static_cast<const _Float16*>(x), (int)X, (int)M, K, lhs, rhs, (int)R, w, sc, gs, (int)E, N,
+            static_cast<_Float16*>(out));
       break;
     case NVFP4_F32:
       gather_mfma_kernel<float, 4><<<grid, dim3(64 * waves), 0, s>>>(
