@@ -42,9 +42,10 @@
 //    lane l taking row l (the gated form: one load per plane, each for its
 //    32 lanes), and lane swaps give each tile's 16 rows to its four q lanes;
 //    word 4i+q uses byte 2i + q/2 of its chunk's eight;
-//  * with bf16 activations and one, three or four 16-row fragments in the
-//    multi-row kernel, and with bf16 or f16 in every pass of the gather,
-//    the weights go through a private LDS slice per wavefront instead,
+//  * with bf16 activations and one, three or four 16-row fragments or
+//    float32 activations in the multi-row kernel, and with bf16 or f16 in
+//    every pass of the gather, the weights go through a private LDS slice
+//    per wavefront instead,
 //    copied by load-to-LDS instructions that read 8 whole rows of 128 bytes
 //    each, and are read back in the layout above (described before
 //    set_lds_rows);
@@ -577,6 +578,56 @@ __device__ __forceinline__ void run_pairgroups_lds(f32x4_t (&acc)[kTiles][MF], c
   }
 }
 
+// float32 activations with the weights in the LDS slices: a wavefront takes
+// both halves of each of its pair-groups, wid, wid + nw, ...  The pair-group's
+// eight weight copies, chunk 0's activations and the scales are issued
+// together; chunk 1's activations are loaded after chunk 0 is multiplied,
+// so a wavefront holds one chunk's activations at a time, as with half
+// units, while the weights and scales are read once per pair-group.
+template <int MF>
+__device__ __forceinline__ void run_halves_lds(f32x4_t (&acc)[kTiles][MF], const Sources<MF>& src,
+                                               const LdsWeights& lw, int wid, int nw, int64_t npg, int half) {
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][f][i] = 0.0f;
+  HalfUnit<MF, float> p;
+  const rsrc_t wr = src.w;
+  for (int64_t pg = wid; pg < npg; pg += nw) {
+    const uint32_t g = (uint32_t)pg;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, NVFP4_LDS(lw.tile[t] + 64 * h), 16, lw.go[t][h], g * 128u, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int f = 0; f < MF; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            p.x[f][i][h] = load16(src.x, src.xo[f], (g * 256u + c * 128u + i * 32u) * 4u + h * 16u);
+      if (c == 0) p.s = load16(src.s, src.so, g * 16u);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c == 0) {
+        // the copies were issued first: with this chunk's activation and
+        // scale loads still allowed in flight, they have landed
+        constexpr int kAfter = 8 * MF + 1;
+        __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | (kAfter & 0xF) | ((kAfter >> 4) << 14));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) p.w[t] = lw.tile[t][lw.ro[c]];
+      compute_half<float, MF>(acc, p, (uint32_t)c, half);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // C[n][m] of tile t: element i of lane l is weight row 16t + 4(l/16) + i,
 // activation row l % 16 of the fragment; four bf16 to out row `orow`.
 template <typename TO>
@@ -627,8 +678,11 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   // 48 / 64 took 9.8-10.0 / 11.4-11.6 / 17.4 / 19.5 / 23.0 us against
   // 10.2-10.4 / 12.6-12.7 / 18.4-18.5 / 21.3-21.4 / 25.3-25.4 us; with two
   // fragments M = 17 took 14.1 against 13.3 us (M = 24: 15.4 against 15.9
-  // us), and the gated form at M = 3 22.9 against 21.0 us.
-  constexpr bool kLW = LWS && __is_same(TX, __bf16) && !GLU && MF != 2;
+  // us), and the gated form at M = 3 22.9 against 21.0 us.  float32 (half
+  // units) takes the slices too, a whole pair-group per wavefront
+  // (run_halves_lds): M = 6 / 16 / 33 / 48 took 16.3 / 17.7 / 35.8 / 38.5
+  // us against 16.7 / 19.0 / 37.6 / 40.2 us (M = 3 and 24 unchanged).
+  constexpr bool kLW = LWS && !GLU && ((__is_same(TX, __bf16) && MF != 2) || HALF);   // HALF: float32
   constexpr int kPart = kTileUnits > MF * 64 ? kTileUnits : MF * 64;
   constexpr int kLwWaves = kLW ? MAXW : 1;
   __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles * MF][kLW ? 1 : 64];
@@ -670,7 +724,12 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
   for (int f = 0; f < MF; ++f) src.xo[f] = (uint32_t)(((16 * f + r16) * K + 8 * q) * (int64_t)sizeof(TX));
 
   f32x4_t acc[kTiles][MF];
-  if constexpr (HALF) {
+  if constexpr (HALF && kLW) {
+    static_assert(__is_same(TX, float) && !GLU, "half units serve float32 activations");
+    LdsWeights lw;
+    set_lds_rows<false>(lw, wt0 + wid * kPart, wt1 + wid * kPart, wt2 + wid * kPart, wt3 + wid * kPart, n0, lane, K);
+    run_halves_lds<MF>(acc, src, lw, wid, nw, K / kPG, q >> 1);
+  } else if constexpr (HALF) {
     static_assert(__is_same(TX, float) && !GLU, "half units serve float32 activations");
     run_halves<MF>(acc, src, wid, nw, K / kPG, q >> 1);
   } else if constexpr (kLW) {
@@ -733,11 +792,15 @@ void launch_mf(const TX* x, int64_t M, int64_t K, int64_t N, const uint32_t* w, 
                const float* gs, TX* out, hipStream_t s, int64_t B, const MatrixStrides& bst) {
   const int64_t blocks = (N + kRows - 1) / kRows;
   const int64_t units = (HALF ? 2 : 1) * (K / kPG);
-  const int waves = (int)(units < MAXW ? units : MAXW);
-  // the LDS weight slices need a full block (bf16 only; one, three or four fragments)
-  constexpr bool kSlices = __is_same(TX, __bf16) && MF != 2;
+  int waves = (int)(units < MAXW ? units : MAXW);
+  // the LDS weight slices need a full block (bf16 with one, three or four
+  // fragments; float32 with its half units, one whole pair-group per
+  // wavefront: a full block needs K / 256 >= MAXW)
+  constexpr bool kSlices = (__is_same(TX, __bf16) && MF != 2) || HALF;
+  const bool full = HALF ? K / kPG >= MAXW : waves == MAXW;
+  if (HALF && full) waves = MAXW;
   const dim3 grid((unsigned)blocks, (unsigned)B);
-  if (kSlices && waves == MAXW) {
+  if (kSlices && full) {
     if (B > 1)
       skinny_kernel<TX, MF, MAXW, false, HALF, true, kSlices><<<grid, dim3(64 * waves), 0, s>>>(
           x, w, sc, gs, out, M, K, N, nullptr, nullptr, nullptr, 0, bst);
@@ -804,7 +867,9 @@ void gather_mfma_kernel(
   // counts live in wt0 while no weights are in flight (the scan and the
   // passes are separated by barriers).  With the two index lists that is 40
   // KiB, four blocks per compute unit as before (f16 fits in 128 registers
-  // with it).  float32 keeps the weights in registers.
+  // with it).  float32 keeps the weights in registers: its form with the
+  // slices (a whole pair-group per wavefront) would spill at the
+  // four-waves-per-SIMD limit.
   constexpr bool kLW = LWS && sizeof(TX) == 2;
   __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles][kLW ? 1 : 64];
   __shared__ uint4 wt0[(kLW ? MAXW : 1) * kTileUnits], wt1[(kLW ? MAXW : 1) * kTileUnits],
