@@ -669,20 +669,24 @@ __global__ __launch_bounds__(64 * MAXW) void skinny_kernel(const TX* __restrict_
                                                           const uint8_t* __restrict__ scu = nullptr,
                                                           const float* __restrict__ gsu = nullptr, int act = 0,
                                                           MatrixStrides bst = {}) {
-  // bf16 activations in the plain form with one, three or four fragments
-  // stage the weights in per-wavefront LDS slices, one array per tile
+  // The weights go through per-wavefront LDS slices, one array per tile
   // (kPart units per wavefront each), which later hold the wavefront's
-  // partial sums of that tile; the other forms keep the weights in
-  // registers and the partial sums in a buffer of their own.  Measured,
-  // same process (K = 4096, N = 14336, bit-identical): M = 3 / 16 / 33 /
-  // 48 / 64 took 9.8-10.0 / 11.4-11.6 / 17.4 / 19.5 / 23.0 us against
-  // 10.2-10.4 / 12.6-12.7 / 18.4-18.5 / 21.3-21.4 / 25.3-25.4 us; with two
-  // fragments M = 17 took 14.1 against 13.3 us (M = 24: 15.4 against 15.9
-  // us), and the gated form at M = 3 22.9 against 21.0 us.  float32 (half
-  // units) takes the slices too, a whole pair-group per wavefront
-  // (run_halves_lds): M = 6 / 16 / 33 / 48 took 16.3 / 17.7 / 35.8 / 38.5
-  // us against 16.7 / 19.0 / 37.6 / 40.2 us (M = 3 and 24 unchanged).
-  constexpr bool kLW = LWS && !GLU && ((__is_same(TX, __bf16) && MF != 2) || HALF);   // HALF: float32
+  // partial sums of that tile, for bf16 in the plain form with one, three or
+  // four fragments and in the gated form with one, and for float32 (half
+  // units become a whole pair-group per wavefront, run_halves_lds); the
+  // other forms keep the weights in registers and the partial sums in a
+  // buffer of their own.  Measured, same process (K = 4096, N = 14336):
+  //  * plain bf16, bit-identical: M = 3 / 16 / 33 / 48 / 64 took 9.8-10.0 /
+  //    11.4-11.6 / 17.4 / 19.5 / 23.0 us against 10.2-10.4 / 12.6-12.7 /
+  //    18.4-18.5 / 21.3-21.4 / 25.3-25.4 us; with two fragments M = 17 took
+  //    14.1 against 13.3 us (M = 24: 15.4 against 15.9 us), so two keep
+  //    registers;
+  //  * gated bf16, bit-identical: M = 3 / 8 / 16 took 20.4-20.5 / 22.1 /
+  //    23.8-23.9 us against 21.2-21.4 / 22.7-22.9 / 25.4 us;
+  //  * float32: M = 6 / 16 / 33 / 48 took 16.3 / 17.7 / 35.8 / 38.5 us
+  //    against 16.7 / 19.0 / 37.6 / 40.2 us (M = 3 and 24 unchanged).
+  constexpr bool kLW = LWS && ((!GLU && ((__is_same(TX, __bf16) && MF != 2) || HALF)) ||   // HALF: float32
+                                (GLU && __is_same(TX, __bf16) && MF == 1));
   constexpr int kPart = kTileUnits > MF * 64 ? kTileUnits : MF * 64;
   constexpr int kLwWaves = kLW ? MAXW : 1;
   __shared__ f32x4_t red_s[kLW ? 1 : MAXW][kLW ? 1 : kTiles * MF][kLW ? 1 : 64];
@@ -823,8 +827,14 @@ void launch_mf_glu(const TX* x, int64_t M, int64_t K, int64_t F, const uint32_t*
   const int64_t blocks = (F + kRows / 2 - 1) / (kRows / 2);
   const int64_t npg = K / kPG;
   const int waves = (int)(npg < MAXW ? npg : MAXW);
-  skinny_kernel<TX, MF, MAXW, true><<<dim3((unsigned)blocks), dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, F,
-                                                                                         wu, scu, gsu, act);
+  // the LDS weight slices: bf16 with one fragment, full blocks
+  constexpr bool kSlices = __is_same(TX, __bf16) && MF == 1;
+  const dim3 grid((unsigned)blocks);
+  if (kSlices && waves == MAXW)
+    skinny_kernel<TX, MF, MAXW, true, false, false, kSlices><<<grid, dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M,
+                                                                                                K, F, wu, scu, gsu, act);
+  else
+    skinny_kernel<TX, MF, MAXW, true><<<grid, dim3(64 * waves), 0, s>>>(x, w, sc, gs, out, M, K, F, wu, scu, gsu, act);
 }
 
 // 16-bit activations: up to four 16-row fragments in one launch.
