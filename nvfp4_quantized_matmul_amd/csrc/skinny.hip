@@ -653,9 +653,9 @@ __device__ __forceinline__ void store4(TO* out, int64_t orow, int64_t n, int64_t
 // BAT: batched weights, blockIdx.y selects the matrix (strides bst); a
 // separate instantiation so the single-matrix kernel reads no strides.
 //
-// LWS: the launcher allows the LDS weight slices (used for bf16 in the
-// plain form with one, three or four fragments, see kLW below); it does so
-// only when the block has all MAXW wavefronts, since the slices are sized
+// LWS: the launcher allows the LDS weight slices (the forms that use them
+// are listed at kLW below); it does so only when the block has all MAXW
+// wavefronts, since the slices are sized
 // for MAXW and a smaller block would hold LDS that bounds the blocks per
 // compute unit for nothing.
 template <typename TX, int MF, int MAXW, bool GLU = false, bool HALF = false, bool BAT = false, bool LWS = false>
