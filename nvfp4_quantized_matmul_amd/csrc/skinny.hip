@@ -354,7 +354,8 @@ __device__ __forceinline__ void run_pairgroups(f32x4_t (&acc)[kTiles][MF], const
 }
 
 // ---------------------------------------------------------------------------
-// Weights through LDS (2-byte activations).  In registers, a weight load
+// Weights through LDS (the forms listed at skinny_kernel's kLW and the
+// 2-byte gather).  In registers, a weight load
 // takes 64 bytes of each of 16 rows (the MFMA operand layout allows no more
 // per row), so every load touches 16 cache lines for half of each.  Here
 // each wavefront copies its pair-group's 64 rows x 128 bytes into its own
@@ -517,6 +518,7 @@ __device__ __forceinline__ void load_pg_lds_cm(PairGroup<MF, TX>& p, const Sourc
 template <typename TX, int MF>
 __device__ __forceinline__ void compute_pg_lds_cm(f32x4_t (&acc)[kTiles][MF], const PairGroup<MF, TX>& p,
                                                   const LdsWeights& lw, int half) {
+  static_assert(__is_same(TX, __bf16), "the chunk-major form serves bf16 activations");
   // the copies were issued first: with every activation and scale load
   // still allowed in flight, they have landed
   constexpr int kAfter = 8 * MF * XLoads<TX>::n + 1;
