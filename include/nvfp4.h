@@ -348,6 +348,24 @@ int nvfp4_qmm_batched(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B,
                       nvfp4_route_t route, void* out, hipStream_t stream);
 
 /*
+ * nvfp4_qmm_batched_ws -- nvfp4_qmm_batched with a caller-owned workspace
+ * (device, 16-byte aligned, not overlapping x or out), which every matrix on
+ * the GEMM route uses in turn as nvfp4_qmm_ws does (the launches are ordered
+ * on the stream, so one workspace serves the batch).  It needs at least
+ * nvfp4_qmm_workspace_size(M, K, N, transpose, dtype, route) bytes, the size
+ * for one matrix; with less (or NULL, 0) it is nvfp4_qmm_batched.  So float32
+ * activations and non-transposed planes at GEMM sizes run on the matrix
+ * cores here too.  Errors as for nvfp4_qmm_batched, plus NVFP4_ERR_SHAPE for
+ * a negative size, a NULL workspace with a positive size or an overlap, and
+ * NVFP4_ERR_ALIGN for a misaligned workspace; nothing is launched then.
+ */
+int nvfp4_qmm_batched_ws(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B,
+                         int64_t M, int64_t K, int64_t N, const uint32_t* w,
+                         const uint8_t* scales, const float* gs, int transpose,
+                         nvfp4_route_t route, void* workspace,
+                         int64_t workspace_bytes, void* out, hipStream_t stream);
+
+/*
  * nvfp4_gather_qmm -- GatherQMM over NVFP4 experts (mlxcel PR "native NVFP4
  * for ROCm QuantizedMatmul/GatherQMM", "Summary": the per-expert global
  * scale, a weight group reloaded only when the expert changes; "Changes

@@ -71,6 +71,7 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_quantize": [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp],
         "nvfp4_qmm": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_qmm_batched": [vp, c_int, i64, i64, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
+        "nvfp4_qmm_batched_ws": [vp, c_int, i64, i64, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, i64, vp, vp],
         "nvfp4_qmm_ws": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, i64, vp, vp],
         "nvfp4_qmm_noalloc": [vp, c_int, i64, i64, i64, vp, vp, vp, c_int, c_int, vp, vp],
         "nvfp4_static_scratch_bytes": [],
@@ -394,7 +395,9 @@ def qmm_batched(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
 
     x [XB, M, K] with XB = 1 (shared by every matrix) or XB = B; w [B, N, K/8]
     (transpose) or [B, K, N/8]; scales as for check_planes; gs float32 [B] or
-    None.  Returns [B, M, N] in x's dtype.
+    None.  Returns [B, M, N] in x's dtype.  Where the GEMM route wants a
+    workspace (as for qmm), one from torch's allocator serves every matrix
+    through nvfp4_qmm_batched_ws.
     """
     check_planes(w, scales)
     if w.dim() != 3 or x.dim() != 3:
@@ -421,8 +424,16 @@ def qmm_batched(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
     elif out.dtype != x.dtype or tuple(out.shape) != (B, M, N):
         raise ValueError("out has the wrong dtype or shape")
     _require_gpu(out)
+    tr = int(bool(transpose))
+    ws_bytes = _qmm_workspace_bytes(lib, dev, M, K, N, tr, code, _ROUTES[route]) if B > 0 else 0
+    if ws_bytes > 0:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        _check("nvfp4_qmm_batched_ws", lib.nvfp4_qmm_batched_ws(
+            _ptr(x), code, XB, B, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), tr, _ROUTES[route],
+            _ptr(ws), ws_bytes, _ptr(out), _stream(dev)))
+        return out
     _check("nvfp4_qmm_batched", lib.nvfp4_qmm_batched(
-        _ptr(x), code, XB, B, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), int(bool(transpose)),
+        _ptr(x), code, XB, B, M, K, N, _ptr(w), _ptr(scales), _ptr(gs), tr,
         _ROUTES[route], _ptr(out), _stream(dev)))
     return out
 

@@ -108,6 +108,56 @@ bool glu_fused(int64_t M, int64_t K, int64_t F, nvfp4_dtype_t dtype) {
 
 bool valid_act(int act) { return act == NVFP4_ACT_GELU_TANH || act == NVFP4_ACT_GELU || act == NVFP4_ACT_SILU; }
 
+// nvfp4_qmm_batched and nvfp4_qmm_batched_ws: the workspace (work,
+// work_bytes, both checked by the caller) serves the GEMM route of every
+// matrix in turn; the launches are ordered on the stream, so one workspace
+// is enough.
+int qmm_batched_impl(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B, int64_t M, int64_t K, int64_t N,
+                     const uint32_t* w, const uint8_t* scales, const float* gs, int transpose,
+                     nvfp4_route_t route, void* work, int64_t work_bytes, void* out, hipStream_t stream) {
+  if (B < 0 || XB < 0 || M < 0 || K < 0 || N < 0) return NVFP4_ERR_SHAPE;
+  if (B == 0) return (XB == 0 || XB == 1) ? NVFP4_OK : NVFP4_ERR_SHAPE;
+  if (XB != 1 && XB != B) return NVFP4_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
+  if (transpose != 0 && transpose != 1) return NVFP4_ERR_SHAPE;
+  if (transpose ? (K % 16) != 0 : (N % 16) != 0) return NVFP4_ERR_SHAPE;
+  // Per-matrix strides (elements of x and out, words of w, bytes of scales);
+  // every total must fit in int64.
+  const int64_t ds = dtype_size(dtype);
+  int64_t xs, ws, ss, os, t;
+  if (!mul_ok(M, K, &xs) || !mul_ok(M, N, &os) || !mul_ok(N, K, &t)) return NVFP4_ERR_SHAPE;
+  ws = t / 8;
+  ss = t / 16;
+  if (!size3(XB, xs, ds, &t) || !size3(B, os, ds, &t) || !size3(B, ws, 4, &t) || !mul_ok(B, ss, &t))
+    return NVFP4_ERR_SHAPE;
+  if (XB == 1) xs = 0;
+  const char* xb = static_cast<const char*>(x);
+  char* ob = static_cast<char*>(out);
+  // Every slice is checked before anything is enqueued.
+  QmmPlan plan{};
+  for (int64_t b = 0; b < B; ++b) {
+    const int st = qmm_plan(xb ? xb + b * xs * ds : nullptr, dtype, M, K, N, w ? w + b * ws : nullptr,
+                            scales ? scales + b * ss : nullptr, gs ? gs + b : nullptr, transpose, route,
+                            ob ? ob + b * os * ds : nullptr, &plan);
+    if (st != NVFP4_OK) return st;
+  }
+  if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
+  if (work && plan.kind == QmmPlan::kGemmMfma &&
+      (overlaps(work, work_bytes, out, B * os * ds) || overlaps(work, work_bytes, x, (XB == 1 ? 1 : B) * M * K * ds)))
+    return NVFP4_ERR_SHAPE;
+  // The decode and multi-row kernels take the whole batch in one launch
+  // (the same kernel and arithmetic as one call per matrix); other routes
+  // launch per matrix.
+  if (plan.kind == QmmPlan::kQmv && transpose &&
+      nvfp4host::launch_qmv_batched(x, dtype, B, xs, M, K, N, w, scales, gs, out, stream))
+    return launched();
+  for (int64_t b = 0; b < B; ++b)
+    qmm_launch(plan, xb ? xb + b * xs * ds : nullptr, dtype, M, K, N, w ? w + b * ws : nullptr,
+               scales ? scales + b * ss : nullptr, gs ? gs + b : nullptr, transpose, ob + b * os * ds,
+               stream, work, work_bytes);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -399,44 +449,17 @@ int nvfp4_qmm_glu(const void* x, nvfp4_dtype_t dtype, int64_t M, int64_t K, int6
 int nvfp4_qmm_batched(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B, int64_t M, int64_t K,
                       int64_t N, const uint32_t* w, const uint8_t* scales, const float* gs,
                       int transpose, nvfp4_route_t route, void* out, hipStream_t stream) {
-  if (B < 0 || XB < 0 || M < 0 || K < 0 || N < 0) return NVFP4_ERR_SHAPE;
-  if (B == 0) return (XB == 0 || XB == 1) ? NVFP4_OK : NVFP4_ERR_SHAPE;
-  if (XB != 1 && XB != B) return NVFP4_ERR_SHAPE;
-  if (!valid_dtype(dtype)) return NVFP4_ERR_DTYPE;
-  if (transpose != 0 && transpose != 1) return NVFP4_ERR_SHAPE;
-  if (transpose ? (K % 16) != 0 : (N % 16) != 0) return NVFP4_ERR_SHAPE;
-  // Per-matrix strides (elements of x and out, words of w, bytes of scales);
-  // every total must fit in int64.
-  const int64_t ds = dtype_size(dtype);
-  int64_t xs, ws, ss, os, t;
-  if (!mul_ok(M, K, &xs) || !mul_ok(M, N, &os) || !mul_ok(N, K, &t)) return NVFP4_ERR_SHAPE;
-  ws = t / 8;
-  ss = t / 16;
-  if (!size3(XB, xs, ds, &t) || !size3(B, os, ds, &t) || !size3(B, ws, 4, &t) || !mul_ok(B, ss, &t))
-    return NVFP4_ERR_SHAPE;
-  if (XB == 1) xs = 0;
-  const char* xb = static_cast<const char*>(x);
-  char* ob = static_cast<char*>(out);
-  // Every slice is checked before anything is enqueued.
-  QmmPlan plan{};
-  for (int64_t b = 0; b < B; ++b) {
-    const int st = qmm_plan(xb ? xb + b * xs * ds : nullptr, dtype, M, K, N, w ? w + b * ws : nullptr,
-                            scales ? scales + b * ss : nullptr, gs ? gs + b : nullptr, transpose, route,
-                            ob ? ob + b * os * ds : nullptr, &plan);
-    if (st != NVFP4_OK) return st;
-  }
-  if (plan.kind == QmmPlan::kNothing) return NVFP4_OK;
-  // The decode and multi-row kernels take the whole batch in one launch
-  // (the same kernel and arithmetic as one call per matrix); other routes
-  // launch per matrix.
-  if (plan.kind == QmmPlan::kQmv && transpose &&
-      nvfp4host::launch_qmv_batched(x, dtype, B, xs, M, K, N, w, scales, gs, out, stream))
-    return launched();
-  for (int64_t b = 0; b < B; ++b)
-    qmm_launch(plan, xb ? xb + b * xs * ds : nullptr, dtype, M, K, N, w ? w + b * ws : nullptr,
-               scales ? scales + b * ss : nullptr, gs ? gs + b : nullptr, transpose, ob + b * os * ds,
-               stream);
-  return launched();
+  return qmm_batched_impl(x, dtype, XB, B, M, K, N, w, scales, gs, transpose, route, nullptr, 0, out, stream);
+}
+
+int nvfp4_qmm_batched_ws(const void* x, nvfp4_dtype_t dtype, int64_t XB, int64_t B, int64_t M, int64_t K,
+                         int64_t N, const uint32_t* w, const uint8_t* scales, const float* gs, int transpose,
+                         nvfp4_route_t route, void* workspace, int64_t workspace_bytes, void* out,
+                         hipStream_t stream) {
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return NVFP4_ERR_SHAPE;
+  if (workspace && !aligned(workspace, 16)) return NVFP4_ERR_ALIGN;
+  return qmm_batched_impl(x, dtype, XB, B, M, K, N, w, scales, gs, transpose, route, workspace, workspace_bytes,
+                          out, stream);
 }
 
 int nvfp4_gather_qmm(const void* x, nvfp4_dtype_t dtype, int64_t X, int64_t M, int64_t K,

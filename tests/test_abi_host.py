@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("nvfp4_transcode", "nvfp4_dequantize", "nvfp4_quantize", "nvfp4_qmm", "nvfp4_qmm_ws",
                  "nvfp4_qmm_noalloc", "nvfp4_static_scratch_bytes",
-                 "nvfp4_qmm_workspace_size", "nvfp4_qmm_batched", "nvfp4_gather_qmm",
+                 "nvfp4_qmm_workspace_size", "nvfp4_qmm_batched", "nvfp4_qmm_batched_ws", "nvfp4_gather_qmm",
                  "nvfp4_qmm_glu", "nvfp4_qmm_glu_workspace_size",
                  "nvfp4_select_route", "nvfp4_status_string", "nvfp4_version", "nvfp4_qmv_max_rows"):
         assert want in names
@@ -313,6 +313,21 @@ def test_qmm_batched_validation(lib):
     assert qmm_b(lib, B=0, XB=1, x=None, w=None, s=None, out=None) == OK
     assert qmm_b(lib, B=0, XB=0, x=None, w=None, s=None, out=None) == OK
     assert qmm_b(lib, M=0, x=None, w=None, s=None, out=None) == OK
+
+
+def test_qmm_batched_ws_validation(lib):
+    """The workspace form checks its workspace like nvfp4_qmm_ws and the
+    batch like nvfp4_qmm_batched, all before any launch (M = 300: the GEMM
+    route, where the workspace is used)."""
+    f = lib.nvfp4_qmm_batched_ws
+    args = lambda **k: (k.get("x", FAKE), BF16, 3, 3, 300, 64, 32, FAKE, FAKE, None, 1, 0,
+                        k.get("ws", P(0x40000000)), k.get("nb", 1024), k.get("out", FAKE), None)
+    assert f(*args(nb=-1)) == SHAPE
+    assert f(*args(ws=None, nb=16)) == SHAPE
+    assert f(*args(ws=MISALIGNED)) == ALIGN
+    assert f(*args(x=None)) == NULLPTR
+    assert f(*args(ws=P(0x100000 + 3 * 300 * 32 * 2 - 512))) == SHAPE   # overlaps the last output matrix
+    assert f(*args(ws=P(0x100000 + 300 * 64 * 2 - 512), out=P(0x20000000))) == SHAPE   # overlaps x
 
 
 def gather(lib, x=FAKE, dt=BF16, X=2, M=1, K=64, lhs=None, rhs=FAKE, R=4, w=FAKE, s=FAKE,
