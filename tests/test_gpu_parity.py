@@ -1285,6 +1285,35 @@ def test_qmm_random_sweep(i, M, K, N, dtype, route, with_gs):
     assert rel(out, ref) <= TOL[dtype], (M, K, N, dtype, route)
 
 
+def _slice_sweep_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        K = 256 * int(g.integers(16, 33))          # at least 16 pair-groups: full blocks for every width
+        M = int(g.integers(2, 65))
+        N = int(g.integers(1, 1200))
+        dtype = [torch.bfloat16, torch.float32][int(g.integers(0, 2))]
+        gated = dtype == torch.bfloat16 and M <= 16 and bool(g.integers(0, 2))
+        cases.append((i, M, K, N, dtype, gated))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,K,N,dtype,gated", _slice_sweep_cases(20, 2026))
+def test_multirow_lds_slices_random_sweep(i, M, K, N, dtype, gated):
+    """The multi-row kernel's forms whose weights go through per-wavefront
+    LDS slices (bf16 with one, three or four fragments, the gated bf16 form
+    with one, float32 with whole pair-groups per wavefront; bf16 with two
+    fragments keeps registers), at random K >= 4096 (several pair-groups per
+    wavefront for K > 4096), random M and ragged N, against the oracle."""
+    if gated:
+        g, u = glu_planes(7700 + i, M, K, N)
+        out, ref = run_glu(g, u, dtype, "silu")
+    else:
+        case = synth.dense_case(7800 + i, M, K, N, with_gs=bool(i % 2))
+        out, ref = run_qmm(case, dtype, "qmv", guard=True)
+    assert rel(out, ref) <= TOL[dtype], (M, K, N, dtype, gated)
+
+
 def _nt_sweep_cases(n, seed):
     g = np.random.default_rng(seed)
     cases = []
