@@ -903,7 +903,7 @@ def main():
                     "unit": "TFLOP/s", "flops": pre.flops,
                     "roofline": {"bound": "mfma", "achieved": round(ptf, 2), "peak": BF16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(ptf / BF16_PEAK_TFLOPS, 4),
-                                 "kernel": "gemm_mfma_v3_kernel", "kernel_duration": pdur},
+                                 "kernel": "gemm_mfma_v3p_kernel (persistent)", "kernel_duration": pdur},
                     "cpu_baseline": cpu_pre,
                     "activations_f16": dt_rates["f16"],
                     "activations_f32": dt_rates["f32"],

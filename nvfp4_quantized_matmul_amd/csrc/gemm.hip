@@ -678,6 +678,176 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// Persistent form of the plain tile (2-byte activations, K a multiple of 384
+// with at least 12 slabs).  The plain launch starts every tile of a round on
+// every compute unit at once, and the first slabs' loads then queue behind
+// each other before any multiply can start.  Here one block per compute unit
+// walks its tiles, and the last three steps of a tile queue the next tile's
+// first two activation slabs and three weight slabs into exactly the stages
+// its first steps read (slab counts are multiples of the stage rings), so
+// the next tile's start-up overlaps this tile's last multiplies and its
+// epilogue.  Each XCD owns a contiguous run of tiles (activation tiles
+// fastest), its blocks taking them round-robin, as in the plain launch.
+// ----------------------------------------------------------------------------
+
+// 32-bit offsets of a plain tile's slab-0 loads from the operand bases
+// (activation elements, plane words, scale bytes; as in gemm_mfma_v3_kernel),
+// so each load is a scalar base plus one offset register.
+struct V3Off {
+  uint32_t x[8];
+  uint32_t w[2];
+  uint32_t s;
+};
+
+__device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int64_t N, int64_t m_blk,
+                                            int64_t n_blk, int wave, int lane) {
+  const int64_t kw = K / 8, ks = K / 16;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = (i * 4 + wave) * 64 + lane;
+    const int r = slot >> 3, c = (slot & 7) ^ swz(r);
+    int64_t m = m_blk + r;
+    if (m >= M) m = M - 1;
+    o.x[i] = (uint32_t)(m * K + c * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = (i * 4 + wave) * 64 + lane;
+    const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);
+    int64_t n = n_blk + r;
+    if (n >= N) n = N - 1;
+    o.w[i] = (uint32_t)(n * kw + 4 * half);
+  }
+  int64_t n = n_blk + wave * 64 + lane;
+  if (n >= N) n = N - 1;
+  o.s = (uint32_t)(n * ks);
+}
+
+struct V3Base {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint8_t* s;
+};
+
+__device__ __forceinline__ void v3p_issue_x(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
+                                            int wave) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds(b.x + (o.x[i] + slab * kV3BK), NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, 0, 0);
+}
+__device__ __forceinline__ void v3p_issue_w(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
+                                            int wave) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds(b.w + (o.w[i] + slab * 8), NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(b.s + (o.s + slab * 4), NVFP4_LDS(&st.s[wave * 64]), 4, 0, 0);
+}
+
+// One tile's slabs (nslabs % 6 == 0, nslabs >= 12).  `issued`: the first
+// slabs were queued by the previous tile.  With has_next, the last three
+// steps queue the next tile's slabs 0-1 (activations) and 0-2 (weights) from
+// the offsets `no`, and the loads stay in flight when this returns;
+// otherwise they queue this tile's last slab again and the load counter is
+// drained.
+template <typename TA>
+__device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stage (&X)[3], const V3Stage (&W)[6],
+                                             const V3Base& b, const V3Off& o, const V3Off& no, bool has_next,
+                                             bool issued, uint32_t nslabs, int wave, int l32, int h) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.0f;
+  if (!issued) {
+    v3p_issue_w(W[0], b, o, 0, wave);
+    v3p_issue_x(X[0], b, o, 0, wave);
+    v3p_issue_w(W[1], b, o, 1, wave);
+    v3p_issue_x(X[1], b, o, 1, wave);
+    v3p_issue_w(W[2], b, o, 2, wave);
+  }
+#define NVFP4_V3P_STEP(XI, WI, XO, XSLAB, WO, WSLAB)                                 \
+  do {                                                                               \
+    wait_vmem(true);                                                                 \
+    __builtin_amdgcn_s_barrier();                                                    \
+    v3p_issue_x(X[((XI) + 2) % 3], b, XO, XSLAB, wave);                              \
+    v3p_issue_w(W[((WI) + 3) % 6], b, WO, WSLAB, wave);                              \
+    const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
+    v3_compute<TA>(acc, cur, wave, l32, h);                                          \
+  } while (0)
+  uint32_t s = 0;
+  for (; s + 6 < nslabs; s += 6) {
+    NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3);
+    NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4);
+    NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5);
+    NVFP4_V3P_STEP(0, 3, o, s + 5, o, s + 6);
+    NVFP4_V3P_STEP(1, 4, o, s + 6, o, s + 7);
+    NVFP4_V3P_STEP(2, 5, o, s + 7, o, s + 8);
+  }
+  NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3);
+  NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4);
+  NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5);
+  // without a next tile, `no` holds this tile's offsets and the tail
+  // queues its last slab again
+  const uint32_t last = nslabs - 1;
+  const uint32_t q0 = has_next ? 0u : last, q1 = has_next ? 1u : last, q2 = has_next ? 2u : last;
+  NVFP4_V3P_STEP(0, 3, o, last, no, q0);
+  NVFP4_V3P_STEP(1, 4, no, q0, no, q1);
+  NVFP4_V3P_STEP(2, 5, no, q1, no, q2);
+  if (!has_next) wait_vmem(false);   // no load-to-LDS may land after the last tile
+#undef NVFP4_V3P_STEP
+}
+
+template <typename TA>
+__global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
+    const TA* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
+    const float* __restrict__ gs, TA* __restrict__ out, int64_t M, int64_t K, int64_t N, int64_t tiles_m,
+    int64_t tiles_total, int64_t per_xcd) {
+  __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
+  __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2], w3[kV3BN * 2], w4[kV3BN * 2], w5[kV3BN * 2];
+  __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN], s3[kV3BN], s4[kV3BN], s5[kV3BN];
+  const V3Stage st0{x0, w0, s0}, st1{x1, w1, s1}, st2{x2, w2, s2};
+  const V3Stage XS[3] = {st0, st1, st2};
+  const V3Stage WS[6] = {st0, st1, st2, {x0, w3, s3}, {x0, w4, s4}, {x0, w5, s5}};
+
+  // XCD x (blocks b with b % 8 == x) owns logical tiles [x per_xcd, (x + 1)
+  // per_xcd); its bpx blocks take them round-robin.
+  const int64_t bpx = (int64_t)gridDim.x / 8;
+  const int64_t t_begin = ((int64_t)blockIdx.x % 8) * per_xcd;
+  const int64_t t_end = t_begin + per_xcd < tiles_total ? t_begin + per_xcd : tiles_total;
+  int64_t tile = t_begin + (int64_t)blockIdx.x / 8;
+  if (tile >= t_end) return;   // whole block, before any barrier
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t nslabs = (uint32_t)(K / kV3BK);
+  const float g = global_factor(gs, 0);
+  const V3Base base{reinterpret_cast<const uint16_t*>(x), w, sc};
+  V3Off o, no;
+  v3p_offsets(o, M, K, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kV3BN, wave, lane);
+  bool issued = false;
+  for (;;) {
+    // The lane index passes through an empty asm each tile, so values
+    // derived from it are computed per tile instead of being hoisted out of
+    // the tile loop and held in registers across it.
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int lx = ln & 31, hx = ln >> 5;
+    const int64_t next = tile + bpx;
+    const bool has_next = next < t_end;
+    v3p_offsets(no, M, K, N, ((has_next ? next : tile) % tiles_m) * kV3BM, ((has_next ? next : tile) / tiles_m) * kV3BN,
+                wave, ln);
+    f32x16_t acc[2][8];
+    v3p_mainloop<TA>(acc, XS, WS, base, o, no, has_next, issued, nslabs, wave, lx, hx);
+    v3_store_tile<TA>(acc, out, M, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kV3BN, g, wave, lx, hx);
+    if (!has_next) break;
+    tile = next;
+    o = no;
+    issued = true;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Non-transposed planes (w [K, N/8], quantized along N): dequantize, then a
 // matrix-core GEMM on the dense copy, the order of the pages' own GEMM route.
 // ----------------------------------------------------------------------------
@@ -1078,6 +1248,17 @@ static void launch_v3(const T* x, int64_t M, int64_t K, int64_t N, const uint32_
     if (rgrid > 4096) rgrid = 4096;
     if (rgrid < 1) rgrid = 1;
     split_reduce_kernel<T><<<dim3((unsigned)rgrid), dim3(256), 0, s>>>(static_cast<const float*>(ws), sp, MN, gs, out);
+    return;
+  }
+  const int64_t nslabs = K / kV3BK;
+  const int64_t cus = device_cu_count();
+  if (nslabs % 6 == 0 && nslabs >= 12 && tiles > cus && cus % 8 == 0 && M * K < ((int64_t)1 << 31) &&
+      N * (K / 8) < ((int64_t)1 << 31)) {
+    // persistent: one block per compute unit, each XCD a contiguous run of tiles
+    const int64_t per_xcd = (tiles + 7) / 8;
+    const int64_t bpx = per_xcd < cus / 8 ? per_xcd : cus / 8;
+    gemm_mfma_v3p_kernel<T><<<dim3((unsigned)(8 * bpx)), dim3(kMfmaThreads), 0, s>>>(x, w, sc, gs, out, M, K, N,
+                                                                                    tiles_m, tiles, per_xcd);
     return;
   }
   const int64_t grid = (tiles + 7) / 8 * 8;
