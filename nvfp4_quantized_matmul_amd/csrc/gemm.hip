@@ -11,6 +11,10 @@
 //    into exact bf16 (or f16) MFMA operands; float32 activations run it over
 //    their exact three-part bf16 split (split_f32_kernel); forms for the K
 //    split of few tiles and for the gated MLP projection.  Described below.
+//  * gemm_mfma_v3p_kernel: the plain v3 tile as a persistent launch (one
+//    block per compute unit walking its tiles, each tile's first slabs queued
+//    during the previous tile's last steps) when there are more tiles than
+//    compute units and K is a multiple of 384.
 //  * gemm_mfma_kernel (bf16 activations, transposed plane, K % 32 == 0):
 //    each wavefront decodes its weight rows straight from the packed words
 //    into bf16 MFMA operands (one 32-bit word = the eight k-values one lane
@@ -691,8 +695,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
 // ----------------------------------------------------------------------------
 
 // 32-bit offsets of a plain tile's slab-0 loads from the operand bases
-// (activation elements, plane words, scale bytes; as in gemm_mfma_v3_kernel),
-// so each load is a scalar base plus one offset register.
+// (activation elements, plane words, scale bytes; as in gemm_mfma_v3_kernel):
+// one register per load address instead of a 64-bit pointer's two, which
+// leaves room for the next tile's offsets.
 struct V3Off {
   uint32_t x[8];
   uint32_t w[2];
