@@ -694,10 +694,13 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
 // fastest), its blocks taking them round-robin, as in the plain launch.
 // ----------------------------------------------------------------------------
 
-// 32-bit offsets of a plain tile's slab-0 loads from the operand bases
-// (activation elements, plane words, scale bytes; as in gemm_mfma_v3_kernel):
-// one register per load address instead of a 64-bit pointer's two, which
-// leaves room for the next tile's offsets.
+// 32-bit byte offsets of a plain tile's slab-0 loads from the operand bases
+// (as in gemm_mfma_v3_kernel).  The loads are buffer loads to LDS: a buffer
+// resource per operand, the fixed lane offset in a register and the slab's
+// offset in a scalar, so there is no address arithmetic per load and no load
+// waits for an earlier one to release a shared address register (with
+// 64-bit addresses built per load in one register pair, issuing a slab's 11
+// loads took ~580 cycles).
 struct V3Off {
   uint32_t x[8];
   uint32_t w[2];
@@ -713,7 +716,7 @@ __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int6
     const int r = slot >> 3, c = (slot & 7) ^ swz(r);
     int64_t m = m_blk + r;
     if (m >= M) m = M - 1;
-    o.x[i] = (uint32_t)(m * K + c * 8);
+    o.x[i] = (uint32_t)((m * K + c * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -721,31 +724,103 @@ __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int6
     const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);
     int64_t n = n_blk + r;
     if (n >= N) n = N - 1;
-    o.w[i] = (uint32_t)(n * kw + 4 * half);
+    o.w[i] = (uint32_t)((n * kw + 4 * half) * 4);
   }
   int64_t n = n_blk + wave * 64 + lane;
   if (n >= N) n = N - 1;
   o.s = (uint32_t)(n * ks);
 }
 
+typedef __amdgpu_buffer_rsrc_t v3_rsrc_t;
+
+__device__ __forceinline__ v3_rsrc_t v3_buffer(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 struct V3Base {
-  const uint16_t* x;
-  const uint32_t* w;
-  const uint8_t* s;
+  v3_rsrc_t x, w, s;
 };
 
 __device__ __forceinline__ void v3p_issue_x(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
                                             int wave) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds(b.x + (o.x[i] + slab * kV3BK), NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.x, NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, o.x[i],
+                                             slab * (kV3BK * 2), 0, 0);
 }
 __device__ __forceinline__ void v3p_issue_w(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
                                             int wave) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    __builtin_amdgcn_global_load_lds(b.w + (o.w[i] + slab * 8), NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(b.s + (o.s + slab * 4), NVFP4_LDS(&st.s[wave * 64]), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.w, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, o.w[i], slab * 32, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(b.s, NVFP4_LDS(&st.s[wave * 64]), 4, o.s, slab * 4, 0, 0);
+}
+
+// The next slabs' 11 loads of a step (8 activation, 2 weight, 1 scale
+// copies), issued one at a time between the step's multiplies.
+struct V3pIssue {
+  const V3Stage* xs;
+  const V3Stage* ws;
+  const V3Off* xo;
+  const V3Off* wo;
+  uint32_t xslab, wslab;
+  int wave;
+  const V3Base* b;
+  __device__ __forceinline__ void operator()(int k) const {
+    if (k < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->x, NVFP4_LDS(&xs->x[(k * 4 + wave) * 64]), 16, xo->x[k],
+                                               xslab * (kV3BK * 2), 0, 0);
+    else if (k < 10)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->w, NVFP4_LDS(&ws->w[((k - 8) * 4 + wave) * 64]), 16, wo->w[k - 8],
+                                               wslab * 32, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->s, NVFP4_LDS(&ws->s[wave * 64]), 4, wo->s, wslab * 4, 0, 0);
+  }
+};
+
+// v3_compute with the step's loads spread over its multiplies: three after
+// multiply pairs 1, 3 and 5 of sub-steps 0-2, two after pairs 1 and 3 of
+// sub-step 3, in issue order, so a load never waits for the whole step's
+// loads to enter the memory pipeline before the first multiply.
+template <typename TA>
+__device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave, int l32, int h,
+                                            const V3pIssue& iss) {
+  typedef typename V3Ops<TA>::vec vec;
+  uint4 wr[2];
+  float slo[2], shi[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int row = wave * 64 + a * 32 + l32;
+    wr[a] = st.w[wslot(row, h)];
+    const uint32_t sv = st.s[row] >> (16 * h);
+    slo[a] = e4m3<0>(sv);
+    shi[a] = e4m3<1>(sv);
+  }
+  int k = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vec B[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]);
+    vec A[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
+      A[a] = V3Ops<TA>::decode(word, j < 2 ? slo[a] : shi[a]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      acc[0][b] = V3Ops<TA>::mfma(A[0], B[b], acc[0][b]);
+      acc[1][b] = V3Ops<TA>::mfma(A[1], B[b], acc[1][b]);
+      if ((b & 1) && (j < 3 ? b < 7 : b < 5)) {
+        __builtin_amdgcn_sched_barrier(0);
+        iss(k);
+        ++k;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
 }
 
 // One tile's slabs (nslabs % 6 == 0, nslabs >= 12).  `issued`: the first
@@ -775,10 +850,9 @@ __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stag
   do {                                                                               \
     wait_vmem(true);                                                                 \
     __builtin_amdgcn_s_barrier();                                                    \
-    v3p_issue_x(X[((XI) + 2) % 3], b, XO, XSLAB, wave);                              \
-    v3p_issue_w(W[((WI) + 3) % 6], b, WO, WSLAB, wave);                              \
+    const V3pIssue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &(XO), &(WO), (XSLAB), (WSLAB), wave, &b}; \
     const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
-    v3_compute<TA>(acc, cur, wave, l32, h);                                          \
+    v3p_compute<TA>(acc, cur, wave, l32, h, iss);                                    \
   } while (0)
   uint32_t s = 0;
   for (; s + 6 < nslabs; s += 6) {
@@ -827,7 +901,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const uint32_t nslabs = (uint32_t)(K / kV3BK);
   const float g = global_factor(gs, 0);
-  const V3Base base{reinterpret_cast<const uint16_t*>(x), w, sc};
+  const V3Base base{v3_buffer(x, M * K * 2), v3_buffer(w, N * (K / 2)), v3_buffer(sc, N * (K / 16))};
   V3Off o, no;
   v3p_offsets(o, M, K, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kV3BN, wave, lane);
   bool issued = false;
@@ -1258,7 +1332,7 @@ static void launch_v3(const T* x, int64_t M, int64_t K, int64_t N, const uint32_
   const int64_t nslabs = K / kV3BK;
   const int64_t cus = device_cu_count();
   if (nslabs % 6 == 0 && nslabs >= 12 && tiles > cus && cus % 8 == 0 && M * K < ((int64_t)1 << 31) &&
-      N * (K / 8) < ((int64_t)1 << 31)) {
+      N * (K / 8) < ((int64_t)1 << 30)) {   // byte offsets within 32 bits
     // persistent: one block per compute unit, each XCD a contiguous run of tiles
     const int64_t per_xcd = (tiles + 7) / 8;
     const int64_t bpx = per_xcd < cus / 8 ? per_xcd : cus / 8;
