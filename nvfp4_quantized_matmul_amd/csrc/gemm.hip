@@ -778,10 +778,12 @@ struct V3pIssue {
   }
 };
 
-// v3_compute with the step's loads spread over its multiplies: three after
-// multiply pairs 1, 3 and 5 of sub-steps 0-2, two after pairs 1 and 3 of
-// sub-step 3, in issue order, so a load never waits for the whole step's
-// loads to enter the memory pipeline before the first multiply.
+// v3_compute with the step's loads spread over its multiplies, in issue
+// order: load k goes out after multiply kV3pLoadAfter[k] of the step's 64
+// (-1: before the first fragment reads), so no multiply waits for the whole
+// step's loads to enter the memory pipeline, and the loads still leave early
+// in the step.
+constexpr int kV3pLoadAfter[11] = {1, 3, 5, 7, 9, 11, 13, 15, 17, 19, 21};
 template <typename TA>
 __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave, int l32, int h,
                                             const V3pIssue& iss) {
@@ -796,7 +798,10 @@ __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage
     slo[a] = e4m3<0>(sv);
     shi[a] = e4m3<1>(sv);
   }
-  int k = 0;
+#pragma unroll
+  for (int k = 0; k < 11; ++k)
+    if (kV3pLoadAfter[k] < 0) iss(k);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     vec B[8];
@@ -811,13 +816,16 @@ __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      acc[0][b] = V3Ops<TA>::mfma(A[0], B[b], acc[0][b]);
-      acc[1][b] = V3Ops<TA>::mfma(A[1], B[b], acc[1][b]);
-      if ((b & 1) && (j < 3 ? b < 7 : b < 5)) {
-        __builtin_amdgcn_sched_barrier(0);
-        iss(k);
-        ++k;
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        acc[a][b] = V3Ops<TA>::mfma(A[a], B[b], acc[a][b]);
+#pragma unroll
+        for (int k = 0; k < 11; ++k)
+          if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
+            __builtin_amdgcn_sched_barrier(0);
+            iss(k);
+            __builtin_amdgcn_sched_barrier(0);
+          }
       }
     }
   }
