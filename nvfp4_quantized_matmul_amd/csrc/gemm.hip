@@ -1339,8 +1339,10 @@ static void launch_v3(const T* x, int64_t M, int64_t K, int64_t N, const uint32_
   }
   const int64_t nslabs = K / kV3BK;
   const int64_t cus = device_cu_count();
-  if (nslabs % 6 == 0 && nslabs >= 12 && tiles > cus && cus % 8 == 0 && M * K < ((int64_t)1 << 31) &&
-      N * (K / 8) < ((int64_t)1 << 30)) {   // byte offsets within 32 bits
+  // (buffer resources hold at most 2^31 - 1 bytes: activations M K 2 and
+  // plane N K / 2 bytes below 2^31)
+  if (nslabs % 6 == 0 && nslabs >= 12 && tiles > cus && cus % 8 == 0 && M * K < ((int64_t)1 << 30) &&
+      N * (K / 8) < ((int64_t)1 << 29)) {
     // persistent: one block per compute unit, each XCD a contiguous run of tiles
     const int64_t per_xcd = (tiles + 7) / 8;
     const int64_t bpx = per_xcd < cus / 8 ? per_xcd : cus / 8;
