@@ -479,6 +479,185 @@ __device__ __forceinline__ void v3_store_tile(const f32x16_t (&acc)[2][8], TO* _
   }
 }
 
+// 32-bit byte offsets of a plain tile's slab-0 loads from the operand bases
+// (as in gemm_mfma_v3_kernel).  The loads are buffer loads to LDS: a buffer
+// resource per operand, the fixed lane offset in a register and the slab's
+// offset in a scalar, so there is no address arithmetic per load and no load
+// waits for an earlier one to release a shared address register (with
+// 64-bit addresses built per load in one register pair, issuing a slab's 11
+// loads took ~580 cycles).
+struct V3Off {
+  uint32_t x[8];
+  uint32_t w[2];
+  uint32_t s;
+};
+
+typedef __amdgpu_buffer_rsrc_t v3_rsrc_t;
+
+__device__ __forceinline__ v3_rsrc_t v3_buffer(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+struct V3Base {
+  v3_rsrc_t x, w, s;
+};
+
+__device__ __forceinline__ void v3p_issue_x(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
+                                            int wave) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.x, NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, o.x[i],
+                                             slab * (kV3BK * 2), 0, 0);
+}
+__device__ __forceinline__ void v3p_issue_w(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
+                                            int wave) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.w, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, o.w[i], slab * 32, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(b.s, NVFP4_LDS(&st.s[wave * 64]), 4, o.s, slab * 4, 0, 0);
+}
+
+// The next slabs' 11 loads of a step (8 activation, 2 weight, 1 scale
+// copies), issued one at a time between the step's multiplies.  kLaneScale:
+// the scale copy is a global load from a per-lane address (the gated form,
+// whose scale lanes read two planes), the others buffer loads.
+template <bool kLaneScale = false>
+struct V3pIssueT {
+  const V3Stage* xs;
+  const V3Stage* ws;
+  const V3Off* xo;
+  const V3Off* wo;
+  uint32_t xslab, wslab;
+  int wave;
+  const V3Base* b;
+  const uint8_t* lane_s;   // kLaneScale: this lane's scale row at slab 0
+  __device__ __forceinline__ void operator()(int k) const {
+    if (k < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->x, NVFP4_LDS(&xs->x[(k * 4 + wave) * 64]), 16, xo->x[k],
+                                               xslab * (kV3BK * 2), 0, 0);
+    else if (k < 10)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->w, NVFP4_LDS(&ws->w[((k - 8) * 4 + wave) * 64]), 16, wo->w[k - 8],
+                                               wslab * 32, 0, 0);
+    else if constexpr (kLaneScale)
+      __builtin_amdgcn_global_load_lds(lane_s + (size_t)wslab * 4, NVFP4_LDS(&ws->s[wave * 64]), 4, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->s, NVFP4_LDS(&ws->s[wave * 64]), 4, wo->s, wslab * 4, 0, 0);
+  }
+};
+typedef V3pIssueT<false> V3pIssue;
+
+// v3_compute with the step's loads spread over its multiplies, in issue
+// order: load k goes out after multiply kV3pLoadAfter[k] of the step's 64
+// (-1: before the first fragment reads), so no multiply waits for the whole
+// step's loads to enter the memory pipeline, and the loads still leave early
+// in the step.
+constexpr int kV3pLoadAfter[11] = {1, 3, 5, 7, 9, 11, 13, 15, 17, 19, 21};
+template <typename TA, typename Issue>
+__device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave, int l32, int h,
+                                            const Issue& iss) {
+  typedef typename V3Ops<TA>::vec vec;
+  uint4 wr[2];
+  float slo[2], shi[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int row = wave * 64 + a * 32 + l32;
+    wr[a] = st.w[wslot(row, h)];
+    const uint32_t sv = st.s[row] >> (16 * h);
+    slo[a] = e4m3<0>(sv);
+    shi[a] = e4m3<1>(sv);
+  }
+#pragma unroll
+  for (int k = 0; k < 11; ++k)
+    if (kV3pLoadAfter[k] < 0) iss(k);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vec B[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]);
+    vec A[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
+      A[a] = V3Ops<TA>::decode(word, j < 2 ? slo[a] : shi[a]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        acc[a][b] = V3Ops<TA>::mfma(A[a], B[b], acc[a][b]);
+#pragma unroll
+        for (int k = 0; k < 11; ++k)
+          if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
+            __builtin_amdgcn_sched_barrier(0);
+            iss(k);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+    }
+  }
+}
+
+// v3_mainloop with buffer loads spread between the multiplies, as in the
+// persistent launch (same stages, waits and issue order, so the same sums).
+// Activation slab s meets weight slab s mod wslabs; the loads past the last
+// slab queue it again.  `lane_s`: the gated form's per-lane scale rows.
+template <typename TA, bool kLaneScale>
+__device__ __forceinline__ void v3b_mainloop(f32x16_t (&acc)[2][8], const V3Stage (&X)[3], const V3Stage (&W)[6],
+                                             const V3Base& b, const V3Off& o, const uint8_t* lane_s,
+                                             int64_t nslabs, int64_t wslabs, int wave, int l32, int h) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.0f;
+  auto wsl = [&](int64_t q) { return (uint32_t)(q < wslabs ? q : q % wslabs); };
+  auto cl = [&](int64_t q) { return q < nslabs ? q : nslabs - 1; };
+  typedef V3pIssueT<kLaneScale> Issue;
+  {
+    const Issue p0{&X[0], &W[0], &o, &o, 0u, 0u, wave, &b, lane_s};
+    const Issue p1{&X[1], &W[1], &o, &o, (uint32_t)cl(1), wsl(cl(1)), wave, &b, lane_s};
+    const Issue p2{&X[2], &W[2], &o, &o, (uint32_t)cl(2), wsl(cl(2)), wave, &b, lane_s};
+#pragma unroll
+    for (int k = 8; k < 11; ++k) p0(k);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p0(k);
+#pragma unroll
+    for (int k = 8; k < 11; ++k) p1(k);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p1(k);
+#pragma unroll
+    for (int k = 8; k < 11; ++k) p2(k);
+  }
+#define NVFP4_V3B_STEP(S, XI, WI)                                                    \
+  do {                                                                               \
+    wait_vmem(true);                                                                 \
+    __builtin_amdgcn_s_barrier();                                                    \
+    const Issue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &o, &o, (uint32_t)cl((S) + 2), \
+                    wsl(cl((S) + 3)), wave, &b, lane_s};                             \
+    const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
+    v3p_compute<TA>(acc, cur, wave, l32, h, iss);                                    \
+  } while (0)
+  int64_t s = 0;
+  for (; s + 6 <= nslabs; s += 6) {
+    NVFP4_V3B_STEP(s, 0, 0);
+    NVFP4_V3B_STEP(s + 1, 1, 1);
+    NVFP4_V3B_STEP(s + 2, 2, 2);
+    NVFP4_V3B_STEP(s + 3, 0, 3);
+    NVFP4_V3B_STEP(s + 4, 1, 4);
+    NVFP4_V3B_STEP(s + 5, 2, 5);
+  }
+  if (s < nslabs) NVFP4_V3B_STEP(s, 0, 0);
+  if (s + 1 < nslabs) NVFP4_V3B_STEP(s + 1, 1, 1);
+  if (s + 2 < nslabs) NVFP4_V3B_STEP(s + 2, 2, 2);
+  if (s + 3 < nslabs) NVFP4_V3B_STEP(s + 3, 0, 3);
+  if (s + 4 < nslabs) NVFP4_V3B_STEP(s + 4, 1, 4);
+  wait_vmem(false);   // no load-to-LDS may land after this point
+#undef NVFP4_V3B_STEP
+}
+
 // What one block computes.
 //   kV3Plain: out tile = round(g * x W^T) over 256 weight rows.
 //   kV3Split: the block multiplies slabs [split * per_split, ...) of its tile
@@ -507,7 +686,10 @@ constexpr int kV3Plain = 0, kV3Split = 1, kV3Glu = 2, kV3GluSplit = 3;
 // whose activation rows are three bf16 parts laid end to end (K = 192
 // wslabs): one plane multiplies each part and the three sums accumulate
 // together.
-template <int kMode, int kAct = 0, typename TA = __bf16, typename TO = __bf16>
+// kBuf: every operand below 2^31 bytes, so the loads are buffer loads from
+// 32-bit offsets, spread between the multiplies (v3b_mainloop); otherwise
+// global loads from 64-bit addresses, all issued after each step's barrier.
+template <int kMode, int kAct = 0, typename TA = __bf16, typename TO = __bf16, bool kBuf = false>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     const TA* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
     const float* __restrict__ gs, TO* __restrict__ out, int64_t M, int64_t K, int64_t N,
@@ -547,52 +729,88 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
   const int64_t nslabs = kSplit ? (all_slabs - first_slab < per_split ? all_slabs - first_slab : per_split)
                                 : all_slabs;
 
-  // Source addresses of this lane's loads for slab 0.  Rows past M or N
-  // re-read the last row (their results are never stored).
-  V3Src src;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int slot = (i * 4 + wave) * 64 + lane;
-    const int r = slot >> 3, c = (slot & 7) ^ swz(r);
-    int64_t m = m_blk + r;
-    if (m >= M) m = M - 1;
-    src.x[i] = reinterpret_cast<const uint16_t*>(x) + m * K + c * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = (i * 4 + wave) * 64 + lane;
-    const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);   // inverse of wslot
-    if constexpr (kGlu) {
-      // Tile row r = 64 w' + 32 a + l: feature n_blk + 32 w' + l of the gate
-      // (a = 0) or up (a = 1) plane.
-      int64_t f = n_blk + (r >> 6) * 32 + (r & 31);
-      if (f >= N) f = N - 1;
-      src.w[i] = (((r >> 5) & 1) ? wu : w) + f * kw + 4 * half;
-    } else {
-      int64_t n = n_blk + r;
-      if (n >= N) n = N - 1;
-      src.w[i] = w + n * kw + 4 * half;
-    }
-  }
-  if constexpr (kGlu) {
-    int64_t f = n_blk + wave * 32 + (lane & 31);
-    if (f >= N) f = N - 1;
-    src.s = ((lane >> 5) ? scu : sc) + f * ks;
-  } else {
-    int64_t n = n_blk + wave * 64 + lane;
-    if (n >= N) n = N - 1;
-    src.s = sc + n * ks;
-  }
-  if (kSplit) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) src.x[i] += first_slab * kV3BK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) src.w[i] += first_slab * 8;
-    src.s += first_slab * 4;
-  }
-
   f32x16_t acc[2][8];
-  v3_mainloop<TA>(acc, XS, WS, src, nslabs, wslabs, wave, l32, h);
+  if constexpr (kBuf) {
+    // Byte offsets of this lane's loads for slab 0 (rows past M or N re-read
+    // the last row; their results are never stored).
+    V3Off o;
+    const uint8_t* lane_s = nullptr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = (i * 4 + wave) * 64 + lane;
+      const int r = slot >> 3, c = (slot & 7) ^ swz(r);
+      int64_t m = m_blk + r;
+      if (m >= M) m = M - 1;
+      o.x[i] = (uint32_t)((m * K + c * 8 + first_slab * kV3BK) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = (i * 4 + wave) * 64 + lane;
+      const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);
+      int64_t n = kGlu ? n_blk + (r >> 6) * 32 + (r & 31) : n_blk + r;   // gated: plane (r >> 5) & 1 = wave & 1
+      if (n >= N) n = N - 1;
+      o.w[i] = (uint32_t)((n * kw + 4 * half + first_slab * 8) * 4);
+    }
+    if constexpr (kGlu) {
+      int64_t f = n_blk + wave * 32 + (lane & 31);
+      if (f >= N) f = N - 1;
+      lane_s = ((lane >> 5) ? scu : sc) + f * ks + first_slab * 4;
+      o.s = 0;
+    } else {
+      int64_t n = n_blk + wave * 64 + lane;
+      if (n >= N) n = N - 1;
+      o.s = (uint32_t)(n * ks + first_slab * 4);
+    }
+    const V3Base b{v3_buffer(x, M * K * 2), v3_buffer((kGlu && (wave & 1)) ? wu : w, N * kw * 4),
+                   v3_buffer(sc, N * ks)};
+    v3b_mainloop<TA, kGlu>(acc, XS, WS, b, o, lane_s, nslabs, wslabs, wave, l32, h);
+  } else {
+    // Source addresses of this lane's loads for slab 0.  Rows past M or N
+    // re-read the last row (their results are never stored).
+    V3Src src;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = (i * 4 + wave) * 64 + lane;
+      const int r = slot >> 3, c = (slot & 7) ^ swz(r);
+      int64_t m = m_blk + r;
+      if (m >= M) m = M - 1;
+      src.x[i] = reinterpret_cast<const uint16_t*>(x) + m * K + c * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = (i * 4 + wave) * 64 + lane;
+      const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);   // inverse of wslot
+      if constexpr (kGlu) {
+        // Tile row r = 64 w' + 32 a + l: feature n_blk + 32 w' + l of the gate
+        // (a = 0) or up (a = 1) plane.
+        int64_t f = n_blk + (r >> 6) * 32 + (r & 31);
+        if (f >= N) f = N - 1;
+        src.w[i] = (((r >> 5) & 1) ? wu : w) + f * kw + 4 * half;
+      } else {
+        int64_t n = n_blk + r;
+        if (n >= N) n = N - 1;
+        src.w[i] = w + n * kw + 4 * half;
+      }
+    }
+    if constexpr (kGlu) {
+      int64_t f = n_blk + wave * 32 + (lane & 31);
+      if (f >= N) f = N - 1;
+      src.s = ((lane >> 5) ? scu : sc) + f * ks;
+    } else {
+      int64_t n = n_blk + wave * 64 + lane;
+      if (n >= N) n = N - 1;
+      src.s = sc + n * ks;
+    }
+    if (kSplit) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) src.x[i] += first_slab * kV3BK;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) src.w[i] += first_slab * 8;
+      src.s += first_slab * 4;
+    }
+
+    v3_mainloop<TA>(acc, XS, WS, src, nslabs, wslabs, wave, l32, h);
+  }
 
   if constexpr (kMode == kV3GluSplit) {
     // Tile-local partial: fragment (a, b) holds C[n][m] with tile row
@@ -694,19 +912,6 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
 // fastest), its blocks taking them round-robin, as in the plain launch.
 // ----------------------------------------------------------------------------
 
-// 32-bit byte offsets of a plain tile's slab-0 loads from the operand bases
-// (as in gemm_mfma_v3_kernel).  The loads are buffer loads to LDS: a buffer
-// resource per operand, the fixed lane offset in a register and the slab's
-// offset in a scalar, so there is no address arithmetic per load and no load
-// waits for an earlier one to release a shared address register (with
-// 64-bit addresses built per load in one register pair, issuing a slab's 11
-// loads took ~580 cycles).
-struct V3Off {
-  uint32_t x[8];
-  uint32_t w[2];
-  uint32_t s;
-};
-
 __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int64_t N, int64_t m_blk,
                                             int64_t n_blk, int wave, int lane) {
   const int64_t kw = K / 8, ks = K / 16;
@@ -729,106 +934,6 @@ __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int6
   int64_t n = n_blk + wave * 64 + lane;
   if (n >= N) n = N - 1;
   o.s = (uint32_t)(n * ks);
-}
-
-typedef __amdgpu_buffer_rsrc_t v3_rsrc_t;
-
-__device__ __forceinline__ v3_rsrc_t v3_buffer(const void* p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-struct V3Base {
-  v3_rsrc_t x, w, s;
-};
-
-__device__ __forceinline__ void v3p_issue_x(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
-                                            int wave) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.x, NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, o.x[i],
-                                             slab * (kV3BK * 2), 0, 0);
-}
-__device__ __forceinline__ void v3p_issue_w(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
-                                            int wave) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.w, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, o.w[i], slab * 32, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(b.s, NVFP4_LDS(&st.s[wave * 64]), 4, o.s, slab * 4, 0, 0);
-}
-
-// The next slabs' 11 loads of a step (8 activation, 2 weight, 1 scale
-// copies), issued one at a time between the step's multiplies.
-struct V3pIssue {
-  const V3Stage* xs;
-  const V3Stage* ws;
-  const V3Off* xo;
-  const V3Off* wo;
-  uint32_t xslab, wslab;
-  int wave;
-  const V3Base* b;
-  __device__ __forceinline__ void operator()(int k) const {
-    if (k < 8)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->x, NVFP4_LDS(&xs->x[(k * 4 + wave) * 64]), 16, xo->x[k],
-                                               xslab * (kV3BK * 2), 0, 0);
-    else if (k < 10)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->w, NVFP4_LDS(&ws->w[((k - 8) * 4 + wave) * 64]), 16, wo->w[k - 8],
-                                               wslab * 32, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b->s, NVFP4_LDS(&ws->s[wave * 64]), 4, wo->s, wslab * 4, 0, 0);
-  }
-};
-
-// v3_compute with the step's loads spread over its multiplies, in issue
-// order: load k goes out after multiply kV3pLoadAfter[k] of the step's 64
-// (-1: before the first fragment reads), so no multiply waits for the whole
-// step's loads to enter the memory pipeline, and the loads still leave early
-// in the step.
-constexpr int kV3pLoadAfter[11] = {1, 3, 5, 7, 9, 11, 13, 15, 17, 19, 21};
-template <typename TA>
-__device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave, int l32, int h,
-                                            const V3pIssue& iss) {
-  typedef typename V3Ops<TA>::vec vec;
-  uint4 wr[2];
-  float slo[2], shi[2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int row = wave * 64 + a * 32 + l32;
-    wr[a] = st.w[wslot(row, h)];
-    const uint32_t sv = st.s[row] >> (16 * h);
-    slo[a] = e4m3<0>(sv);
-    shi[a] = e4m3<1>(sv);
-  }
-#pragma unroll
-  for (int k = 0; k < 11; ++k)
-    if (kV3pLoadAfter[k] < 0) iss(k);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    vec B[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]);
-    vec A[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
-      A[a] = V3Ops<TA>::decode(word, j < 2 ? slo[a] : shi[a]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        acc[a][b] = V3Ops<TA>::mfma(A[a], B[b], acc[a][b]);
-#pragma unroll
-        for (int k = 0; k < 11; ++k)
-          if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
-            __builtin_amdgcn_sched_barrier(0);
-            iss(k);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      }
-    }
-  }
 }
 
 // One tile's slabs (nslabs % 6 == 0, nslabs >= 12).  `issued`: the first
@@ -1316,6 +1421,14 @@ int64_t gemm_splits(int64_t M, int64_t K, int64_t N) {
   return best;
 }
 
+// The v3 kernel's buffer-load form applies when every operand stays below
+// 2^31 bytes (buffer resources hold 31-bit sizes): activation rows of Kx
+// 2-byte elements, planes of N rows of K / 2 bytes.
+static bool v3_buffers_fit(int64_t M, int64_t Kx, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)1 << 31;
+  return M * Kx * 2 < lim && N * (K / 2) < lim && N * (K / 16) < lim;
+}
+
 // The two-byte MFMA GEMM (bf16 or f16 activations and output) with an
 // optional K split through the workspace.
 template <typename T>
@@ -1327,9 +1440,11 @@ static void launch_v3(const T* x, int64_t M, int64_t K, int64_t N, const uint32_
   if (sp > 1 && ws_bytes >= sp * M * N * 4 && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) {
     const int64_t per = v3_piece(K / kV3BK, sp);
     const int64_t grid = (tiles * sp + 7) / 8 * 8;
-    gemm_mfma_v3_kernel<kV3Split, 0, T, T><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-        x, w, sc, gs, out, M, K, N, tiles_m, tiles, per, static_cast<float*>(ws), nullptr, nullptr, nullptr, 0,
-        K / kV3BK);
+    auto kern = v3_buffers_fit(M, K, N, K) ? gemm_mfma_v3_kernel<kV3Split, 0, T, T, true>
+                                           : gemm_mfma_v3_kernel<kV3Split, 0, T, T, false>;
+    kern<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(x, w, sc, gs, out, M, K, N, tiles_m, tiles, per,
+                                                            static_cast<float*>(ws), nullptr, nullptr, nullptr, 0,
+                                                            K / kV3BK);
     const int64_t MN = M * N;
     int64_t rgrid = (MN / 4 + 255) / 256;
     if (rgrid > 4096) rgrid = 4096;
@@ -1351,8 +1466,10 @@ static void launch_v3(const T* x, int64_t M, int64_t K, int64_t N, const uint32_
     return;
   }
   const int64_t grid = (tiles + 7) / 8 * 8;
-  gemm_mfma_v3_kernel<kV3Plain, 0, T, T><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-      x, w, sc, gs, out, M, K, N, tiles_m, tiles, 0, nullptr, nullptr, nullptr, nullptr, 0, K / kV3BK);
+  auto kern = v3_buffers_fit(M, K, N, K) ? gemm_mfma_v3_kernel<kV3Plain, 0, T, T, true>
+                                         : gemm_mfma_v3_kernel<kV3Plain, 0, T, T, false>;
+  kern<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(x, w, sc, gs, out, M, K, N, tiles_m, tiles, 0, nullptr,
+                                                          nullptr, nullptr, nullptr, 0, K / kV3BK);
 }
 
 // Workspace of the float32 form: the [M, 3K] bf16 split of the activations.
@@ -1445,9 +1562,11 @@ bool launch_gemm_mfma(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int
       const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
       const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
       const int64_t grid = (tiles + 7) / 8 * 8;
-      gemm_mfma_v3_kernel<kV3Plain, 0, __bf16, float><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
-          reinterpret_cast<const __bf16*>(xs), w, sc, gs, static_cast<float*>(out), M, 3 * K, N, tiles_m, tiles, 0,
-          nullptr, nullptr, nullptr, nullptr, 0, K / kV3BK);
+      auto kern = v3_buffers_fit(M, 3 * K, N, K) ? gemm_mfma_v3_kernel<kV3Plain, 0, __bf16, float, true>
+                                                 : gemm_mfma_v3_kernel<kV3Plain, 0, __bf16, float, false>;
+      kern<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(reinterpret_cast<const __bf16*>(xs), w, sc, gs,
+                                                              static_cast<float*>(out), M, 3 * K, N, tiles_m, tiles,
+                                                              0, nullptr, nullptr, nullptr, nullptr, 0, K / kV3BK);
       return true;
     }
   }
@@ -1497,9 +1616,15 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
   const int64_t dp = tiles - tail;
   if (dp > 0) {
     const int64_t grid = (dp + 7) / 8 * 8;
-    auto glu = gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_SILU>;
-    if (act == NVFP4_ACT_GELU_TANH) glu = gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU_TANH>;
-    if (act == NVFP4_ACT_GELU) glu = gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU>;
+    const bool buf = v3_buffers_fit(M, K, F, K);
+    auto glu = buf ? gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_SILU, __bf16, __bf16, true>
+                   : gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_SILU, __bf16, __bf16, false>;
+    if (act == NVFP4_ACT_GELU_TANH)
+      glu = buf ? gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU_TANH, __bf16, __bf16, true>
+                : gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU_TANH, __bf16, __bf16, false>;
+    if (act == NVFP4_ACT_GELU)
+      glu = buf ? gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU, __bf16, __bf16, true>
+                : gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_GELU, __bf16, __bf16, false>;
     glu<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate,
                                                           static_cast<__bf16*>(out), M, K, F, tiles_m, dp, 0, nullptr,
                                                           w_up, s_up, gs_up, 0, K / kV3BK);
@@ -1507,7 +1632,9 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
   if (tail == 0) return;
   const int64_t per = v3_piece(K / kV3BK, sp);
   const int64_t grid = (tail * sp + 7) / 8 * 8;
-  gemm_mfma_v3_kernel<kV3GluSplit><<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
+  auto split = v3_buffers_fit(M, K, F, K) ? gemm_mfma_v3_kernel<kV3GluSplit, 0, __bf16, __bf16, true>
+                                          : gemm_mfma_v3_kernel<kV3GluSplit, 0, __bf16, __bf16, false>;
+  split<<<dim3((unsigned)grid), dim3(kMfmaThreads), 0, s>>>(
       static_cast<const __bf16*>(x), w_gate, s_gate, gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m, tail, per,
       static_cast<float*>(ws), w_up, s_up, gs_up, dp, K / kV3BK);
   int64_t rgrid = (tail * 256 * 32 + 255) / 256;
