@@ -552,7 +552,7 @@ typedef V3pIssueT<false> V3pIssue;
 // step's loads to enter the memory pipeline, and the loads still leave early
 // in the step.
 constexpr int kV3pLoadAfter[11] = {1, 3, 5, 7, 9, 11, 13, 15, 17, 19, 21};
-template <typename TA, typename Issue>
+template <typename TA, bool kDbl = false, typename Issue>
 __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave, int l32, int h,
                                             const Issue& iss) {
   typedef typename V3Ops<TA>::vec vec;
@@ -569,6 +569,52 @@ __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage
 #pragma unroll
   for (int k = 0; k < 11; ++k)
     if (kV3pLoadAfter[k] < 0) iss(k);
+  auto rdB = [&](int j, int b) { return __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]); };
+  auto dec = [&](int j, int a) {
+    const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
+    return V3Ops<TA>::decode(word, j < 2 ? slo[a] : shi[a]);
+  };
+  if constexpr (kDbl) {
+    // Double-buffered fragments: sub-step j + 1's fragments are read and its
+    // words decoded into the other registers between sub-step j's
+    // multiplies (32 + 8 more registers).
+    vec B[2][8], A[2][2];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) B[0][b] = rdB(0, b);
+    A[0][0] = dec(0, 0);
+    A[0][1] = dec(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = j & 1, n = c ^ 1;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          acc[a][b] = V3Ops<TA>::mfma(A[c][a], B[c][b], acc[a][b]);
+#pragma unroll
+          for (int k = 0; k < 11; ++k)
+            if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
+              __builtin_amdgcn_sched_barrier(0);
+              iss(k);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          if (j < 3) {
+            if (a == 0) {
+              __builtin_amdgcn_sched_barrier(0);
+              B[n][b] = rdB(j + 1, b);
+              __builtin_amdgcn_sched_barrier(0);
+            } else if (b == 2 || b == 5) {
+              __builtin_amdgcn_sched_barrier(0);
+              A[n][b == 2 ? 0 : 1] = dec(j + 1, b == 2 ? 0 : 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -965,7 +1011,7 @@ __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stag
     __builtin_amdgcn_s_barrier();                                                    \
     const V3pIssue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &(XO), &(WO), (XSLAB), (WSLAB), wave, &b}; \
     const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
-    v3p_compute<TA>(acc, cur, wave, l32, h, iss);                                    \
+    v3p_compute<TA, true>(acc, cur, wave, l32, h, iss);                              \
   } while (0)
   uint32_t s = 0;
   for (; s + 6 < nslabs; s += 6) {
