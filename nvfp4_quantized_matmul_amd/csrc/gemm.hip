@@ -13,8 +13,9 @@
 //    split of few tiles and for the gated MLP projection.  Described below.
 //  * gemm_mfma_v3p_kernel: the plain v3 tile as a persistent launch (one
 //    block per compute unit walking its tiles, each tile's first slabs queued
-//    during the previous tile's last steps) when there are more tiles than
-//    compute units and K is a multiple of 384.
+//    during the previous tile's last steps, each step's first operands read
+//    during the previous step's last multiplies) when there are more tiles
+//    than compute units and K is a multiple of 384.
 //  * gemm_mfma_kernel (bf16 activations, transposed plane, K % 32 == 0):
 //    each wavefront decodes its weight rows straight from the packed words
 //    into bf16 MFMA operands (one 32-bit word = the eight k-values one lane
@@ -552,7 +553,7 @@ typedef V3pIssueT<false> V3pIssue;
 // step's loads to enter the memory pipeline, and the loads still leave early
 // in the step.
 constexpr int kV3pLoadAfter[11] = {1, 3, 5, 7, 9, 11, 13, 15, 17, 19, 21};
-template <typename TA, bool kDbl = false, typename Issue>
+template <typename TA, typename Issue>
 __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage& st, int wave, int l32, int h,
                                             const Issue& iss) {
   typedef typename V3Ops<TA>::vec vec;
@@ -569,52 +570,6 @@ __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage
 #pragma unroll
   for (int k = 0; k < 11; ++k)
     if (kV3pLoadAfter[k] < 0) iss(k);
-  auto rdB = [&](int j, int b) { return __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]); };
-  auto dec = [&](int j, int a) {
-    const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
-    return V3Ops<TA>::decode(word, j < 2 ? slo[a] : shi[a]);
-  };
-  if constexpr (kDbl) {
-    // Double-buffered fragments: sub-step j + 1's fragments are read and its
-    // words decoded into the other registers between sub-step j's
-    // multiplies (32 + 8 more registers).
-    vec B[2][8], A[2][2];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) B[0][b] = rdB(0, b);
-    A[0][0] = dec(0, 0);
-    A[0][1] = dec(0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = j & 1, n = c ^ 1;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          acc[a][b] = V3Ops<TA>::mfma(A[c][a], B[c][b], acc[a][b]);
-#pragma unroll
-          for (int k = 0; k < 11; ++k)
-            if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
-              __builtin_amdgcn_sched_barrier(0);
-              iss(k);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          if (j < 3) {
-            if (a == 0) {
-              __builtin_amdgcn_sched_barrier(0);
-              B[n][b] = rdB(j + 1, b);
-              __builtin_amdgcn_sched_barrier(0);
-            } else if (b == 2 || b == 5) {
-              __builtin_amdgcn_sched_barrier(0);
-              A[n][b == 2 ? 0 : 1] = dec(j + 1, b == 2 ? 0 : 1);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-        }
-      }
-    }
-    return;
-  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -982,6 +937,133 @@ __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int6
   o.s = (uint32_t)(n * ks);
 }
 
+// Fragment registers of the persistent launch, carried from one step to the
+// next: two sets of eight activation fragments and two decoded A operands
+// (set j & 1 feeds sub-step j), and the weight words and block scales of the
+// step being decoded.
+template <typename TA>
+struct V3Frags {
+  typename V3Ops<TA>::vec B[2][8], A[2][2];
+  uint4 wr[2];
+  uint32_t sr[2];
+  float slo[2], shi[2];
+};
+
+// The step's words and scale words from LDS (v3q_words), then the two block
+// scales of each row decoded (v3q_scales), kept apart so that the LDS reads
+// can be in flight during multiplies before anything waits for them.
+template <typename TA>
+__device__ __forceinline__ void v3q_words(V3Frags<TA>& f, const V3Stage& st, int wave, int l32, int h) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int row = wave * 64 + a * 32 + l32;
+    f.wr[a] = st.w[wslot(row, h)];
+    f.sr[a] = st.s[row];
+  }
+}
+template <typename TA>
+__device__ __forceinline__ void v3q_scales(V3Frags<TA>& f, int h) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const uint32_t sv = f.sr[a] >> (16 * h);
+    f.slo[a] = e4m3<0>(sv);
+    f.shi[a] = e4m3<1>(sv);
+  }
+}
+template <typename TA>
+__device__ __forceinline__ typename V3Ops<TA>::vec v3q_dec(const V3Frags<TA>& f, int j, int a) {
+  const uint32_t word = j == 0 ? f.wr[a].x : j == 1 ? f.wr[a].y : j == 2 ? f.wr[a].z : f.wr[a].w;
+  return V3Ops<TA>::decode(word, j < 2 ? f.slo[a] : f.shi[a]);
+}
+template <typename TA>
+__device__ __forceinline__ typename V3Ops<TA>::vec v3q_rdB(const V3Stage& st, int j, int b, int l32, int h) {
+  return __builtin_bit_cast(typename V3Ops<TA>::vec, st.x[xslot(b * 32 + l32, 4 * h + j)]);
+}
+
+// A step's first operands: words, scales, sub-step 0's A operands and
+// fragments of stage `st` into set 0.
+template <typename TA>
+__device__ __forceinline__ void v3q_first(V3Frags<TA>& f, const V3Stage& st, int wave, int l32, int h) {
+  v3q_words<TA>(f, st, wave, l32, h);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) f.B[0][b] = v3q_rdB<TA>(st, 0, b, l32, h);
+  v3q_scales<TA>(f, h);
+  f.A[0][0] = v3q_dec<TA>(f, 0, 0);
+  f.A[0][1] = v3q_dec<TA>(f, 0, 1);
+}
+
+// One step of the persistent launch, entered with sub-step 0's operands of
+// stage `st` in set 0.  Sub-step j + 1's fragments are read and its words
+// decoded into the other set between sub-step j's multiplies, and the
+// step's loads go out between its multiplies as in v3p_compute.  With
+// kNext, the wait and barrier that make the next slab readable come after
+// the first multiply pair of sub-step 3 (every fragment of this step is in
+// registers by then), and the rest of sub-step 3 reads the next step's
+// words, scales and sub-step 0 operands from stage `nx` into set 0, so the
+// next step starts with its multiplies.  The next step's loads overwrite
+// only stages that every wavefront has finished reading at that barrier.
+template <typename TA, bool kNext, typename Issue>
+__device__ __forceinline__ void v3q_step(f32x16_t (&acc)[2][8], V3Frags<TA>& f, const V3Stage& st,
+                                         const V3Stage& nx, int wave, int l32, int h, const Issue& iss) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = j & 1, n = c ^ 1;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        acc[a][b] = V3Ops<TA>::mfma(f.A[c][a], f.B[c][b], acc[a][b]);
+#pragma unroll
+        for (int k = 0; k < 11; ++k)
+          if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
+            __builtin_amdgcn_sched_barrier(0);
+            iss(k);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        if (j < 3) {
+          if (a == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            f.B[n][b] = v3q_rdB<TA>(st, j + 1, b, l32, h);
+            __builtin_amdgcn_sched_barrier(0);
+          } else if (b == 2 || b == 5) {
+            __builtin_amdgcn_sched_barrier(0);
+            f.A[n][b == 2 ? 0 : 1] = v3q_dec<TA>(f, j + 1, b == 2 ? 0 : 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (kNext) {
+          if (b == 0 && a == 1) {
+            // every LDS read of this step has returned (lgkmcnt 0) and
+            // this wavefront's part of the next slab has landed (vmcnt 14:
+            // the step's 11 loads went out in sub-steps 0 and 1); then the
+            // block meets
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt((0x7 << 4) | kV3WaitLoads);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            v3q_words<TA>(f, nx, wave, l32, h);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (b == 2 && a == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            v3q_scales<TA>(f, h);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (b >= 1 && a == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            f.B[n][b - 1] = v3q_rdB<TA>(nx, 0, b - 1, l32, h);
+            __builtin_amdgcn_sched_barrier(0);
+          } else if (a == 1 && (b == 3 || b == 5)) {
+            __builtin_amdgcn_sched_barrier(0);
+            f.A[n][b == 3 ? 0 : 1] = v3q_dec<TA>(f, 0, b == 3 ? 0 : 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (kNext) f.B[0][7] = v3q_rdB<TA>(nx, 0, 7, l32, h);
+}
+
 // One tile's slabs (nslabs % 6 == 0, nslabs >= 12).  `issued`: the first
 // slabs were queued by the previous tile.  With has_next, the last three
 // steps queue the next tile's slabs 0-1 (activations) and 0-2 (weights) from
@@ -1005,33 +1087,41 @@ __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stag
     v3p_issue_x(X[1], b, o, 1, wave);
     v3p_issue_w(W[2], b, o, 2, wave);
   }
-#define NVFP4_V3P_STEP(XI, WI, XO, XSLAB, WO, WSLAB)                                 \
+  // slab 0 readable, its operands into set 0; every later step is made
+  // readable inside the step before it
+  wait_vmem(true);
+  __builtin_amdgcn_s_barrier();
+  V3Frags<TA> f;
+  {
+    const V3Stage first{X[0].x, W[0].w, W[0].s};
+    v3q_first<TA>(f, first, wave, l32, h);
+  }
+#define NVFP4_V3P_STEP(XI, WI, XO, XSLAB, WO, WSLAB, NEXT)                           \
   do {                                                                               \
-    wait_vmem(true);                                                                 \
-    __builtin_amdgcn_s_barrier();                                                    \
     const V3pIssue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &(XO), &(WO), (XSLAB), (WSLAB), wave, &b}; \
     const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
-    v3p_compute<TA, true>(acc, cur, wave, l32, h, iss);                              \
+    const V3Stage nxt{X[((XI) + 1) % 3].x, W[((WI) + 1) % 6].w, W[((WI) + 1) % 6].s}; \
+    v3q_step<TA, NEXT>(acc, f, cur, nxt, wave, l32, h, iss);                         \
   } while (0)
   uint32_t s = 0;
   for (; s + 6 < nslabs; s += 6) {
-    NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3);
-    NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4);
-    NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5);
-    NVFP4_V3P_STEP(0, 3, o, s + 5, o, s + 6);
-    NVFP4_V3P_STEP(1, 4, o, s + 6, o, s + 7);
-    NVFP4_V3P_STEP(2, 5, o, s + 7, o, s + 8);
+    NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3, true);
+    NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4, true);
+    NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5, true);
+    NVFP4_V3P_STEP(0, 3, o, s + 5, o, s + 6, true);
+    NVFP4_V3P_STEP(1, 4, o, s + 6, o, s + 7, true);
+    NVFP4_V3P_STEP(2, 5, o, s + 7, o, s + 8, true);
   }
-  NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3);
-  NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4);
-  NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5);
+  NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3, true);
+  NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4, true);
+  NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5, true);
   // without a next tile, `no` holds this tile's offsets and the tail
   // queues its last slab again
   const uint32_t last = nslabs - 1;
   const uint32_t q0 = has_next ? 0u : last, q1 = has_next ? 1u : last, q2 = has_next ? 2u : last;
-  NVFP4_V3P_STEP(0, 3, o, last, no, q0);
-  NVFP4_V3P_STEP(1, 4, no, q0, no, q1);
-  NVFP4_V3P_STEP(2, 5, no, q1, no, q2);
+  NVFP4_V3P_STEP(0, 3, o, last, no, q0, true);
+  NVFP4_V3P_STEP(1, 4, no, q0, no, q1, true);
+  NVFP4_V3P_STEP(2, 5, no, q1, no, q2, false);
   if (!has_next) wait_vmem(false);   // no load-to-LDS may land after the last tile
 #undef NVFP4_V3P_STEP
 }
