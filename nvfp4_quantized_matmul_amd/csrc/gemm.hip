@@ -297,6 +297,12 @@ template <typename TA> struct V3Ops;
 template <> struct V3Ops<__bf16> {
   typedef bf16x8_t vec;
   static __device__ __forceinline__ vec decode(uint32_t w, float s) { return decode_word_bf16(w, s); }
+  // Pair P of decode(w, s): elements 2P and 2P + 1 as one dword.
+  template <int P>
+  static __device__ __forceinline__ uint32_t pair(uint32_t w, float s) {
+    const f32x2_t v = e2m1x2_f32<P>(w);
+    return pack_bf16_exact(v.x * s, v.y * s);
+  }
   static __device__ __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -304,6 +310,12 @@ template <> struct V3Ops<__bf16> {
 template <> struct V3Ops<_Float16> {
   typedef f16x8_t vec;
   static __device__ __forceinline__ vec decode(uint32_t w, float s) { return decode_word_f16(w, s); }
+  template <int P>
+  static __device__ __forceinline__ uint32_t pair(uint32_t w, float s) {
+    const _Float16 hs = (_Float16)s;
+    const f16x2_t ss = {hs, hs};
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, P) * ss);
+  }
   static __device__ __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -943,7 +955,8 @@ __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int6
 // step being decoded.
 template <typename TA>
 struct V3Frags {
-  typename V3Ops<TA>::vec B[2][8], A[2][2];
+  typename V3Ops<TA>::vec B[2][8];
+  uint32_t A[2][2][4];
   uint4 wr[2];
   uint32_t sr[2];
   float slo[2], shi[2];
@@ -970,10 +983,27 @@ __device__ __forceinline__ void v3q_scales(V3Frags<TA>& f, int h) {
     f.shi[a] = e4m3<1>(sv);
   }
 }
-template <typename TA>
-__device__ __forceinline__ typename V3Ops<TA>::vec v3q_dec(const V3Frags<TA>& f, int j, int a) {
+// Pair P of sub-step j's A operand for weight rows a (the word's elements
+// 2P, 2P + 1), into set n: four VALU instructions, so that one pair fits in
+// the shadow of one multiply (a whole word's sixteen in one place would
+// hold the next multiply back).
+template <typename TA, int P>
+__device__ __forceinline__ void v3q_pair(V3Frags<TA>& f, int n, int j, int a) {
   const uint32_t word = j == 0 ? f.wr[a].x : j == 1 ? f.wr[a].y : j == 2 ? f.wr[a].z : f.wr[a].w;
-  return V3Ops<TA>::decode(word, j < 2 ? f.slo[a] : f.shi[a]);
+  f.A[n][a][P] = V3Ops<TA>::template pair<P>(word, j < 2 ? f.slo[a] : f.shi[a]);
+}
+template <typename TA>
+__device__ __forceinline__ void v3q_pair_any(V3Frags<TA>& f, int n, int j, int a, int p) {
+  switch (p) {
+    case 0: v3q_pair<TA, 0>(f, n, j, a); break;
+    case 1: v3q_pair<TA, 1>(f, n, j, a); break;
+    case 2: v3q_pair<TA, 2>(f, n, j, a); break;
+    default: v3q_pair<TA, 3>(f, n, j, a); break;
+  }
+}
+template <typename TA>
+__device__ __forceinline__ typename V3Ops<TA>::vec v3q_A(const V3Frags<TA>& f, int c, int a) {
+  return __builtin_bit_cast(typename V3Ops<TA>::vec, f.A[c][a]);
 }
 template <typename TA>
 __device__ __forceinline__ typename V3Ops<TA>::vec v3q_rdB(const V3Stage& st, int j, int b, int l32, int h) {
@@ -988,8 +1018,10 @@ __device__ __forceinline__ void v3q_first(V3Frags<TA>& f, const V3Stage& st, int
 #pragma unroll
   for (int b = 0; b < 8; ++b) f.B[0][b] = v3q_rdB<TA>(st, 0, b, l32, h);
   v3q_scales<TA>(f, h);
-  f.A[0][0] = v3q_dec<TA>(f, 0, 0);
-  f.A[0][1] = v3q_dec<TA>(f, 0, 1);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) v3q_pair_any<TA>(f, 0, 0, a, p);
 }
 
 // One step of the persistent launch, entered with sub-step 0's operands of
@@ -1012,26 +1044,29 @@ __device__ __forceinline__ void v3q_step(f32x16_t (&acc)[2][8], V3Frags<TA>& f, 
     for (int b = 0; b < 8; ++b) {
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        acc[a][b] = V3Ops<TA>::mfma(f.A[c][a], f.B[c][b], acc[a][b]);
+        acc[a][b] = V3Ops<TA>::mfma(v3q_A<TA>(f, c, a), f.B[c][b], acc[a][b]);
+        const int m = 2 * b + a;   // multiplies issued in this sub-step, minus one
 #pragma unroll
         for (int k = 0; k < 11; ++k)
-          if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
+          if (kV3pLoadAfter[k] == 16 * j + m) {
             __builtin_amdgcn_sched_barrier(0);
             iss(k);
             __builtin_amdgcn_sched_barrier(0);
           }
         if (j < 3) {
+          // sub-step j + 1: fragment b after the first multiply of pair b,
+          // the A operands one dword (pair) after each odd multiply
           if (a == 0) {
             __builtin_amdgcn_sched_barrier(0);
             f.B[n][b] = v3q_rdB<TA>(st, j + 1, b, l32, h);
             __builtin_amdgcn_sched_barrier(0);
-          } else if (b == 2 || b == 5) {
+          } else {
             __builtin_amdgcn_sched_barrier(0);
-            f.A[n][b == 2 ? 0 : 1] = v3q_dec<TA>(f, j + 1, b == 2 ? 0 : 1);
+            v3q_pair_any<TA>(f, n, j + 1, b >> 2, b & 3);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else if constexpr (kNext) {
-          if (b == 0 && a == 1) {
+          if (m == 1) {
             // every LDS read of this step has returned (lgkmcnt 0) and
             // this wavefront's part of the next slab has landed (vmcnt 14:
             // the step's 11 loads went out in sub-steps 0 and 1); then the
@@ -1043,7 +1078,7 @@ __device__ __forceinline__ void v3q_step(f32x16_t (&acc)[2][8], V3Frags<TA>& f, 
             v3q_words<TA>(f, nx, wave, l32, h);
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (b == 2 && a == 1) {
+          if (m == 5) {
             __builtin_amdgcn_sched_barrier(0);
             v3q_scales<TA>(f, h);
             __builtin_amdgcn_sched_barrier(0);
@@ -1052,9 +1087,11 @@ __device__ __forceinline__ void v3q_step(f32x16_t (&acc)[2][8], V3Frags<TA>& f, 
             __builtin_amdgcn_sched_barrier(0);
             f.B[n][b - 1] = v3q_rdB<TA>(nx, 0, b - 1, l32, h);
             __builtin_amdgcn_sched_barrier(0);
-          } else if (a == 1 && (b == 3 || b == 5)) {
+          }
+          if (m >= 7 && m <= 14) {
+            // the next step's sub-step 0 A operands, one dword per multiply
             __builtin_amdgcn_sched_barrier(0);
-            f.A[n][b == 3 ? 0 : 1] = v3q_dec<TA>(f, 0, b == 3 ? 0 : 1);
+            v3q_pair_any<TA>(f, n, 0, (m - 7) >> 2, (m - 7) & 3);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
