@@ -582,31 +582,58 @@ __device__ __forceinline__ void v3p_compute(f32x16_t (&acc)[2][8], const V3Stage
 #pragma unroll
   for (int k = 0; k < 11; ++k)
     if (kV3pLoadAfter[k] < 0) iss(k);
+  // Each sub-step multiplies by A operand (weight rows 0-31 against the
+  // eight fragments, then rows 32-63), so with no extra registers: the
+  // second A is decoded one dword (pair) after each of the first four
+  // multiplies, and during the second half each fragment register is
+  // refilled with the next sub-step's fragment once its last multiply is
+  // issued and the next sub-step's first A is decoded one pair at a time
+  // (no more than four VALU instructions between two multiplies; a whole
+  // word is sixteen).  Each accumulator still takes one multiply per
+  // sub-step in k order, so the sums are those of v3_compute.
+  auto word = [&](int j, int a) { return j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w; };
+  auto rdB = [&](int j, int b) { return __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]); };
+  auto pair = [&](uint32_t (&A)[4], int j, int a, int p) {
+    const uint32_t w = word(j, a);
+    const float sc = j < 2 ? slo[a] : shi[a];
+    switch (p) {
+      case 0: A[0] = V3Ops<TA>::template pair<0>(w, sc); break;
+      case 1: A[1] = V3Ops<TA>::template pair<1>(w, sc); break;
+      case 2: A[2] = V3Ops<TA>::template pair<2>(w, sc); break;
+      default: A[3] = V3Ops<TA>::template pair<3>(w, sc); break;
+    }
+  };
+  vec B[8];
+  uint32_t A0[4], A1[4];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) B[b] = rdB(0, b);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) pair(A0, 0, 0, p);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    vec B[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) B[b] = __builtin_bit_cast(vec, st.x[xslot(b * 32 + l32, 4 * h + j)]);
-    vec A[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const uint32_t word = j == 0 ? wr[a].x : j == 1 ? wr[a].y : j == 2 ? wr[a].z : wr[a].w;
-      A[a] = V3Ops<TA>::decode(word, j < 2 ? slo[a] : shi[a]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        acc[a][b] = V3Ops<TA>::mfma(A[a], B[b], acc[a][b]);
+      for (int b = 0; b < 8; ++b) {
+        acc[a][b] = V3Ops<TA>::mfma(__builtin_bit_cast(vec, a == 0 ? A0 : A1), B[b], acc[a][b]);
 #pragma unroll
         for (int k = 0; k < 11; ++k)
-          if (kV3pLoadAfter[k] == 16 * j + 2 * b + a) {
+          if (kV3pLoadAfter[k] == 16 * j + 8 * a + b) {
             __builtin_amdgcn_sched_barrier(0);
             iss(k);
             __builtin_amdgcn_sched_barrier(0);
           }
+        if (a == 0 && b < 4) {
+          __builtin_amdgcn_sched_barrier(0);
+          pair(A1, j, 1, b);
+          __builtin_amdgcn_sched_barrier(0);
+        } else if (a == 1 && j < 3) {
+          __builtin_amdgcn_sched_barrier(0);
+          B[b] = rdB(j + 1, b);
+          if (b < 4) pair(A0, j + 1, 0, b);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
