@@ -15,7 +15,8 @@
 //    block per compute unit walking its tiles, each tile's first slabs queued
 //    during the previous tile's last steps, each step's first operands read
 //    during the previous step's last multiplies) when there are more tiles
-//    than compute units and K is a multiple of 384.
+//    than compute units and K is a multiple of 384; the same for the gated
+//    MLP projection's whole rounds of tiles.
 //  * gemm_mfma_kernel (bf16 activations, transposed plane, K % 32 == 0):
 //    each wavefront decodes its weight rows straight from the packed words
 //    into bf16 MFMA operands (one 32-bit word = the eight k-values one lane
@@ -492,6 +493,51 @@ __device__ __forceinline__ void v3_store_tile(const f32x16_t (&acc)[2][8], TO* _
   }
 }
 
+// Epilogue of a gated tile: fragment (0, b) holds the gate sums and (1, b)
+// the up sums of the same (feature, row) pairs (feature n_blk + 32 wave +
+// 8 jj + 4 h + i, row m_blk + 32 b + l32); out = act(g_gate gate) (g_up up),
+// rounded once, as one 16-byte store of eight features per row.
+template <int kAct>
+__device__ __forceinline__ void v3_store_glu(const f32x16_t (&acc)[2][8], __bf16* __restrict__ out, int64_t M,
+                                             int64_t N, int64_t m_blk, int64_t n_blk, float gg, float gu, int wave,
+                                             int l32, int h) {
+  const bool vec_ok = (N % 8) == 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int64_t m = m_blk + b * 32 + l32;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      uint32_t r0[2], r1[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        float v[4];
+        const int idx[4] = {(2 * p) * 4 + 2 * d, (2 * p) * 4 + 2 * d + 1, (2 * p + 1) * 4 + 2 * d,
+                            (2 * p + 1) * 4 + 2 * d + 1};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = glu_act_t<kAct>(acc[0][b][idx[e]] * gg) * (acc[1][b][idx[e]] * gu);
+        r0[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+        r1[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+      }
+      const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r1[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(r0[1], r1[1], false, false);
+      const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      const int64_t f = n_blk + wave * 32 + 16 * p + 8 * h;
+      if (m >= M) continue;
+      __bf16* q = out + m * N + f;
+      if (vec_ok && f + 7 < N) {
+        *reinterpret_cast<uint4*>(q) = v;
+      } else {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (f + i < N) q[i] = __builtin_bit_cast(__bf16, (uint16_t)(wv[i / 2] >> (16 * (i % 2))));
+      }
+    }
+  }
+}
+
 // 32-bit byte offsets of a plain tile's slab-0 loads from the operand bases
 // (as in gemm_mfma_v3_kernel).  The loads are buffer loads to LDS: a buffer
 // resource per operand, the fixed lane offset in a register and the slab's
@@ -514,21 +560,6 @@ __device__ __forceinline__ v3_rsrc_t v3_buffer(const void* p, int64_t bytes) {
 struct V3Base {
   v3_rsrc_t x, w, s;
 };
-
-__device__ __forceinline__ void v3p_issue_x(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
-                                            int wave) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.x, NVFP4_LDS(&st.x[(i * 4 + wave) * 64]), 16, o.x[i],
-                                             slab * (kV3BK * 2), 0, 0);
-}
-__device__ __forceinline__ void v3p_issue_w(const V3Stage& st, const V3Base& b, const V3Off& o, uint32_t slab,
-                                            int wave) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.w, NVFP4_LDS(&st.w[(i * 4 + wave) * 64]), 16, o.w[i], slab * 32, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(b.s, NVFP4_LDS(&st.s[wave * 64]), 4, o.s, slab * 4, 0, 0);
-}
 
 // The next slabs' 11 loads of a step (8 activation, 2 weight, 1 scale
 // copies), issued one at a time between the step's multiplies.  kLaneScale:
@@ -896,44 +927,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
     return;
   }
   if constexpr (kGlu) {
-    // Fragment (0, b) holds the gate sums and (1, b) the up sums of the same
-    // (feature, row) pairs, laid out as below; one output fragment per b.
-    const float gg = global_factor(gs, 0), gu = global_factor(gsu, 0);
-    const bool vec_ok = (N % 8) == 0;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int64_t m = m_blk + b * 32 + l32;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        uint32_t r0[2], r1[2];
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          float v[4];
-          const int idx[4] = {(2 * p) * 4 + 2 * d, (2 * p) * 4 + 2 * d + 1, (2 * p + 1) * 4 + 2 * d,
-                              (2 * p + 1) * 4 + 2 * d + 1};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = glu_act_t<kAct>(acc[0][b][idx[e]] * gg) * (acc[1][b][idx[e]] * gu);
-          r0[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-          r1[d] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
-        }
-        const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r1[0], false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(r0[1], r1[1], false, false);
-        const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-        const int64_t f = n_blk + wave * 32 + 16 * p + 8 * h;
-        if (m >= M) continue;
-        __bf16* q = out + m * N + f;
-        if (vec_ok && f + 7 < N) {
-          *reinterpret_cast<uint4*>(q) = v;
-        } else {
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (f + i < N) q[i] = __builtin_bit_cast(__bf16, (uint16_t)(wv[i / 2] >> (16 * (i % 2))));
-        }
-      }
-    }
+    v3_store_glu<kAct>(acc, out, M, N, m_blk, n_blk, global_factor(gs, 0), global_factor(gsu, 0), wave, l32, h);
     return;
   }
   v3_store_tile<TO>(acc, out, M, N, m_blk, n_blk, global_factor(gs, 0), wave, l32, h);
@@ -952,8 +946,14 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
 // fastest), its blocks taking them round-robin, as in the plain launch.
 // ----------------------------------------------------------------------------
 
+// kGlu: the gated tile (128 features from n_blk; wavefront w's rows come
+// from the gate plane for even w and the up plane for odd w, feature
+// n_blk + 32 (r / 64) + r % 32 for tile row r), and `ls` the lane's scale row
+// at slab 0 (the gate plane's for lanes 0-31, the up plane's for 32-63).
+template <bool kGlu = false>
 __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int64_t N, int64_t m_blk,
-                                            int64_t n_blk, int wave, int lane) {
+                                            int64_t n_blk, int wave, int lane, const uint8_t* sc = nullptr,
+                                            const uint8_t* scu = nullptr, const uint8_t** ls = nullptr) {
   const int64_t kw = K / 8, ks = K / 16;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -967,13 +967,20 @@ __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int6
   for (int i = 0; i < 2; ++i) {
     const int q = (i * 4 + wave) * 64 + lane;
     const int r = q >> 1, half = (q & 1) ^ ((r >> 3) & 1);
-    int64_t n = n_blk + r;
+    int64_t n = kGlu ? n_blk + (r >> 6) * 32 + (r & 31) : n_blk + r;
     if (n >= N) n = N - 1;
     o.w[i] = (uint32_t)((n * kw + 4 * half) * 4);
   }
-  int64_t n = n_blk + wave * 64 + lane;
-  if (n >= N) n = N - 1;
-  o.s = (uint32_t)(n * ks);
+  if constexpr (kGlu) {
+    int64_t f = n_blk + wave * 32 + (lane & 31);
+    if (f >= N) f = N - 1;
+    *ls = ((lane >> 5) ? scu : sc) + f * ks;
+    o.s = 0;
+  } else {
+    int64_t n = n_blk + wave * 64 + lane;
+    if (n >= N) n = N - 1;
+    o.s = (uint32_t)(n * ks);
+  }
 }
 
 // Fragment registers of the persistent launch, carried from one step to the
@@ -1134,10 +1141,12 @@ __device__ __forceinline__ void v3q_step(f32x16_t (&acc)[2][8], V3Frags<TA>& f, 
 // the offsets `no`, and the loads stay in flight when this returns;
 // otherwise they queue this tile's last slab again and the load counter is
 // drained.
-template <typename TA>
+template <typename TA, bool kGlu = false>
 __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stage (&X)[3], const V3Stage (&W)[6],
                                              const V3Base& b, const V3Off& o, const V3Off& no, bool has_next,
-                                             bool issued, uint32_t nslabs, int wave, int l32, int h) {
+                                             bool issued, uint32_t nslabs, int wave, int l32, int h,
+                                             const uint8_t* ls = nullptr, const uint8_t* nls = nullptr) {
+  typedef V3pIssueT<kGlu> Issue;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -1145,11 +1154,20 @@ __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stag
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.0f;
   if (!issued) {
-    v3p_issue_w(W[0], b, o, 0, wave);
-    v3p_issue_x(X[0], b, o, 0, wave);
-    v3p_issue_w(W[1], b, o, 1, wave);
-    v3p_issue_x(X[1], b, o, 1, wave);
-    v3p_issue_w(W[2], b, o, 2, wave);
+    // weights of slab 0, activations of slab 0, weights of slab 1, ...
+    const Issue p0{&X[0], &W[0], &o, &o, 0u, 0u, wave, &b, ls};
+    const Issue p1{&X[1], &W[1], &o, &o, 1u, 1u, wave, &b, ls};
+    const Issue p2{&X[2], &W[2], &o, &o, 2u, 2u, wave, &b, ls};
+#pragma unroll
+    for (int k = 8; k < 11; ++k) p0(k);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p0(k);
+#pragma unroll
+    for (int k = 8; k < 11; ++k) p1(k);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p1(k);
+#pragma unroll
+    for (int k = 8; k < 11; ++k) p2(k);
   }
   // slab 0 readable, its operands into set 0; every later step is made
   // readable inside the step before it
@@ -1160,41 +1178,47 @@ __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stag
     const V3Stage first{X[0].x, W[0].w, W[0].s};
     v3q_first<TA>(f, first, wave, l32, h);
   }
-#define NVFP4_V3P_STEP(XI, WI, XO, XSLAB, WO, WSLAB, NEXT)                           \
+#define NVFP4_V3P_STEP(XI, WI, XO, XSLAB, WO, WSLAB, WLS, NEXT)                      \
   do {                                                                               \
-    const V3pIssue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &(XO), &(WO), (XSLAB), (WSLAB), wave, &b}; \
+    const Issue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &(XO), &(WO), (XSLAB), (WSLAB), wave, &b, (WLS)}; \
     const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
     const V3Stage nxt{X[((XI) + 1) % 3].x, W[((WI) + 1) % 6].w, W[((WI) + 1) % 6].s}; \
     v3q_step<TA, NEXT>(acc, f, cur, nxt, wave, l32, h, iss);                         \
   } while (0)
   uint32_t s = 0;
   for (; s + 6 < nslabs; s += 6) {
-    NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3, true);
-    NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4, true);
-    NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5, true);
-    NVFP4_V3P_STEP(0, 3, o, s + 5, o, s + 6, true);
-    NVFP4_V3P_STEP(1, 4, o, s + 6, o, s + 7, true);
-    NVFP4_V3P_STEP(2, 5, o, s + 7, o, s + 8, true);
+    NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3, ls, true);
+    NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4, ls, true);
+    NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5, ls, true);
+    NVFP4_V3P_STEP(0, 3, o, s + 5, o, s + 6, ls, true);
+    NVFP4_V3P_STEP(1, 4, o, s + 6, o, s + 7, ls, true);
+    NVFP4_V3P_STEP(2, 5, o, s + 7, o, s + 8, ls, true);
   }
-  NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3, true);
-  NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4, true);
-  NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5, true);
+  NVFP4_V3P_STEP(0, 0, o, s + 2, o, s + 3, ls, true);
+  NVFP4_V3P_STEP(1, 1, o, s + 3, o, s + 4, ls, true);
+  NVFP4_V3P_STEP(2, 2, o, s + 4, o, s + 5, ls, true);
   // without a next tile, `no` holds this tile's offsets and the tail
   // queues its last slab again
   const uint32_t last = nslabs - 1;
   const uint32_t q0 = has_next ? 0u : last, q1 = has_next ? 1u : last, q2 = has_next ? 2u : last;
-  NVFP4_V3P_STEP(0, 3, o, last, no, q0, true);
-  NVFP4_V3P_STEP(1, 4, no, q0, no, q1, true);
-  NVFP4_V3P_STEP(2, 5, no, q1, no, q2, false);
+  NVFP4_V3P_STEP(0, 3, o, last, no, q0, nls, true);
+  NVFP4_V3P_STEP(1, 4, no, q0, no, q1, nls, true);
+  NVFP4_V3P_STEP(2, 5, no, q1, no, q2, nls, false);
   if (!has_next) wait_vmem(false);   // no load-to-LDS may land after the last tile
 #undef NVFP4_V3P_STEP
 }
 
-template <typename TA>
+// kGlu: the gated MLP projection's tiles (N is the feature count; the
+// second plane wu, scu, gsu holds the up rows) with the gated epilogue for
+// activation kAct, bf16 only.
+template <typename TA, bool kGlu = false, int kAct = 0>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
     const TA* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
     const float* __restrict__ gs, TA* __restrict__ out, int64_t M, int64_t K, int64_t N, int64_t tiles_m,
-    int64_t tiles_total, int64_t per_xcd) {
+    int64_t tiles_total, int64_t per_xcd, const uint32_t* __restrict__ wu = nullptr,
+    const uint8_t* __restrict__ scu = nullptr, const float* __restrict__ gsu = nullptr) {
+  static_assert(!kGlu || __is_same(TA, __bf16), "the gated form is bf16");
+  constexpr int64_t kTileN = kGlu ? kV3BN / 2 : kV3BN;   // output columns per tile
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
   __shared__ uint4 w0[kV3BN * 2], w1[kV3BN * 2], w2[kV3BN * 2], w3[kV3BN * 2], w4[kV3BN * 2], w5[kV3BN * 2];
   __shared__ uint32_t s0[kV3BN], s1[kV3BN], s2[kV3BN], s3[kV3BN], s4[kV3BN], s5[kV3BN];
@@ -1214,9 +1238,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const uint32_t nslabs = (uint32_t)(K / kV3BK);
   const float g = global_factor(gs, 0);
-  const V3Base base{v3_buffer(x, M * K * 2), v3_buffer(w, N * (K / 2)), v3_buffer(sc, N * (K / 16))};
+  const float gu = kGlu ? global_factor(gsu, 0) : 0.0f;
+  const V3Base base{v3_buffer(x, M * K * 2), v3_buffer((kGlu && (wave & 1)) ? wu : w, N * (K / 2)),
+                    v3_buffer(sc, N * (K / 16))};
   V3Off o, no;
-  v3p_offsets(o, M, K, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kV3BN, wave, lane);
+  const uint8_t *ls = nullptr, *nls = nullptr;
+  v3p_offsets<kGlu>(o, M, K, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, wave, lane, sc, scu, &ls);
   bool issued = false;
   for (;;) {
     // The lane index passes through an empty asm each tile, so values
@@ -1227,14 +1254,18 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
     const int lx = ln & 31, hx = ln >> 5;
     const int64_t next = tile + bpx;
     const bool has_next = next < t_end;
-    v3p_offsets(no, M, K, N, ((has_next ? next : tile) % tiles_m) * kV3BM, ((has_next ? next : tile) / tiles_m) * kV3BN,
-                wave, ln);
+    v3p_offsets<kGlu>(no, M, K, N, ((has_next ? next : tile) % tiles_m) * kV3BM,
+                      ((has_next ? next : tile) / tiles_m) * kTileN, wave, ln, sc, scu, &nls);
     f32x16_t acc[2][8];
-    v3p_mainloop<TA>(acc, XS, WS, base, o, no, has_next, issued, nslabs, wave, lx, hx);
-    v3_store_tile<TA>(acc, out, M, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kV3BN, g, wave, lx, hx);
+    v3p_mainloop<TA, kGlu>(acc, XS, WS, base, o, no, has_next, issued, nslabs, wave, lx, hx, ls, nls);
+    if constexpr (kGlu)
+      v3_store_glu<kAct>(acc, out, M, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, g, gu, wave, lx, hx);
+    else
+      v3_store_tile<TA>(acc, out, M, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, g, wave, lx, hx);
     if (!has_next) break;
     tile = next;
     o = no;
+    ls = nls;
     issued = true;
   }
 }
@@ -1814,7 +1845,21 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
   if (ws && (reinterpret_cast<uintptr_t>(ws) & 15) == 0) glu_tail_split(M, K, F, &tail, &sp);
   if (sp < 2 || ws_bytes < tail * sp * 65536 * 4) tail = 0;
   const int64_t dp = tiles - tail;
-  if (dp > 0) {
+  const int64_t nslabs = K / kV3BK;
+  const int64_t cus = device_cu_count();
+  if (dp > cus && nslabs % 6 == 0 && nslabs >= 12 && cus % 8 == 0 && M * K < ((int64_t)1 << 30) &&
+      F * (K / 8) < ((int64_t)1 << 29)) {
+    // whole rounds as a persistent launch (as the plain GEMM's), one block
+    // per compute unit, each XCD a contiguous run of tiles
+    const int64_t per_xcd = (dp + 7) / 8;
+    const int64_t bpx = per_xcd < cus / 8 ? per_xcd : cus / 8;
+    auto glu = gemm_mfma_v3p_kernel<__bf16, true, NVFP4_ACT_SILU>;
+    if (act == NVFP4_ACT_GELU_TANH) glu = gemm_mfma_v3p_kernel<__bf16, true, NVFP4_ACT_GELU_TANH>;
+    if (act == NVFP4_ACT_GELU) glu = gemm_mfma_v3p_kernel<__bf16, true, NVFP4_ACT_GELU>;
+    glu<<<dim3((unsigned)(8 * bpx)), dim3(kMfmaThreads), 0, s>>>(static_cast<const __bf16*>(x), w_gate, s_gate,
+                                                               gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m,
+                                                               dp, per_xcd, w_up, s_up, gs_up);
+  } else if (dp > 0) {
     const int64_t grid = (dp + 7) / 8 * 8;
     const bool buf = v3_buffers_fit(M, K, F, K);
     auto glu = buf ? gemm_mfma_v3_kernel<kV3Glu, NVFP4_ACT_SILU, __bf16, __bf16, true>

@@ -957,6 +957,54 @@ def test_qmm_glu_fused_tail_split():
     assert oracle.relative_error(host(out), host(plain)) <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("shape,workspace", [((300, 768, 128 * 140 - 37), False),
+                                             ((300, 768, 128 * 300 - 100), True),
+                                             ((2048, 5376, 21504), True)])
+def test_qmm_glu_persistent_route(shape, workspace):
+    """More whole-round tiles of the fused gated kernel than compute units
+    and K a multiple of 384: the persistent launch, whose blocks walk several
+    tiles with the next tile's first slabs queued during the current tile's
+    last steps.  280 tiles in one launch (no workspace); 600 tiles with the
+    binding's workspace (512 persistent, the 88 left split along K) and the
+    same call without one (600 persistent); and the MLP prefill shape.
+    Ragged row and feature tiles; sampled features of every feature tile
+    region against the oracle, a second call bit-equal to the first, and
+    the workspace form against the one-launch form."""
+    M, K, F = shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = ((M + 255) // 256) * ((F + 127) // 128)
+    assert tiles > cus and K % 384 == 0 and glu_is_fused(M, K, F, torch.bfloat16)
+    g, u = glu_planes(6900 + M + F, M, K, F)
+    x_t, x_ref = activations(g.x, torch.bfloat16)
+    wg, sg, wu_, su_ = words(g.w), u8(g.scales), words(u.w), u8(u.scales)
+    ggs, ugs = f32(g.gs), f32(u.gs)
+    lib = nv.load_library()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def one_launch():
+        out, check = guarded((M, F), torch.bfloat16)
+        assert lib.nvfp4_qmm_glu(P(x_t), 1, M, K, F, P(wg), P(sg), P(ggs), P(wu_), P(su_), P(ugs), 0, None, 0,
+                                 P(out), st) == 0
+        torch.cuda.synchronize()
+        check()
+        return out
+
+    plain = one_launch()
+    assert torch.equal(plain.view(torch.int16), one_launch().view(torch.int16))
+    outs = [plain]
+    if workspace:
+        assert glu_workspace(M, K, F, torch.bfloat16) > 0
+        outs.append(nv.qmm_glu(x_t, wg, sg, ggs, wu_, su_, ugs, act="gelu_tanh"))
+        torch.cuda.synchronize()
+        assert oracle.relative_error(host(outs[1]), host(plain)) <= TOL[torch.bfloat16]
+    feats = np.unique(np.concatenate([np.arange(0, F, max(1, F // 97)), np.arange(F - 130, F), [127, 128]]))
+    ref = oracle.qmm_glu(x_ref, g.w[feats], g.scales[feats], g.gs[0], u.w[feats], u.scales[feats], u.gs[0],
+                         "gelu_tanh")
+    for out in outs:
+        assert oracle.relative_error(host(out)[:, feats], ref) <= TOL[torch.bfloat16], shape
+
+
 @pytest.mark.parametrize("K,splits", [(2688, 7), (2112, 7), (1600, 5)])
 def test_qmm_glu_tail_split_piece_lengths(K, splits):
     """One tile of 256 rows x 128 features shared by up to 8 blocks along K:
