@@ -950,11 +950,15 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3_kernel(
 // from the gate plane for even w and the up plane for odd w, feature
 // n_blk + 32 (r / 64) + r % 32 for tile row r), and `ls` the lane's scale row
 // at slab 0 (the gate plane's for lanes 0-31, the up plane's for 32-63).
+// K is the activation row length, Kw the weight row length (K except for
+// float32 activations, whose rows are three bf16 parts: K = 3 Kw).
 template <bool kGlu = false>
 __device__ __forceinline__ void v3p_offsets(V3Off& o, int64_t M, int64_t K, int64_t N, int64_t m_blk,
                                             int64_t n_blk, int wave, int lane, const uint8_t* sc = nullptr,
-                                            const uint8_t* scu = nullptr, const uint8_t** ls = nullptr) {
-  const int64_t kw = K / 8, ks = K / 16;
+                                            const uint8_t* scu = nullptr, const uint8_t** ls = nullptr,
+                                            int64_t Kw = 0) {
+  if (Kw == 0) Kw = K;
+  const int64_t kw = Kw / 8, ks = Kw / 16;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int slot = (i * 4 + wave) * 64 + lane;
@@ -1141,12 +1145,19 @@ __device__ __forceinline__ void v3q_step(f32x16_t (&acc)[2][8], V3Frags<TA>& f, 
 // the offsets `no`, and the loads stay in flight when this returns;
 // otherwise they queue this tile's last slab again and the load counter is
 // drained.
-template <typename TA, bool kGlu = false>
+// kWrap: activation slab s meets weight slab s mod wslabs (float32
+// activations: three bf16 parts per row against one plane row).
+template <typename TA, bool kGlu = false, bool kWrap = false>
 __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stage (&X)[3], const V3Stage (&W)[6],
                                              const V3Base& b, const V3Off& o, const V3Off& no, bool has_next,
                                              bool issued, uint32_t nslabs, int wave, int l32, int h,
-                                             const uint8_t* ls = nullptr, const uint8_t* nls = nullptr) {
+                                             const uint8_t* ls = nullptr, const uint8_t* nls = nullptr,
+                                             uint32_t wslabs = 0) {
   typedef V3pIssueT<kGlu> Issue;
+  auto wsl = [&](uint32_t q) -> uint32_t {
+    if constexpr (kWrap) return q < wslabs ? q : q % wslabs;
+    return q;
+  };
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -1180,7 +1191,7 @@ __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stag
   }
 #define NVFP4_V3P_STEP(XI, WI, XO, XSLAB, WO, WSLAB, WLS, NEXT)                      \
   do {                                                                               \
-    const Issue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &(XO), &(WO), (XSLAB), (WSLAB), wave, &b, (WLS)}; \
+    const Issue iss{&X[((XI) + 2) % 3], &W[((WI) + 3) % 6], &(XO), &(WO), (XSLAB), wsl(WSLAB), wave, &b, (WLS)}; \
     const V3Stage cur{X[XI].x, W[WI].w, W[WI].s};                                    \
     const V3Stage nxt{X[((XI) + 1) % 3].x, W[((WI) + 1) % 6].w, W[((WI) + 1) % 6].s}; \
     v3q_step<TA, NEXT>(acc, f, cur, nxt, wave, l32, h, iss);                         \
@@ -1211,12 +1222,15 @@ __device__ __forceinline__ void v3p_mainloop(f32x16_t (&acc)[2][8], const V3Stag
 // kGlu: the gated MLP projection's tiles (N is the feature count; the
 // second plane wu, scu, gsu holds the up rows) with the gated epilogue for
 // activation kAct, bf16 only.
-template <typename TA, bool kGlu = false, int kAct = 0>
+// TO float: float32 activations as rows of three bf16 parts (K = 3 Kw,
+// Kw = 64 wslabs the plane's row length), float32 output.
+template <typename TA, bool kGlu = false, int kAct = 0, typename TO = TA>
 __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
     const TA* __restrict__ x, const uint32_t* __restrict__ w, const uint8_t* __restrict__ sc,
-    const float* __restrict__ gs, TA* __restrict__ out, int64_t M, int64_t K, int64_t N, int64_t tiles_m,
+    const float* __restrict__ gs, TO* __restrict__ out, int64_t M, int64_t K, int64_t N, int64_t tiles_m,
     int64_t tiles_total, int64_t per_xcd, const uint32_t* __restrict__ wu = nullptr,
-    const uint8_t* __restrict__ scu = nullptr, const float* __restrict__ gsu = nullptr) {
+    const uint8_t* __restrict__ scu = nullptr, const float* __restrict__ gsu = nullptr, int64_t wslabs = 0) {
+  constexpr bool kWrap = sizeof(TO) == 4;
   static_assert(!kGlu || __is_same(TA, __bf16), "the gated form is bf16");
   constexpr int64_t kTileN = kGlu ? kV3BN / 2 : kV3BN;   // output columns per tile
   __shared__ uint4 x0[kV3BM * 8], x1[kV3BM * 8], x2[kV3BM * 8];
@@ -1239,11 +1253,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
   const uint32_t nslabs = (uint32_t)(K / kV3BK);
   const float g = global_factor(gs, 0);
   const float gu = kGlu ? global_factor(gsu, 0) : 0.0f;
-  const V3Base base{v3_buffer(x, M * K * 2), v3_buffer((kGlu && (wave & 1)) ? wu : w, N * (K / 2)),
-                    v3_buffer(sc, N * (K / 16))};
+  const int64_t Kw = kWrap ? wslabs * kV3BK : K;
+  const V3Base base{v3_buffer(x, M * K * 2), v3_buffer((kGlu && (wave & 1)) ? wu : w, N * (Kw / 2)),
+                    v3_buffer(sc, N * (Kw / 16))};
   V3Off o, no;
   const uint8_t *ls = nullptr, *nls = nullptr;
-  v3p_offsets<kGlu>(o, M, K, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, wave, lane, sc, scu, &ls);
+  v3p_offsets<kGlu>(o, M, K, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, wave, lane, sc, scu, &ls, Kw);
   bool issued = false;
   for (;;) {
     // The lane index passes through an empty asm each tile, so values
@@ -1255,13 +1270,14 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void gemm_mfma_v3p_kernel(
     const int64_t next = tile + bpx;
     const bool has_next = next < t_end;
     v3p_offsets<kGlu>(no, M, K, N, ((has_next ? next : tile) % tiles_m) * kV3BM,
-                      ((has_next ? next : tile) / tiles_m) * kTileN, wave, ln, sc, scu, &nls);
+                      ((has_next ? next : tile) / tiles_m) * kTileN, wave, ln, sc, scu, &nls, Kw);
     f32x16_t acc[2][8];
-    v3p_mainloop<TA, kGlu>(acc, XS, WS, base, o, no, has_next, issued, nslabs, wave, lx, hx, ls, nls);
+    v3p_mainloop<TA, kGlu, kWrap>(acc, XS, WS, base, o, no, has_next, issued, nslabs, wave, lx, hx, ls, nls,
+                                  (uint32_t)(Kw / kV3BK));
     if constexpr (kGlu)
       v3_store_glu<kAct>(acc, out, M, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, g, gu, wave, lx, hx);
     else
-      v3_store_tile<TA>(acc, out, M, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, g, wave, lx, hx);
+      v3_store_tile<TO>(acc, out, M, N, (tile % tiles_m) * kV3BM, (tile / tiles_m) * kTileN, g, wave, lx, hx);
     if (!has_next) break;
     tile = next;
     o = no;
@@ -1792,6 +1808,17 @@ bool launch_gemm_mfma(const void* x, nvfp4_dtype_t dt, int64_t M, int64_t K, int
       split_f32_kernel<<<dim3((unsigned)sgrid), dim3(256), 0, s>>>(static_cast<const float*>(x), M, K, xs);
       const int64_t tiles_m = (M + kV3BM - 1) / kV3BM;
       const int64_t tiles = tiles_m * ((N + kV3BN - 1) / kV3BN);
+      const int64_t cus = device_cu_count();
+      if ((3 * K / kV3BK) % 6 == 0 && K / kV3BK >= 4 && tiles > cus && cus % 8 == 0 &&
+          M * 3 * K < ((int64_t)1 << 30) && N * (K / 8) < ((int64_t)1 << 29)) {
+        // persistent, as the bf16 prefill: one block per compute unit
+        const int64_t per_xcd = (tiles + 7) / 8;
+        const int64_t bpx = per_xcd < cus / 8 ? per_xcd : cus / 8;
+        gemm_mfma_v3p_kernel<__bf16, false, 0, float><<<dim3((unsigned)(8 * bpx)), dim3(kMfmaThreads), 0, s>>>(
+            reinterpret_cast<const __bf16*>(xs), w, sc, gs, static_cast<float*>(out), M, 3 * K, N, tiles_m, tiles,
+            per_xcd, nullptr, nullptr, nullptr, K / kV3BK);
+        return true;
+      }
       const int64_t grid = (tiles + 7) / 8 * 8;
       auto kern = v3_buffers_fit(M, 3 * K, N, K) ? gemm_mfma_v3_kernel<kV3Plain, 0, __bf16, float, true>
                                                  : gemm_mfma_v3_kernel<kV3Plain, 0, __bf16, float, false>;
@@ -1858,7 +1885,7 @@ void launch_gemm_glu(const void* x, int64_t M, int64_t K, int64_t F, const uint3
     if (act == NVFP4_ACT_GELU) glu = gemm_mfma_v3p_kernel<__bf16, true, NVFP4_ACT_GELU>;
     glu<<<dim3((unsigned)(8 * bpx)), dim3(kMfmaThreads), 0, s>>>(static_cast<const __bf16*>(x), w_gate, s_gate,
                                                                gs_gate, static_cast<__bf16*>(out), M, K, F, tiles_m,
-                                                               dp, per_xcd, w_up, s_up, gs_up);
+                                                               dp, per_xcd, w_up, s_up, gs_up, 0);
   } else if (dp > 0) {
     const int64_t grid = (dp + 7) / 8 * 8;
     const bool buf = v3_buffers_fit(M, K, F, K);

@@ -609,13 +609,16 @@ def test_prefill_gemm_full_size_sampled():
 
 
 @pytest.mark.parametrize("shape,dtype", [((1300, 768, 12000), torch.bfloat16),
-                                         ((777, 1152, 30000), torch.float16)])
+                                         ((777, 1152, 30000), torch.float16),
+                                         ((1300, 768, 12000), torch.float32)])
 def test_prefill_persistent_route_ragged(shape, dtype):
     """More output tiles than compute units and K a multiple of 384: the
     persistent prefill kernel, whose blocks walk several tiles and queue each
-    next tile's first slabs during the current tile's last steps.  Partial
-    row and column tiles; sampled rows (every row tile) against the oracle,
-    and a second call equal to the first bit for bit."""
+    next tile's first slabs during the current tile's last steps (float32
+    activations: their three-part bf16 rows of 3K, weight slab s mod K/64,
+    with the binding's workspace).  Partial row and column tiles; sampled
+    rows (every row tile) against the oracle, and a second call equal to the
+    first bit for bit."""
     M, K, N = shape
     assert ((M + 255) // 256) * ((N + 255) // 256) > 256 and K % 384 == 0
     case = synth.dense_case(4300 + M + K, M, K, N, with_gs=True)
@@ -623,7 +626,7 @@ def test_prefill_persistent_route_ragged(shape, dtype):
     out = nv.qmm(x_t, words(case.w), u8(case.scales), f32(case.gs), route="gemm")
     again = nv.qmm(x_t, words(case.w), u8(case.scales), f32(case.gs), route="gemm")
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    assert torch.equal(out.view(torch.uint8), again.view(torch.uint8))
     rows = np.unique(np.concatenate([np.arange(0, M, 61), [1, 255, 256, M - 2, M - 1]]))
     ref = oracle.qmm(x_ref[rows], case.w, case.scales, case.gs[0])
     assert oracle.relative_error(host(out)[rows], ref) <= TOL[dtype]
